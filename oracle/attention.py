@@ -1,0 +1,115 @@
+"""Textbook decode attention over dequantized caches, in float64.
+
+What the fused compressed-domain kernel reaches is exactly softmax attention
+over the dequantized cache: the unfused nine-step path of the "TurboQuant
+Triton deep dive" (section "nine-step path": unpack, look up, rotate back,
+scale by the norm, dot with the query) followed by softmax(q k^T / sqrt(d)) v
+("PolarQuant-KV", section 3.3; the 1/sqrt(d) logit scale also in "turbo4
+post-mortem", section 9).  The oracle therefore dequantizes every cached
+vector, forms the logits, takes a max-subtracted softmax and the weighted sum
+of dequantized values.
+
+Grouped-query attention: query head g reads KV head g // (Hq / Hkv).
+
+Besides the plain path, two helpers restate the identities the fast path
+relies on, so that tests can pin them:
+
+* ``compressed_scores``: the logit evaluated on the codes with a query that
+  was rotated once, <Pi q, n c[idx]> ("TurboQuant Triton deep dive", trick 1:
+  <q, Pi^T y> = <Pi q, y>), plus the QJL term <S q, 2b - 1> (trick 2);
+* ``split_records`` / ``combine_records``: the online-softmax state
+  (m, l, acc) of any partition of the keys and its merge (trick 3).
+"""
+
+import numpy as np
+
+from . import formats, rotation
+
+
+def softmax_attention(q, khat, vhat):
+    """o = softmax(q khat^T / sqrt(d)) vhat for one query vector; returns (o, logits)."""
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    if khat.shape[0] == 0:
+        return np.zeros(vhat.shape[1]), np.zeros(0)
+    s = khat @ q / np.sqrt(d)
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return p @ vhat, s
+
+
+def decode_attention(q, kv_k, kv_v, seq_lens, G):
+    """Attention for q [B, Hq, d] over dequantized caches kv_k/kv_v [B][Hkv] -> [N, d].
+
+    Returns (out [B, Hq, d], logits: list of per-(b, g) arrays).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, d = q.shape
+    out = np.zeros((B, Hq, d))
+    logits = [[None] * Hq for _ in range(B)]
+    for b in range(B):
+        n = int(seq_lens[b])
+        for g in range(Hq):
+            h = g // G
+            o, s = softmax_attention(q[b, g], kv_k[b][h][:n], kv_v[b][h][:n])
+            out[b, g] = o
+            logits[b][g] = s
+    return out, logits
+
+
+def compressed_scores(q, blocks, fmt, d, tabs, signs, S=None):
+    """Logits evaluated in the compressed domain for one query vector.
+
+    PQ4/PQ3: s_i = sum over blocks of n_blk * <Pi q, c[idx]> / sqrt(d).
+    TQ3K:    s_i = n * (<Pi q, c[idx]> + sqrt(pi/2)/d * gamma * <S q, 2b-1>) / sqrt(d).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    q_rot = rotation.rotate(q[None, :], signs)[0]
+    cent = tabs.centroids.astype(np.float64)
+    if fmt in (formats.PQ4, formats.PQ3):
+        if fmt == formats.PQ4:
+            norms, idx = formats.unpack_pq4(blocks, d)
+        else:
+            norms, idx = formats.unpack_pq3(blocks, d)
+        bs = formats.block_size_of(fmt)
+        s = np.zeros(blocks.shape[0])
+        for blk in range(d // bs):
+            sl = slice(bs * blk, bs * (blk + 1))
+            s += norms[:, blk] * (cent[idx[:, sl]] @ q_rot[sl])
+        return s / np.sqrt(d)
+    if fmt == formats.TQ3K:
+        n16, g16, idx, bits = formats.unpack_tq3k(blocks, d)
+        q_sk = np.asarray(S, dtype=np.float64) @ q
+        mse = cent[idx] @ q_rot
+        qjl = (2.0 * bits - 1.0) @ q_sk
+        return n16 * (mse + formats.QJL_CONST / d * g16 * qjl) / np.sqrt(d)
+    raise ValueError("compressed scores are defined for key formats")
+
+
+def split_records(s, vhat, bounds):
+    """Online-softmax state of each part [bounds[k], bounds[k+1]) of the keys.
+
+    m = max logit of the part (-inf if empty), l = sum exp(s - m),
+    acc = sum exp(s - m) v.
+    """
+    recs = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        if b <= a:
+            recs.append((-np.inf, 0.0, np.zeros(vhat.shape[1])))
+            continue
+        m = s[a:b].max()
+        e = np.exp(s[a:b] - m)
+        recs.append((m, e.sum(), e @ vhat[a:b]))
+    return recs
+
+
+def combine_records(recs):
+    """Merge (m, l, acc) parts: rescale each by exp(m_p - M) and normalize."""
+    ms = np.array([r[0] for r in recs])
+    if not np.isfinite(ms).any():
+        return np.zeros(recs[0][2].shape[0])
+    M = ms.max()
+    w = np.where(np.isfinite(ms), np.exp(np.where(np.isfinite(ms), ms - M, 0.0)), 0.0)
+    L = sum(wi * r[1] for wi, r in zip(w, recs))
+    acc = sum(wi * r[2] for wi, r in zip(w, recs))
+    return acc / L
