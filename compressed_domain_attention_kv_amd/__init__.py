@@ -1,0 +1,37 @@
+"""Compressed-domain KV-cache attention for MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libtq.so`` (``include/tq.h``):
+argument marshalling only.  Every step of the write and read paths runs in
+the library's HIP kernels; PyTorch provides device memory (tensors) and the
+stream (``torch.cuda.current_stream()``).  Importing this package without a
+built ``libtq.so`` raises: there is no fallback.
+
+Build the library with ``python -m compressed_domain_attention_kv_amd.build``.
+"""
+
+from ._binding import (  # noqa: F401
+    CB_LLOYD_MAX,
+    CB_QUANTILE_MEAN,
+    FMT_GQ2V,
+    FMT_PQ3,
+    FMT_PQ4,
+    FMT_TQ3K,
+    Codebook,
+    Layout,
+    TQError,
+    build_codebook,
+    cache_bytes,
+    decode_attention,
+    decode_combine,
+    decode_partial,
+    decode_splits,
+    decode_workspace_bytes,
+    lib,
+    library_path,
+    quantize_append,
+    quantize_rotated,
+    rotate_sketch_query,
+    strerror,
+    vector_bytes,
+    version,
+)

@@ -1,0 +1,405 @@
+// Write path of libtq on gfx950: quantize-and-append, quantize from given
+// rotated coordinates, and the once-per-query rotation / QJL sketch.
+//
+// One vector is spread over LPV = d/8 lanes holding 8 consecutive
+// coordinates each, so the fp16 row is read with one 16-byte load per lane
+// (fully coalesced) and the Walsh-Hadamard transform runs 3 butterfly
+// stages in registers and log2(LPV) stages across lanes.  Norms and group
+// min/max are lane-group reductions.  Codes are packed in registers and
+// stored as whole dwords / halfwords of the block.
+
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+constexpr int kWriteThreads = 256;
+
+enum class Src { kFp16Rows, kRotated };
+
+struct WriteArgs {
+    const uint16_t* x;        // fp16 rows [nvec][d] (Src::kFp16Rows)
+    const float* y;           // fp32 rotated rows [nvec][d] (Src::kRotated)
+    const uint16_t* norm16;   // fp16 norms [nvec] (Src::kRotated)
+    const int32_t* dst_row;   // [nvec / hkv] rows, or null for dense output
+    const float* S;           // d x d QJL matrix (TQ3K)
+    uint8_t* out;
+    int nvec;
+    int hkv;
+    int capacity;
+    int batch;
+};
+
+// Index of the first fp32 boundary not below y, i.e. #{k : bounds[k] < y}.
+template <int NLEV>
+__device__ __forceinline__ uint32_t code_of(float y, const DevCodebook& cb) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int k = 0; k < NLEV - 1; ++k) c += (y > cb.bounds[k]) ? 1u : 0u;
+    return c;
+}
+
+template <int FMT>
+struct FormatTraits;
+template <>
+struct FormatTraits<TQ_FMT_PQ4> { static constexpr int kLevels = 16; };
+template <>
+struct FormatTraits<TQ_FMT_PQ3> { static constexpr int kLevels = 8; };
+template <>
+struct FormatTraits<TQ_FMT_TQ3K> { static constexpr int kLevels = 4; };
+template <>
+struct FormatTraits<TQ_FMT_GQ2V> { static constexpr int kLevels = 4; };
+
+template <int FMT, int D>
+constexpr int vec_bytes_c() {
+    return FMT == TQ_FMT_PQ4 ? 68 * (D / 128)
+         : FMT == TQ_FMT_PQ3 ? 14 * (D / 32)
+         : FMT == TQ_FMT_TQ3K ? 4 + D / 4 + D / 8
+                              : 12 * (D / kGroup);
+}
+
+template <int FMT, int D, Src SRC>
+__global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, DevCodebook cb) {
+    constexpr int LPV = D / 8;                  // lanes per vector
+    constexpr int VPB = kWriteThreads / LPV;    // vectors per workgroup
+    constexpr int VB = vec_bytes_c<FMT, D>();
+    __shared__ float r_sh[FMT == TQ_FMT_TQ3K ? VPB * D : 1];
+
+    const int tid = threadIdx.x;
+    const int l = tid % LPV;
+    const int slot = tid / LPV;
+    const int vec = blockIdx.x * VPB + slot;
+    bool active = vec < a.nvec;
+
+    // destination byte offset of this vector
+    size_t off = 0;
+    if (active) {
+        if (a.dst_row) {
+            const int t = vec / a.hkv, h = vec % a.hkv;
+            const int r = a.dst_row[t];
+            if (r < 0 || r >= a.batch * a.capacity) {
+                active = false;
+            } else {
+                const int b = r / a.capacity, pos = r % a.capacity;
+                off = ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + pos) * VB;
+            }
+        } else {
+            off = static_cast<size_t>(vec) * VB;
+        }
+    }
+    const int vsrc = vec < a.nvec ? vec : 0;  // inactive lanes compute on row 0 and store nothing
+
+    float v[8];
+    uint32_t n16 = 0;
+    if constexpr (SRC == Src::kFp16Rows) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(a.x + static_cast<size_t>(vsrc) * D + 8 * l);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    } else {
+        const float4* src = reinterpret_cast<const float4*>(a.y + static_cast<size_t>(vsrc) * D + 8 * l);
+        const float4 p0 = src[0], p1 = src[1];
+        v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+        v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+        n16 = a.norm16[vsrc];
+    }
+
+    uint8_t* dst = a.out + off;
+
+    if constexpr (FMT == TQ_FMT_GQ2V) {
+        // asymmetric 2-bit group quantization, groups of 32 channels = 4 lanes
+        float mn = v[0], mx = v[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
+#pragma unroll
+        for (int m = 1; m < 4; m <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, m, LPV));
+            mx = fmaxf(mx, __shfl_xor(mx, m, LPV));
+        }
+        const uint32_t z16 = float_to_half_bits(mn);  // exact: mn is an fp16 value
+        const uint32_t s16 = float_to_half_bits(__fdiv_rn(mx - mn, 3.0f));
+        const float z = half_bits_to_float(z16), s = half_bits_to_float(s16);
+        const float inv = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            uint32_t q = 0;
+            if (s > 0.0f) {
+                const float t = rintf((v[e] - z) * inv);
+                q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 3.0f));
+            }
+            packed |= q << (2 * e);
+        }
+        if (active) {
+            const int grp = l >> 2, lg = l & 3;
+            uint8_t* g = dst + 12 * grp;
+            if (lg == 0) *reinterpret_cast<uint32_t*>(g) = s16 | (z16 << 16);
+            *reinterpret_cast<uint16_t*>(g + 4 + 2 * lg) = static_cast<uint16_t>(packed);
+        }
+        return;
+    } else {
+        constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
+        if constexpr (SRC == Src::kFp16Rows) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+            ss = group_sum<LPV>(ss);
+            const float n = sqrtf(ss);
+            n16 = float_to_half_bits(fminf(n, kFp16Max));
+            const float inv = n > 0.0f ? __fdiv_rn(1.0f, n) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * rotation_sign(cb, 8 * l + e);
+            wht8<LPV>(v, l);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] *= kInvSqrtD;
+        }
+        constexpr int NLEV = FormatTraits<FMT>::kLevels;
+        uint32_t code[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e] = code_of<NLEV>(v[e], cb);
+
+        if constexpr (FMT == TQ_FMT_PQ4) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) word |= code[e] << (4 * e);
+            if (active) {
+                const int blk = l >> 4, lb = l & 15;
+                uint8_t* bp = dst + 68 * blk;
+                if (lb == 0) *reinterpret_cast<uint32_t*>(bp) = n16;
+                *reinterpret_cast<uint32_t*>(bp + 4 + 4 * lb) = word;
+            }
+        } else if constexpr (FMT == TQ_FMT_PQ3) {
+            uint32_t low = 0, high = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                low |= (code[e] & 3u) << (2 * e);
+                high |= ((code[e] >> 2) & 1u) << e;
+            }
+            if (active) {
+                const int blk = l >> 2, lb = l & 3;
+                uint8_t* bp = dst + 14 * blk;
+                if (lb == 0) *reinterpret_cast<uint16_t*>(bp) = static_cast<uint16_t>(n16);
+                *reinterpret_cast<uint16_t*>(bp + 2 + 2 * lb) = static_cast<uint16_t>(low);
+                bp[10 + lb] = static_cast<uint8_t>(high);
+            }
+        } else {  // TQ3K: 2-bit MSE codes plus the QJL sketch of the residual
+            uint32_t low = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) low |= code[e] << (2 * e);
+            // residual in the rotated basis, rotated back: r = Pi^T (y - c)
+            float r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) r[e] = v[e] - cb.centroids[code[e]];
+            wht8<LPV>(r, l);
+            float g2 = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                r[e] = r[e] * kInvSqrtD * rotation_sign(cb, 8 * l + e);
+                g2 += r[e] * r[e];
+            }
+            g2 = group_sum<LPV>(g2);
+            const uint32_t g16 = float_to_half_bits(fminf(sqrtf(g2), kFp16Max));
+            float* rs = r_sh + slot * D;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rs[8 * l + e] = r[e];
+            __syncthreads();
+            uint32_t bits = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int i = 8 * l + e;
+                const float4* Srow = reinterpret_cast<const float4*>(a.S + static_cast<size_t>(i) * D);
+                const float4* rr = reinterpret_cast<const float4*>(rs);
+                float acc = 0.0f;
+#pragma unroll 8
+                for (int j = 0; j < D / 4; ++j) {
+                    const float4 s4 = Srow[j], r4 = rr[j];
+                    acc += s4.x * r4.x + s4.y * r4.y + s4.z * r4.z + s4.w * r4.w;
+                }
+                bits |= (acc >= 0.0f ? 1u : 0u) << e;
+            }
+            if (active) {
+                if (l == 0) *reinterpret_cast<uint32_t*>(dst) = n16 | (g16 << 16);
+                *reinterpret_cast<uint16_t*>(dst + 4 + 2 * l) = static_cast<uint16_t>(low);
+                dst[4 + D / 4 + l] = static_cast<uint8_t>(bits);
+            }
+        }
+    }
+}
+
+// q_rot = Pi q = H (s * q) / sqrt(d); for TQ3K keys also q_sketch = S q.
+template <int D, bool SKETCH>
+__global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float* __restrict__ q, float* __restrict__ q_rot,
+                                                                  float* __restrict__ q_sk, const float* __restrict__ S,
+                                                                  int nvec, DevCodebook cb) {
+    constexpr int LPV = D / 8;
+    constexpr int VPB = kWriteThreads / LPV;
+    constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
+    __shared__ float q_sh[SKETCH ? VPB * D : 1];
+    const int tid = threadIdx.x, l = tid % LPV, slot = tid / LPV;
+    const int vec = blockIdx.x * VPB + slot;
+    const bool active = vec < nvec;
+    const int vsrc = active ? vec : 0;
+    const float4* src = reinterpret_cast<const float4*>(q + static_cast<size_t>(vsrc) * D + 8 * l);
+    const float4 p0 = src[0], p1 = src[1];
+    float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    if constexpr (SKETCH) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q_sh[slot * D + 8 * l + e] = v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= rotation_sign(cb, 8 * l + e);
+    wht8<LPV>(v, l);
+    if (active) {
+        float4* o = reinterpret_cast<float4*>(q_rot + static_cast<size_t>(vec) * D + 8 * l);
+        o[0] = make_float4(v[0] * kInvSqrtD, v[1] * kInvSqrtD, v[2] * kInvSqrtD, v[3] * kInvSqrtD);
+        o[1] = make_float4(v[4] * kInvSqrtD, v[5] * kInvSqrtD, v[6] * kInvSqrtD, v[7] * kInvSqrtD);
+    }
+    if constexpr (SKETCH) {
+        __syncthreads();
+        const float4* qq = reinterpret_cast<const float4*>(q_sh + slot * D);
+        float outv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int i = 8 * l + e;
+            const float4* Srow = reinterpret_cast<const float4*>(S + static_cast<size_t>(i) * D);
+            float acc = 0.0f;
+#pragma unroll 8
+            for (int j = 0; j < D / 4; ++j) {
+                const float4 s4 = Srow[j], x4 = qq[j];
+                acc += s4.x * x4.x + s4.y * x4.y + s4.z * x4.z + s4.w * x4.w;
+            }
+            outv[e] = acc;
+        }
+        if (active) {
+            float4* o = reinterpret_cast<float4*>(q_sk + static_cast<size_t>(vec) * D + 8 * l);
+            o[0] = make_float4(outv[0], outv[1], outv[2], outv[3]);
+            o[1] = make_float4(outv[4], outv[5], outv[6], outv[7]);
+        }
+    }
+}
+
+template <int FMT, int D, Src SRC>
+int launch_quantize(const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
+    constexpr int VPB = kWriteThreads / (D / 8);
+    const int grid = (a.nvec + VPB - 1) / VPB;
+    hipLaunchKernelGGL((quantize_kernel<FMT, D, SRC>), dim3(grid), dim3(kWriteThreads), 0, st, a, to_dev(cb));
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <Src SRC>
+int dispatch_quantize(int fmt, int d, const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
+#define TQ_Q(F)                                                                        \
+    case F:                                                                            \
+        return d == 128 ? launch_quantize<F, 128, SRC>(a, cb, st) : launch_quantize<F, 256, SRC>(a, cb, st);
+    switch (fmt) {
+        TQ_Q(TQ_FMT_PQ4)
+        TQ_Q(TQ_FMT_PQ3)
+        TQ_Q(TQ_FMT_TQ3K)
+        default: break;
+    }
+    if constexpr (SRC == Src::kFp16Rows) {
+        if (fmt == TQ_FMT_GQ2V)
+            return d == 128 ? launch_quantize<TQ_FMT_GQ2V, 128, SRC>(a, cb, st)
+                            : launch_quantize<TQ_FMT_GQ2V, 256, SRC>(a, cb, st);
+    }
+#undef TQ_Q
+    return TQ_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+int tq_quantize_append(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* S_dev,
+                       const uint16_t* k_new, const uint16_t* v_new, const int32_t* dst_row, int T, void* k_cache,
+                       void* v_cache, hipStream_t stream) {
+    using namespace tq;
+    int st = check_layout(L);
+    if (st != TQ_OK) return st;
+    if (T < 0) return TQ_ERR_INVALID;
+    if ((st = check_codebook(cbk, L->k_format, L->head_dim)) != TQ_OK) return st;
+    if ((st = check_codebook(cbv, L->v_format, L->head_dim)) != TQ_OK) return st;
+    if (T == 0) return TQ_OK;
+    if (static_cast<double>(T) * L->n_kv_heads > 2147483647.0) return TQ_ERR_RANGE;
+    if (!k_new || !v_new || !dst_row || !k_cache || !v_cache) return TQ_ERR_INVALID;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(dst_row, 4))
+        return TQ_ERR_INVALID;
+    if (L->k_format == TQ_FMT_TQ3K && (!S_dev || !aligned(S_dev, 16))) return TQ_ERR_INVALID;
+    WriteArgs a{};
+    a.dst_row = dst_row;
+    a.S = S_dev;
+    a.nvec = T * L->n_kv_heads;
+    a.hkv = L->n_kv_heads;
+    a.capacity = L->capacity;
+    a.batch = L->batch;
+    a.x = k_new;
+    a.out = static_cast<uint8_t*>(k_cache);
+    if ((st = dispatch_quantize<Src::kFp16Rows>(L->k_format, L->head_dim, a, *cbk, stream)) != TQ_OK) return st;
+    a.x = v_new;
+    a.out = static_cast<uint8_t*>(v_cache);
+    return dispatch_quantize<Src::kFp16Rows>(L->v_format, L->head_dim, a, *cbv, stream);
+}
+
+int tq_quantize_rotated(int format, const tq_codebook* cb, const float* S_dev, const float* y, const uint16_t* norm16,
+                        int n, void* blocks, hipStream_t stream) {
+    using namespace tq;
+    if (!cb) return TQ_ERR_INVALID;
+    const int d = cb->head_dim;
+    if (d != 128 && d != 256) return TQ_ERR_UNSUPPORTED;
+    if (format != TQ_FMT_PQ4 && format != TQ_FMT_PQ3 && format != TQ_FMT_TQ3K) return TQ_ERR_UNSUPPORTED;
+    int st = check_codebook(cb, format, d);
+    if (st != TQ_OK) return st;
+    if (n < 0) return TQ_ERR_INVALID;
+    if (n == 0) return TQ_OK;
+    if (!y || !norm16 || !blocks || !aligned(y, 16) || !aligned(blocks, 16) || !aligned(norm16, 2))
+        return TQ_ERR_INVALID;
+    if (format == TQ_FMT_TQ3K && (!S_dev || !aligned(S_dev, 16))) return TQ_ERR_INVALID;
+    WriteArgs a{};
+    a.y = y;
+    a.norm16 = norm16;
+    a.S = S_dev;
+    a.out = static_cast<uint8_t*>(blocks);
+    a.nvec = n;
+    a.hkv = 1;
+    a.capacity = 1;
+    a.batch = 1;
+    return dispatch_quantize<Src::kRotated>(format, d, a, *cb, stream);
+}
+
+int tq_rotate_sketch_query(const tq_layout* L, const tq_codebook* cbk, const float* S_dev, const float* q, float* q_rot,
+                           float* q_sketch, hipStream_t stream) {
+    using namespace tq;
+    int st = check_layout(L);
+    if (st != TQ_OK) return st;
+    if ((st = check_codebook(cbk, L->k_format, L->head_dim)) != TQ_OK) return st;
+    if (!q || !q_rot || !aligned(q, 16) || !aligned(q_rot, 16)) return TQ_ERR_INVALID;
+    const bool sketch = L->k_format == TQ_FMT_TQ3K;
+    if (sketch && (!S_dev || !q_sketch || !aligned(S_dev, 16) || !aligned(q_sketch, 16))) return TQ_ERR_INVALID;
+    const int nvec = L->batch * L->n_q_heads;
+    const int d = L->head_dim;
+    const int vpb = kWriteThreads / (d / 8);
+    const int grid = (nvec + vpb - 1) / vpb;
+    const DevCodebook c = to_dev(*cbk);
+    if (d == 128) {
+        if (sketch)
+            hipLaunchKernelGGL((rotate_query_kernel<128, true>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
+                               q_sketch, S_dev, nvec, c);
+        else
+            hipLaunchKernelGGL((rotate_query_kernel<128, false>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
+                               nullptr, nullptr, nvec, c);
+    } else {
+        if (sketch)
+            hipLaunchKernelGGL((rotate_query_kernel<256, true>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
+                               q_sketch, S_dev, nvec, c);
+        else
+            hipLaunchKernelGGL((rotate_query_kernel<256, false>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
+                               nullptr, nullptr, nvec, c);
+    }
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+symbol, and its host-side logic (codebooks, sizes, validation) is right.
+No call here enqueues GPU work."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+tq = pytest.importorskip("compressed_domain_attention_kv_amd")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(tq.lib, n), n
+        assert ctypes.cast(getattr(tq.lib, n), ctypes.c_void_p).value
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(tq.Codebook) == 192
+    assert ctypes.sizeof(tq.Layout) == 32
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("bits,kind", [(4, 0), (3, 0), (2, 0), (4, 1), (3, 1), (2, 1), (1, 0)])
+def test_codebook_tables_equal_the_oracle(d, bits, kind):
+    from oracle import codebook as cb
+    from oracle import prng
+    c, S = tq.build_codebook(d, bits, kind, 1234, 5678, want_qjl_matrix=(bits == 2))
+    t = cb.tables(d, bits, kind)
+    assert np.array_equal(c.centroid_array(), t.centroids)
+    assert np.array_equal(c.bound_array(), t.bounds)
+    assert np.array_equal(c.sign_array(), prng.rotation_signs(1234, d))
+    assert c.n_levels == 1 << bits and c.head_dim == d
+    if S is not None:
+        S_o = prng.qjl_matrix(5678, d)
+        # Box-Muller through libm on both sides: agree to 1 ulp, in practice exactly
+        assert np.max(np.abs(S - S_o) / np.maximum(np.abs(S_o), 1e-30)) <= 2 ** -23
+        assert np.mean(S == S_o) > 0.999
+
+
+def test_codebook_argument_errors():
+    c = tq.Codebook()
+    f = tq.lib.tq_build_codebook
+    assert f(100, 4, 0, 1, 2, ctypes.byref(c), None) == -2
+    assert f(128, 5, 0, 1, 2, ctypes.byref(c), None) == -2
+    assert f(128, 4, 7, 1, 2, ctypes.byref(c), None) == -2
+    assert f(128, 4, 0, 1, 2, None, None) == -1
+
+
+def test_vector_and_cache_bytes():
+    assert tq.vector_bytes(tq.FMT_PQ4, 128) == 68
+    assert tq.vector_bytes(tq.FMT_PQ4, 256) == 136
+    assert tq.vector_bytes(tq.FMT_PQ3, 128) == 56
+    assert tq.vector_bytes(tq.FMT_TQ3K, 128) == 52
+    assert tq.vector_bytes(tq.FMT_GQ2V, 128) == 48
+    assert tq.vector_bytes(tq.FMT_PQ4, 64) == 0
+    L = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
+    k, v = tq.cache_bytes(L)
+    assert k == v == 8 * 8 * 65536 * 68
+    assert k + v == 570_425_344
+
+
+def test_layout_validation_codes():
+    ok = tq.Layout(1, 4, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4)
+    tq.cache_bytes(ok)
+    for bad, code in [
+        (tq.Layout(1, 3, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4), -1),  # Hq not a multiple of Hkv
+        (tq.Layout(1, 4, 2, 128, 100, tq.FMT_PQ4, tq.FMT_PQ4), -1),  # capacity not a multiple of 64
+        (tq.Layout(0, 4, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4), -1),
+        (tq.Layout(1, 4, 2, 96, 128, tq.FMT_PQ4, tq.FMT_PQ4), -2),  # head dim
+        (tq.Layout(1, 4, 2, 128, 128, tq.FMT_GQ2V, tq.FMT_PQ4), -2),  # format pair
+        (tq.Layout(1, 4, 2, 128, 128, tq.FMT_TQ3K, tq.FMT_PQ4), -2),
+    ]:
+        with pytest.raises(tq.TQError) as e:
+            tq.cache_bytes(bad)
+        assert e.value.status == code
+
+
+def test_splits_and_workspace_arithmetic():
+    L = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
+    s = tq.decode_splits(L)
+    assert s >= 1 and 8 * 8 * s >= 2048
+    assert tq.decode_workspace_bytes(L) == 8 * 32 * s * (8 + 4 * 128)
+    assert tq.decode_splits(L, 1024) == 64
+    assert tq.decode_splits(L, 1000) == 0  # not a multiple of 256
+    small = tq.Layout(1, 1, 1, 128, 512, tq.FMT_PQ4, tq.FMT_PQ4)
+    assert tq.decode_splits(small, 256) == 2
+
+
+def test_device_calls_reject_bad_arguments_before_any_launch():
+    """Null pointers and short workspaces are refused on the host (no GPU here)."""
+    L = tq.Layout(1, 4, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4)
+    cb, _ = tq.build_codebook(128, 4, 0, 1, 2)
+    r = ctypes.byref
+    assert tq.lib.tq_quantize_append(r(L), r(cb), r(cb), None, None, None, None, 3, None, None, None) == -1
+    assert tq.lib.tq_quantize_append(r(L), r(cb), r(cb), None, None, None, None, 0, None, None, None) == 0
+    assert tq.lib.tq_quantize_append(r(L), r(cb), r(cb), None, None, None, None, -1, None, None, None) == -1
+    cb3, _ = tq.build_codebook(128, 3, 0, 1, 2)  # wrong bit width for PQ4
+    assert tq.lib.tq_quantize_append(r(L), r(cb3), r(cb), None, ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                     ctypes.c_void_p(16), 1, ctypes.c_void_p(16), ctypes.c_void_p(16), None) == -1
+    assert tq.lib.tq_rotate_sketch_query(r(L), r(cb), None, None, None, None, None) == -1
+    fake = ctypes.c_void_p(1 << 20)
+    need = tq.decode_workspace_bytes(L)
+    assert tq.lib.tq_decode_partial(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
+                                    need - 1, None) == -3
+    assert tq.lib.tq_decode_partial(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 100, fake,
+                                    need, None) == -1
+    misaligned = ctypes.c_void_p((1 << 20) + 4)
+    assert tq.lib.tq_decode_partial(r(L), r(cb), r(cb), fake, None, misaligned, fake, fake, None, 0, fake,
+                                    need, None) == -1
+    Lg = tq.Layout(1, 6, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4)  # G = 3 not built
+    assert tq.lib.tq_decode_partial(r(Lg), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
+                                    1 << 30, None) == -2
+    assert tq.lib.tq_decode_combine(r(L), r(cb), 0, fake, need - 1, fake, None) == -3
+    assert tq.lib.tq_quantize_rotated(9, r(cb), None, fake, fake, 1, fake, None) == -2
+    assert tq.strerror(-3).startswith("workspace")
