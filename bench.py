@@ -1,0 +1,282 @@
+"""Benchmark of the compressed-domain KV-cache decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+Workload (default, ``c4``): batch 8, 32 query heads / 8 KV heads (GQA 4:1),
+d = 128, 4-bit PQ4 keys and values, context 65,536 per sequence: 65,535
+tokens prefilled, then every step quantizes one new fp16 token per sequence
+and KV head into position 65,535, rotates the 256 queries and runs the fused
+split-K decode attention over the compressed bytes.  Inputs are the seeded
+synthetic rows of ``synth`` (Gaussian, 1% of channels scaled by 8), already
+resident in HBM when timing starts.
+
+One step = append (K and V) + query rotation + decode partial + combine.
+Two cache copies (1.14 GB together) alternate between steps so that the
+256 MB Infinity Cache cannot hold the bytes a step reads.
+
+Output: one JSON line.  ``value`` is compressed-KV tokens attended per second
+(batch * context / step time).  ``roofline`` reports the dominant kernel,
+decode_partial: algorithmic K+V bytes per launch over its mean duration
+measured with HIP events on the launch stream, against the 8 TB/s HBM peak.
+``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
+step.  ``--copy-calibration`` additionally runs a plain 1 GiB elementwise
+copy, the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partial_pq4_c4_counters.txt")
+DECODE_SRC = os.path.join(ROOT, "compressed_domain_attention_kv_amd", "csrc", "tq_decode.hip")
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_source_hash():
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode_partial launch from the committed counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    vals = {}
+    for ln in open(COUNTERS_FILE):
+        if ":" in ln and not ln.startswith("#"):
+            k, v = ln.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != decode_source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def gen_rows(w, tensor, count, threads=16):
+    """fp16 [B, count, Hkv, d] rows of every sequence, generated in parallel."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+
+    import synth
+    with ThreadPoolExecutor(threads) as ex:
+        rows = list(ex.map(lambda b: synth.batch_rows(w, tensor, b, 0, count), range(w.batch)))
+    return np.stack(rows)
+
+
+def cpu_baseline(w, target_seconds):
+    """Time the oracle on whole (b, kv-head) streams of one decode step."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import synth
+    from oracle import attention as oatt
+    from oracle import codebook as ocb
+    from oracle import formats as ofmt
+    from oracle import prng as oprng
+
+    d, N, G = w.head_dim, w.context, w.group
+    tk, tv = ocb.tables(d, w.k_bits, w.k_kind), ocb.tables(d, w.v_bits, w.v_kind)
+    sk, sv = oprng.rotation_signs(w.rot_seed_k, d), oprng.rotation_signs(w.rot_seed_v, d)
+    q = synth.queries(w, step=0)
+    done, elapsed = 0, 0.0
+    streams = [(b, h) for b in range(w.batch) for h in range(w.n_kv_heads)]
+    for b, h in streams:
+        # cache bytes the oracle writes itself (setup, not timed)
+        kb = ofmt.encode_rotated(synth.stream(w, synth.K_TENSOR, b, h, 0, N - 1), ofmt.PQ4, tk, sk).blocks
+        vb = ofmt.encode_rotated(synth.stream(w, synth.V_TENSOR, b, h, 0, N - 1), ofmt.PQ4, tv, sv).blocks
+        t0 = time.perf_counter()
+        kn = ofmt.encode_rotated(synth.appended(w, synth.K_TENSOR, b, h, 0)[None], ofmt.PQ4, tk, sk).blocks
+        vn = ofmt.encode_rotated(synth.appended(w, synth.V_TENSOR, b, h, 0)[None], ofmt.PQ4, tv, sv).blocks
+        kdq = ofmt.dequant(np.concatenate([kb, kn]), ofmt.PQ4, d, tk, sk)
+        vdq = ofmt.dequant(np.concatenate([vb, vn]), ofmt.PQ4, d, tv, sv)
+        for g in range(h * G, (h + 1) * G):
+            oatt.softmax_attention(q[b, g], kdq, vdq)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        if elapsed >= target_seconds:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": done * N / elapsed,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{done} of {len(streams)} (sequence, KV head) streams of one decode step: encode the appended "
+                   f"K/V token, dequantize {N} K and V blocks, softmax attention for {G} query heads; "
+                   f"{elapsed:.1f} s of float64 NumPy; host cpu_count {os.cpu_count()}, affinity "
+                   f"{len(os.sched_getaffinity(0))}, BLAS threads {threads}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=2, help="cache copies rotated between steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the decode path runs on a single MI355X and this build has no "
+              "multi-GPU path (sharding is described in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import compressed_domain_attention_kv_amd as tq
+    import synth
+
+    if args.workload != "c4":
+        raise SystemExit("the bench line is the c4 decode workload; other workloads are parity tests")
+    w = synth.C4
+    B, Hq, Hkv, d, cap, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.context
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    L = tq.Layout(B, Hq, Hkv, d, cap, tq.FMT_PQ4, tq.FMT_PQ4)
+    cbk, _ = tq.build_codebook(d, w.k_bits, w.k_kind, w.rot_seed_k, w.qjl_seed)
+    cbv, _ = tq.build_codebook(d, w.v_bits, w.v_kind, w.rot_seed_v, w.qjl_seed + 1)
+
+    # ---- prefill: 65,535 tokens of every sequence, written by the HIP encoder
+    kbytes, vbytes = tq.cache_bytes(L)
+    caches = [(torch.empty(kbytes, dtype=torch.uint8, device=dev), torch.empty(vbytes, dtype=torch.uint8, device=dev))
+              for _ in range(args.copies)]
+    t0 = time.time()
+    k_rows = gen_rows(w, synth.K_TENSOR, w.prefill)
+    v_rows = gen_rows(w, synth.V_TENSOR, w.prefill)
+    _log(f"generated {2 * k_rows.nbytes / 2**30:.2f} GiB of fp16 rows in {time.time() - t0:.1f}s")
+    kc, vc = caches[0]
+    for b in range(B):
+        dst = torch.arange(b * cap, b * cap + w.prefill, dtype=torch.int32, device=dev)
+        tq.quantize_append(L, cbk, cbv, None, torch.from_numpy(k_rows[b]).to(dev), torch.from_numpy(v_rows[b]).to(dev),
+                           dst, kc, vc)
+    del k_rows, v_rows
+    torch.cuda.synchronize()
+    for kc, vc in caches[1:]:
+        kc.copy_(caches[0][0])
+        vc.copy_(caches[0][1])
+    torch.cuda.synchronize()
+    _log(f"prefill {B}x{Hkv} streams x {w.prefill} tokens in {time.time() - t0:.1f}s")
+
+    # ---- per-step inputs, resident before timing
+    total = args.warmup + args.steps
+    kn = np.stack([np.stack([np.stack([synth.appended(w, synth.K_TENSOR, b, h, s) for h in range(Hkv)])
+                             for b in range(B)]) for s in range(total)])
+    vn = np.stack([np.stack([np.stack([synth.appended(w, synth.V_TENSOR, b, h, s) for h in range(Hkv)])
+                             for b in range(B)]) for s in range(total)])
+    k_new = torch.from_numpy(kn).to(dev)  # [steps, B, Hkv, d]: token t = sequence b
+    v_new = torch.from_numpy(vn).to(dev)
+    qs = torch.from_numpy(np.stack([synth.queries(w, step=s) for s in range(total)])).to(dev)
+    dst_row = torch.tensor([b * cap + N - 1 for b in range(B)], dtype=torch.int32, device=dev)
+    seq_lens = torch.full((B,), N, dtype=torch.int32, device=dev)
+    q_rot = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(tq.decode_workspace_bytes(L, args.split_tokens), dtype=torch.uint8, device=dev)
+    splits = tq.decode_splits(L, args.split_tokens)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
+
+    def step(s):
+        kc, vc = caches[s % args.copies]
+        e = ev[s]
+        e[0].record()
+        tq.quantize_append(L, cbk, cbv, None, k_new[s], v_new[s], dst_row, kc, vc)
+        e[1].record()
+        tq.rotate_sketch_query(L, cbk, None, qs[s], q_rot, None)
+        e[2].record()
+        tq.decode_partial(L, cbk, cbv, q_rot, None, kc, vc, seq_lens, ws, split_tokens=args.split_tokens)
+        e[3].record()
+        tq.decode_combine(L, cbv, ws, out, split_tokens=args.split_tokens)
+        e[4].record()
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.warmup, total):
+        step(s)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+
+    def mean_ms(i, j):
+        return float(np.mean([ev[s][i].elapsed_time(ev[s][j]) for s in range(args.warmup, total)]))
+
+    append_ms, rot_ms, partial_ms, combine_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
+    ms_step = t_total / args.steps * 1e3
+    alg_bytes = B * Hkv * N * (tq.vector_bytes(tq.FMT_PQ4, d) * 2)
+    achieved = alg_bytes / (partial_ms * 1e-3) / 1e9
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+        dstc = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dstc)
+        torch.cuda.synchronize()
+        _log("copy calibration: 3 x torch.mul over 1 GiB in, 1 GiB out")
+
+    cpu = None
+    if not args.no_cpu:
+        _log("timing the CPU oracle")
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    res = {
+        "metric": "compressed-KV decode-attention tokens/s; achieved HBM GB/s as % of peak",
+        "value": B * N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "c4: batch 8, 32 query / 8 KV heads, d 128, context 65536 (65535 prefilled + 1 appended "
+                        "per step), PQ4 4-bit K and V (68-byte blocks), seeded Gaussian K/V with 1% outlier channels",
+            "global_batch": B,
+            "seq_len": N,
+            "parallelism": "single GPU; split-K over context",
+            "splits": splits,
+            "cache_copies": args.copies,
+        },
+        "step_breakdown_ms": {"append": append_ms, "rotate_query": rot_ms, "decode_partial": partial_ms,
+                              "decode_combine": combine_ms},
+        "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
+        "roofline": {
+            "kernel": "decode_partial_kernel<PQ4,PQ4,128,4>",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": measured_traffic(),
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

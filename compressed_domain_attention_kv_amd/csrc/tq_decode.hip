@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <utility>
 
 #include "tq_device.h"
 
@@ -53,16 +54,36 @@ struct DecodeArgs {
     int split_len;
 };
 
+// Lane exchange inside a row of 16 lanes through DPP (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// Maximum / sum over the 64 lanes; every lane receives the same value (the
+// butterfly is symmetric, so the sum is bit-identical in all lanes).
 __device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, 64));
-    return x;
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppMirror>(x));
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-    return x;
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    x += dpp<kDppMirror>(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 
 // byte k of a register-resident little-endian byte run (k known at compile time after unrolling)
@@ -347,34 +368,341 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
     }
 }
 
-// One wavefront per (b, query head): merge split records, normalize, rotate back.
-template <int D, bool ROTATED>
-__global__ __launch_bounds__(64) void decode_combine_kernel(const float2* __restrict__ ml, const float* __restrict__ acc,
-                                                           float* __restrict__ out, int splits, DevCodebook cbv) {
-    constexpr int DPL = D / 64;
-    const int row = blockIdx.x, lane = threadIdx.x;
-    const float2* mr = ml + static_cast<size_t>(row) * splits;
-    float M = -INFINITY;
-    for (int s = lane; s < splits; s += 64) M = fmaxf(M, mr[s].x);
-    M = wave_max(M);
-    float o[DPL];
+// ---------------------------------------------------------------------------
+// Matrix-core variant for 4-bit PQ4 keys and values with G = 4 * NGRP query
+// heads per KV head.  The two per-tile contractions
+//     S[g][t] = sum_j q_rot[g][j] * c[code_tj]        (scores)
+//     O[g][j] += sum_t w[g][t] * c[vcode_tj]          (values)
+// have exactly four rows per head group, the shape of v_mfma_f32_4x4x1f32
+// (16 independent 4x4 outer products, fp32 in and out).  The query is held
+// with the A-broadcast layout: lane 4b+i of register r holds head i's
+// coordinate 16r+b, and CBSZ=4/ABID=b broadcasts block b's four values to
+// all blocks, so the rotated query of a head group costs d/16 registers and
+// the 64 softmax weights of a tile 4 registers.  The VALU only unpacks
+// codes, looks centroids up in an LDS pair table and runs the softmax.
+
+constexpr int kPwStride = 80;  // floats per head row of the weight buffer (bank spread for the transposed read)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+template <int D, int NGRP>
+struct SmemMfma {
+    static constexpr int VB = 68 * (D / 128);
+    float ktab[16];                      // centroid of each 4-bit code (16 banks: lookups never conflict)
+    float vtab[16];
+    alignas(16) uint8_t ktile[kWaves][kTile * VB];
+    alignas(16) uint8_t vtile[kWaves][kTile * VB];
+    float pw[kWaves][4 * NGRP * kPwStride];  // w[h][t] of the current tile, padded rows
+};
+
+template <int D, int NGRP>
+__global__ __launch_bounds__(kWaves * 64) void decode_partial_mfma_kernel(DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
+    using SM = SmemMfma<D, NGRP>;
+    constexpr int G = 4 * NGRP;
+    constexpr int VB = SM::VB;
+    constexpr int NB = D / 128;      // 68-byte blocks per vector
+    constexpr int NR = D / 16;       // query registers per head group
+    constexpr int DPL = D / 64;      // value coordinates per lane
+    constexpr int CH = kTile * VB / 16;           // 16-byte chunks per tile
+    constexpr int NCH = (CH + 63) / 64;           // chunks per lane
+    __shared__ __align__(16) SM sm;
+
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int hq0 = h * G;
+    int N = a.seq_lens[b];
+    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
+    const int start = s * a.split_len;
+    const int end = min(start + a.split_len, N);
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+
+    if (start >= end) {
+        for (int g = 0; g < G; ++g) {
+            const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
+            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
+            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
+        }
+        return;
+    }
+
+    if (tid < 16) {
+        sm.ktab[tid] = cbk.centroids[tid];
+        sm.vtab[tid] = cbv.centroids[tid];
+    }
+
+    // rotated query in the A-broadcast layout, scaled by log2(e)/sqrt(d)
+    const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+    const int bl = lane >> 2, il = lane & 3;
+    float qreg[NGRP][NR];
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] = 0.0f;
-    float L = 0.0f;
-    if (M != -INFINITY) {
-        const float* ar = acc + static_cast<size_t>(row) * splits * D;
-        for (int s = 0; s < splits; ++s) {
-            const float2 r = mr[s];
-            if (r.x == -INFINITY) continue;
-            const float f = exp2f(r.x - M);
-            L = fmaf(r.y, f, L);
+    for (int gr = 0; gr < NGRP; ++gr) {
+        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + 4 * gr + il) * D;
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) o[k] = fmaf(ar[static_cast<size_t>(s) * D + lane * DPL + k], f, o[k]);
+        for (int r = 0; r < NR; ++r) qreg[gr][r] = qg[16 * r + bl] * qscale;
+    }
+    __syncthreads();
+
+    float m_run[G], l_run[G];
+    f32x4 accv[NGRP][DPL];
+#pragma unroll
+    for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.0f; }
+#pragma unroll
+    for (int gr = 0; gr < NGRP; ++gr)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) accv[gr][k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
+    const u32x4* kstream = reinterpret_cast<const u32x4*>(a.k_cache + stream_row * VB);
+    const u32x4* vstream = reinterpret_cast<const u32x4*>(a.v_cache + stream_row * VB);
+    u32x4* kd = reinterpret_cast<u32x4*>(sm.ktile[w]);
+    u32x4* vd = reinterpret_cast<u32x4*>(sm.vtile[w]);
+    float* pw = sm.pw[w];
+
+    // register prefetch of the next tile (tiles are in bounds: t0 + 64 <= capacity)
+    u32x4 kpre[NCH], vpre[NCH];
+    int t0 = start + w * kTile;
+    if (t0 < end) {
+        const u32x4* ks = kstream + static_cast<size_t>(t0) * VB / 16;
+        const u32x4* vs = vstream + static_cast<size_t>(t0) * VB / 16;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m) {
+            const int c = (lane + 64 * m) < CH ? lane + 64 * m : CH - 1;
+            kpre[m] = ks[c];
+            vpre[m] = vs[c];
         }
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+
+    for (; t0 < end; t0 += kSplitQuantum) {
+        const int nv = min(kTile, end - t0);
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) o[k] *= inv;
+        for (int m = 0; m < NCH; ++m) {
+            const int c = lane + 64 * m;
+            if (c < CH) { kd[c] = kpre[m]; vd[c] = vpre[m]; }
+        }
+        if (t0 + kSplitQuantum < end) {
+            const u32x4* ks = kstream + static_cast<size_t>(t0 + kSplitQuantum) * VB / 16;
+            const u32x4* vs = vstream + static_cast<size_t>(t0 + kSplitQuantum) * VB / 16;
+#pragma unroll
+            for (int m = 0; m < NCH; ++m) {
+                const int c = (lane + 64 * m) < CH ? lane + 64 * m : CH - 1;
+                kpre[m] = ks[c];
+                vpre[m] = vs[c];
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+        // ---- scores: lane = token, register i of group gr = head 4*gr+i
+        const bool valid = lane < nv;
+        f32x4 sc[NGRP];
+#pragma unroll
+        for (int gr = 0; gr < NGRP; ++gr) sc[gr] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const uint8_t* kb = sm.ktile[w] + lane * VB;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb + 68 * blk);
+            const float nk = half_bits_to_float(kw[0] & 0xFFFFu);
+            f32x4 part[NGRP][2];
+#pragma unroll
+            for (int gr = 0; gr < NGRP; ++gr) part[gr][0] = part[gr][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int rr = 0; rr < 8; ++rr) {
+                // nibble * 4 = byte offset into the 16-entry table: even codes
+                // from (w << 2) & 0x3C.., odd codes from (w >> 2) & 0x3C..
+                const uint32_t w0 = kw[1 + 2 * rr], w1 = kw[2 + 2 * rr];
+                const uint32_t e0 = (w0 << 2) & 0x3C3C3C3Cu, o0 = (w0 >> 2) & 0x3C3C3C3Cu;
+                const uint32_t e1 = (w1 << 2) & 0x3C3C3C3Cu, o1 = (w1 >> 2) & 0x3C3C3C3Cu;
+                const char* kt = reinterpret_cast<const char*>(sm.ktab);
+                float cv[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    cv[2 * q] = *reinterpret_cast<const float*>(kt + ((e0 >> (8 * q)) & 0xFFu));
+                    cv[2 * q + 1] = *reinterpret_cast<const float*>(kt + ((o0 >> (8 * q)) & 0xFFu));
+                    cv[8 + 2 * q] = *reinterpret_cast<const float*>(kt + ((e1 >> (8 * q)) & 0xFFu));
+                    cv[8 + 2 * q + 1] = *reinterpret_cast<const float*>(kt + ((o1 >> (8 * q)) & 0xFFu));
+                }
+                const int r = 8 * blk + rr;
+                static_for<16>([&](auto bc) {
+                    constexpr int B = decltype(bc)::value;
+                    const float val = cv[B];
+#pragma unroll
+                    for (int gr = 0; gr < NGRP; ++gr)
+                        part[gr][rr & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(qreg[gr][r], val, part[gr][rr & 1], 4, B, 0);
+                });
+            }
+#pragma unroll
+            for (int gr = 0; gr < NGRP; ++gr) sc[gr] += nk * (part[gr][0] + part[gr][1]);
+        }
+
+        // ---- online softmax per head; w = p * value norm to LDS, transposed
+        const float nvn = half_bits_to_float(*reinterpret_cast<const uint16_t*>(sm.vtile[w] + lane * VB));
+#pragma unroll
+        for (int gr = 0; gr < NGRP; ++gr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int g = 4 * gr + i;
+                const float tv = valid ? sc[gr][i] : -INFINITY;
+                if (a.scores && valid)
+                    a.scores[(static_cast<size_t>(b) * a.hq + hq0 + g) * a.capacity + t0 + lane] = tv * kLn2;
+                const float mt = wave_max(tv);
+                const float mn = fmaxf(m_run[g], mt);
+                const float p = valid ? exp2f(tv - mn) : 0.0f;
+                const float alpha = exp2f(m_run[g] - mn);
+                l_run[g] = fmaf(l_run[g], alpha, p);  // per-lane partial sum, reduced once per split
+                m_run[g] = mn;
+#pragma unroll
+                for (int k = 0; k < DPL; ++k) accv[gr][k][i] *= alpha;
+                pw[g * kPwStride + lane] = valid ? p * nvn : 0.0f;
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float wreg[NGRP][4];
+#pragma unroll
+        for (int gr = 0; gr < NGRP; ++gr)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wreg[gr][r] = pw[(4 * gr + il) * kPwStride + 16 * r + bl];
+
+        // ---- values: lane owns coordinates DPL*lane .. DPL*lane+DPL-1
+        const int vblk = (DPL * lane) / 128;
+        const int voff = 68 * vblk + 4 + ((DPL * lane) % 128) / 2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            static_for<16>([&](auto bc) {
+                constexpr int B = decltype(bc)::value;
+                const uint8_t* vb = sm.vtile[w] + (16 * r + B) * VB + voff;
+                const char* vt = reinterpret_cast<const char*>(sm.vtab);
+                float val[DPL];
+                if constexpr (DPL == 2) {
+                    const uint32_t by = vb[0];
+                    val[0] = *reinterpret_cast<const float*>(vt + ((by << 2) & 0x3Cu));
+                    val[1] = *reinterpret_cast<const float*>(vt + ((by >> 2) & 0x3Cu));
+                } else {
+                    const uint32_t two = *reinterpret_cast<const uint16_t*>(vb);
+                    val[0] = *reinterpret_cast<const float*>(vt + ((two << 2) & 0x3Cu));
+                    val[1] = *reinterpret_cast<const float*>(vt + ((two >> 2) & 0x3Cu));
+                    val[2] = *reinterpret_cast<const float*>(vt + ((two >> 6) & 0x3Cu));
+                    val[3] = *reinterpret_cast<const float*>(vt + ((two >> 10) & 0x3Cu));
+                }
+#pragma unroll
+                for (int gr = 0; gr < NGRP; ++gr)
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k)
+                        accv[gr][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(wreg[gr][r], val[k], accv[gr][k], 4, B, 0);
+            });
+        }
+    }
+
+    // ---- merge the wavefronts of the workgroup and write the split record
+#pragma unroll
+    for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(&sm.ktile[0][0]);
+    static_assert(sizeof(sm.ktile) + sizeof(sm.vtile) >= sizeof(float) * kWaves * G * (2 + D), "merge buffer");
+#pragma unroll
+    for (int gr = 0; gr < NGRP; ++gr)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = 4 * gr + i;
+            float* r = red + (w * G + g) * (2 + D);
+            if (lane == 0) { r[0] = m_run[g]; r[1] = l_run[g]; }
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) r[2 + lane * DPL + k] = accv[gr][k][i];
+        }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
+        const int g = idx / D, j = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * G + g) * (2 + D)]);
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float* r = red + (ww * G + g) * (2 + D);
+            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+            L = fmaf(r[1], f, L);
+            A = fmaf(r[2 + j], f, A);
+        }
+        const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
+        a.acc[rec * D + j] = A;
+        if (j == 0) a.ml[rec] = make_float2(M, L);
+    }
+}
+
+// One workgroup per (b, query head): merge the split records, normalize and,
+// for rotated value formats, rotate back once.  Each thread owns four
+// coordinates of one split group, so the record rows stream in with 16-byte
+// loads from many splits at once.
+constexpr int kCombineThreads = 256;
+
+template <int D, bool ROTATED>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float2* __restrict__ ml,
+                                                                        const float* __restrict__ acc,
+                                                                        float* __restrict__ out, int splits,
+                                                                        DevCodebook cbv) {
+    constexpr int TPR = D / 4;                    // threads per record row
+    constexpr int NGS = kCombineThreads / TPR;    // split groups
+    constexpr int DPL = D / 64;
+    __shared__ float wave_m[kCombineThreads / 64];
+    __shared__ float4 part[NGS][TPR];
+    __shared__ float part_l[NGS];
+    __shared__ float o_sh[D];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const float2* mr = ml + static_cast<size_t>(row) * splits;
+    float M = -INFINITY;
+    for (int s = tid; s < splits; s += kCombineThreads) M = fmaxf(M, mr[s].x);
+    M = wave_max(M);
+    if (lane == 0) wave_m[tid >> 6] = M;
+    __syncthreads();
+    M = fmaxf(fmaxf(wave_m[0], wave_m[1]), fmaxf(wave_m[2], wave_m[3]));
+    const int grp = tid / TPR, c = tid % TPR;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float L = 0.0f;
+    if (M != -INFINITY) {
+        const float4* ar = reinterpret_cast<const float4*>(acc) + static_cast<size_t>(row) * splits * TPR + c;
+#pragma unroll 4
+        for (int s = grp; s < splits; s += NGS) {
+            const float2 r = mr[s];
+            const float f = r.x == -INFINITY ? 0.0f : exp2f(r.x - M);
+            const float4 v = ar[static_cast<size_t>(s) * TPR];
+            L = fmaf(r.y, f, L);
+            o.x = fmaf(v.x, f, o.x); o.y = fmaf(v.y, f, o.y); o.z = fmaf(v.z, f, o.z); o.w = fmaf(v.w, f, o.w);
+        }
+    }
+    part[grp][c] = o;
+    if (c == 0) part_l[grp] = L;
+    __syncthreads();
+    if (tid < TPR) {
+        float4 t = part[0][tid];
+        float Lt = part_l[0];
+#pragma unroll
+        for (int g = 1; g < NGS; ++g) {
+            const float4 u = part[g][tid];
+            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
+            Lt += part_l[g];
+        }
+        const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
+        o_sh[4 * tid] = t.x * inv;
+        o_sh[4 * tid + 1] = t.y * inv;
+        o_sh[4 * tid + 2] = t.z * inv;
+        o_sh[4 * tid + 3] = t.w * inv;
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    float v[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) v[k] = o_sh[DPL * lane + k];
     if constexpr (ROTATED) {
         // o <- Pi^T o = diag(s) H o / sqrt(d); element j = DPL*lane + k
 #pragma unroll
@@ -382,25 +710,25 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float2* __rest
 #pragma unroll
             for (int k = 0; k < DPL; ++k)
                 if ((k & st) == 0) {
-                    const float x = o[k], y = o[k + st];
-                    o[k] = x + y;
-                    o[k + st] = x - y;
+                    const float x = v[k], y = v[k + st];
+                    v[k] = x + y;
+                    v[k + st] = x - y;
                 }
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) {
             const bool upper = (lane & m) != 0;
 #pragma unroll
             for (int k = 0; k < DPL; ++k) {
-                const float p = __shfl_xor(o[k], m, 64);
-                o[k] = upper ? (p - o[k]) : (o[k] + p);
+                const float p = __shfl_xor(v[k], m, 64);
+                v[k] = upper ? (p - v[k]) : (v[k] + p);
             }
         }
         constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) o[k] *= kInvSqrtD * rotation_sign(cbv, DPL * lane + k);
+        for (int k = 0; k < DPL; ++k) v[k] *= kInvSqrtD * rotation_sign(cbv, DPL * lane + k);
     }
 #pragma unroll
-    for (int k = 0; k < DPL; ++k) out[static_cast<size_t>(row) * D + DPL * lane + k] = o[k];
+    for (int k = 0; k < DPL; ++k) out[static_cast<size_t>(row) * D + DPL * lane + k] = v[k];
 }
 
 int auto_split_tokens(const tq_layout* L) {
@@ -430,9 +758,22 @@ int launch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& c
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+template <int D, int NGRP>
+int launch_partial_mfma(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+                        hipStream_t st) {
+    dim3 grid(a.splits, L->n_kv_heads, L->batch);
+    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, NGRP>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
+                       to_dev(cbv));
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 template <int KF, int VF, int D>
 int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                    hipStream_t st) {
+    if constexpr (KF == TQ_FMT_PQ4 && VF == TQ_FMT_PQ4) {
+        if (G == 4) return launch_partial_mfma<D, 1>(a, L, cbk, cbv, st);
+        if (G == 8) return launch_partial_mfma<D, 2>(a, L, cbk, cbv, st);
+    }
     switch (G) {
         case 1: return launch_partial<KF, VF, D, 1>(a, L, cbk, cbv, st);
         case 2: return launch_partial<KF, VF, D, 2>(a, L, cbk, cbv, st);
@@ -534,11 +875,11 @@ int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_toke
     const bool rot = L->v_format != TQ_FMT_GQ2V;
     const DevCodebook c = to_dev(*cbv);
     if (L->head_dim == 128) {
-        if (rot) hipLaunchKernelGGL((decode_combine_kernel<128, true>), dim3(rows), dim3(64), 0, stream, ml, acc, out, splits, c);
-        else hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3(rows), dim3(64), 0, stream, ml, acc, out, splits, c);
+        if (rot) hipLaunchKernelGGL((decode_combine_kernel<128, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
+        else hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
     } else {
-        if (rot) hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3(rows), dim3(64), 0, stream, ml, acc, out, splits, c);
-        else hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3(rows), dim3(64), 0, stream, ml, acc, out, splits, c);
+        if (rot) hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
+        else hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
     }
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
