@@ -368,22 +368,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
     }
 }
 
-// ---------------------------------------------------------------------------
-// Matrix-core variant for 4-bit PQ4 keys and values with G = 4 * NGRP query
-// heads per KV head.  The two per-tile contractions
-//     S[g][t] = sum_j q_rot[g][j] * c[code_tj]        (scores)
-//     O[g][j] += sum_t w[g][t] * c[vcode_tj]          (values)
-// have exactly four rows per head group, the shape of v_mfma_f32_4x4x1f32
-// (16 independent 4x4 outer products, fp32 in and out).  The query is held
-// with the A-broadcast layout: lane 4b+i of register r holds head i's
-// coordinate 16r+b, and CBSZ=4/ABID=b broadcasts block b's four values to
-// all blocks, so the rotated query of a head group costs d/16 registers and
-// the 64 softmax weights of a tile 4 registers.  The VALU only unpacks
-// codes, looks centroids up in an LDS pair table and runs the softmax.
-
-constexpr int kPwStride = 80;  // floats per head row of the weight buffer (bank spread for the transposed read)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 template <int... I, typename F>
 __device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
@@ -394,30 +381,174 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
-template <int D, int NGRP>
-struct SmemMfma {
-    static constexpr int VB = 68 * (D / 128);
-    float ktab[16];                      // centroid of each 4-bit code (16 banks: lookups never conflict)
-    float vtab[16];
-    alignas(16) uint8_t ktile[kWaves][kTile * VB];
-    alignas(16) uint8_t vtile[kWaves][kTile * VB];
-    float pw[kWaves][4 * NGRP * kPwStride];  // w[h][t] of the current tile, padded rows
+// Byte offset into a 32-entry table from byte Q of a pre-shifted code word:
+// (byte_Q(x) & 0x7C), one sub-dword (SDWA) VALU operation.  The result only
+// ever feeds an LDS address.
+#define TQ_NIBBLE_OFFSET(Q)                                                                              \
+    template <>                                                                                          \
+    __device__ __forceinline__ uint32_t nibble_offset<Q>(uint32_t x) {                                   \
+        uint32_t r;                                                                                      \
+        asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_" #Q \
+            : "=v"(r) : "v"(0x7Cu), "v"(x));                                                             \
+        return r;                                                                                        \
+    }
+template <int Q>
+__device__ __forceinline__ uint32_t nibble_offset(uint32_t x);
+TQ_NIBBLE_OFFSET(0)
+TQ_NIBBLE_OFFSET(1)
+TQ_NIBBLE_OFFSET(2)
+TQ_NIBBLE_OFFSET(3)
+#undef TQ_NIBBLE_OFFSET
+
+// The eight table entries of a dword of PQ4 codes (coordinate 2q = low
+// nibble of byte q) from two 32-entry tables, lo[k] = T[k & 15] and
+// hi[k] = T[k >> 1]: with xl = w << 2, byte q of xl masked by 0x7C is
+// (byte_q & 31) * 4; with xh = w >> 1 it is (byte_q >> 3) * 4.  A 32-entry
+// table of words occupies each of the 32 LDS banks once, so the 64 lanes'
+// lookups never conflict.
+template <typename E>
+__device__ __forceinline__ void decode_word(uint32_t w, const char* lo, const char* hi, E (&c)[8]) {
+    const uint32_t xl = w << 2, xh = w >> 1;
+    static_for<4>([&](auto qc) {
+        constexpr int Q = decltype(qc)::value;
+        c[2 * Q] = *reinterpret_cast<const E*>(lo + nibble_offset<Q>(xl));
+        c[2 * Q + 1] = *reinterpret_cast<const E*>(hi + nibble_offset<Q>(xh));
+    });
+}
+
+// Table entries of nibbles 4H..4H+3 of a code word, given xl = w << 2 and
+// xh = w >> 1 (the same tables and masks as decode_word).
+template <int H>
+__device__ __forceinline__ void decode_half(uint32_t xl, uint32_t xh, const char* lo, const char* hi, uint32_t (&c)[4]) {
+    c[0] = *reinterpret_cast<const uint32_t*>(lo + nibble_offset<2 * H>(xl));
+    c[1] = *reinterpret_cast<const uint32_t*>(hi + nibble_offset<2 * H>(xh));
+    c[2] = *reinterpret_cast<const uint32_t*>(lo + nibble_offset<2 * H + 1>(xl));
+    c[3] = *reinterpret_cast<const uint32_t*>(hi + nibble_offset<2 * H + 1>(xh));
+}
+
+// HBM -> LDS copy of one tile with global_load_lds_dwordx4: copy m moves
+// bytes [1024 m, 1024 m + 1024) and lands lane l's 16 bytes at dst + 1024 m
+// + 16 l.  The copies count in vmcnt until their data is in LDS.
+template <int BYTES>
+__device__ __forceinline__ void tile_to_lds(const uint8_t* src, uint8_t* dst, int lane) {
+    constexpr int N = (BYTES + 1023) / 1024, TAIL = (BYTES - 1024 * (N - 1)) / 16;
+    static_for<N>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        if (m < N - 1 || TAIL == 64 || lane < TAIL)
+            __builtin_amdgcn_global_load_lds(src + 1024 * m + 16 * lane,
+                                             reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                                 reinterpret_cast<uintptr_t>(dst + 1024 * m)),
+                                             16, 0, 0);
+    });
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Program-order point between phases that touch the same LDS bytes through
+// differently typed accesses (no instruction is emitted).
+__device__ __forceinline__ void lds_order() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Online-softmax rescale threshold (log2 units): the running reference m is
+// moved to the maximum only when some score exceeds m + kRescaleSlack, so
+// weights 2^(s - m) stay below 2^kRescaleSlack and a tile without a new
+// maximum costs one compare-and-ballot.  Any reference gives the same
+// softmax; only overflow has to be excluded.
+constexpr float kRescaleSlack = 8.0f;
+
+// MFMA jobs whose centroid lookups are in flight ahead of the product that
+// consumes the oldest (four lookups each; lgkmcnt counts at most 15).
+constexpr int kLookahead = 3;
+
+// bf16 bits nearest to a finite float
+__device__ __forceinline__ uint32_t bf16_rn(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi), packed as (lo << 16) | hi
+__device__ __forceinline__ uint32_t bf16_split(float x) {
+    const uint32_t h = bf16_rn(x);
+    return (bf16_rn(x - __uint_as_float(h << 16)) << 16) | h;
+}
+// the upper 16 bits of x in both halves
+__device__ __forceinline__ uint32_t dup_hi16(uint32_t x) { return __builtin_amdgcn_perm(x, x, 0x03020302u); }
+
+// Sum / maximum over each row of 16 lanes, the result in every lane of the row.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    x += dpp<kDppMirror>(x);
+    return x;
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppMirror>(x));
+    return x;
+}
+
+template <int D, int G>
+struct Bf16Cfg {
+    static constexpr int VB = 68 * (D / 128);     // bytes per token and tensor
+    static constexpr int NB = D / 128;            // 68-byte blocks per vector
+    static constexpr int BYTES = kTile * VB;      // one tensor's tile, a multiple of 16
+    static constexpr int NDMA = (BYTES + 1023) / 1024;
+    static constexpr int NTB = kTile / 16;        // 16-token blocks per tile
+    static constexpr int ROWS = 2 * G;            // MFMA rows in use: (head, hi/lo)
+    static constexpr int WA = NB * NTB * ROWS * 16 + (ROWS < 16 ? 16 : 0);  // weight words per wavefront (+ zero row)
 };
 
-template <int D, int NGRP>
-__global__ __launch_bounds__(kWaves * 64) void decode_partial_mfma_kernel(DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
-    using SM = SmemMfma<D, NGRP>;
-    constexpr int G = 4 * NGRP;
-    constexpr int VB = SM::VB;
-    constexpr int NB = D / 128;      // 68-byte blocks per vector
-    constexpr int NR = D / 16;       // query registers per head group
-    constexpr int DPL = D / 64;      // value coordinates per lane
-    constexpr int CH = kTile * VB / 16;           // 16-byte chunks per tile
-    constexpr int NCH = (CH + 63) / 64;           // chunks per lane
+template <int D, int G>
+struct SmemBf16 {
+    using C = Bf16Cfg<D, G>;
+    uint32_t klo[32], khi[32], vlo[32], vhi[32];  // centroid pairs: lo[k] = P[k & 15], hi[k] = P[k >> 1]
+    alignas(16) uint8_t kbuf[kWaves][C::BYTES];
+    alignas(16) uint8_t vbuf[kWaves][C::BYTES];
+    alignas(16) uint32_t wa[kWaves][C::WA];       // value-product A operand [blk][tb][row][token] (+ zero row)
+    alignas(16) u32x4 qa[8 * C::NB][64];          // score A operand per chunk and lane (shared by the wavefronts)
+};
+
+// ---------------------------------------------------------------------------
+// PQ4 keys and values, G = 4 or 8 query heads per KV head, on the bf16 matrix
+// cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Every fp32 operand x
+// enters as the pair hi = bf16(x), lo = bf16(x - hi), so the operands carry
+// 16 significant bits and the products and sums are exact-in-fp32 MFMA
+// arithmetic:
+//   scores  D[(h,r)][t] = sum_{j,s} q_r[h][j] * c_s[code_tj]
+//           with rows (head h, r = hi/lo of the query), columns 16 tokens and
+//           k = (coordinate j, s = hi/lo of the centroid); the score of head h
+//           is D[(h,hi)] + D[(h,lo)] times the key block norm;
+//   values  D[(h,r)][n] += sum_{t,s} w_r[h][t] * c_s[vcode_t,8n+cb]
+//           with columns the 16 code words n of a 128-coordinate block, one
+//           accumulator per nibble position cb, k = (token, s).
+// Centroid pairs come from 32-entry LDS tables (lookup = one SDWA mask and
+// one ds_read_b32); the query pairs sit in registers for the whole split; the
+// softmax writes the weight pairs to LDS in the A-operand layout.  Tiles move
+// HBM -> LDS with direct-to-LDS loads, double buffered by tensor: the next
+// keys are requested once the scores are done with the current ones, the
+// next values after the value products.
+template <int D, int G>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_partial_bf16_kernel(DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
+    static_assert(G == 4 || G == 8, "two heads per 16-lane row group");
+    using C = Bf16Cfg<D, G>;
+    using SM = SmemBf16<D, G>;
+    constexpr int VB = C::VB, NB = C::NB, NTB = C::NTB, ROWS = C::ROWS, NDMA = C::NDMA;
     __shared__ __align__(16) SM sm;
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;  // MFMA column / row (A side) and k-group
     const int hq0 = h * G;
     int N = a.seq_lens[b];
     N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
@@ -426,215 +557,293 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_mfma_kernel(Decode
     const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
 
     if (start >= end) {
-        for (int g = 0; g < G; ++g) {
-            const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
+        for (int gg = 0; gg < G; ++gg) {
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
             if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
             for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
         }
         return;
     }
 
-    if (tid < 16) {
-        sm.ktab[tid] = cbk.centroids[tid];
-        sm.vtab[tid] = cbv.centroids[tid];
+    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
+    const uint8_t* kstream = a.k_cache + stream_row * VB;
+    const uint8_t* vstream = a.v_cache + stream_row * VB;
+    uint8_t* kbuf = sm.kbuf[w];
+    uint8_t* vbuf = sm.vbuf[w];
+    uint32_t* wa = sm.wa[w];
+
+    // first tile of this wavefront in flight before anything else
+    int t0 = start + w * kTile;
+    if (t0 < end) {
+        tile_to_lds<C::BYTES>(kstream + static_cast<size_t>(t0) * VB, kbuf, lane);
+        tile_to_lds<C::BYTES>(vstream + static_cast<size_t>(t0) * VB, vbuf, lane);
     }
 
-    // rotated query in the A-broadcast layout, scaled by log2(e)/sqrt(d)
-    const float qscale = kLog2e / sqrtf(static_cast<float>(D));
-    const int bl = lane >> 2, il = lane & 3;
-    float qreg[NGRP][NR];
+    if (tid < 32) {
+        sm.klo[tid] = bf16_split(cbk.centroids[tid & 15]);
+        sm.khi[tid] = bf16_split(cbk.centroids[tid >> 1]);
+        sm.vlo[tid] = bf16_split(cbv.centroids[tid & 15]);
+        sm.vhi[tid] = bf16_split(cbv.centroids[tid >> 1]);
+    }
+    if (ROWS < 16 && lane < 16) wa[C::WA - 16 + lane] = 0u;
+
+    // query A operand: row m = n = (head m/2, r = m&1), k-group g holds
+    // coordinates 128 blk + 32 g + 4 cc + u (u = 0..3) of chunk c = 8 blk + cc,
+    // each as the bf16 half r of q * log2(e)/sqrt(d), duplicated for s = hi/lo.
+    if (w == 0) {
+        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+        const int hm = n >> 1, r = n & 1;
+        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + (hm < G ? hm : 0)) * D;
 #pragma unroll
-    for (int gr = 0; gr < NGRP; ++gr) {
-        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + 4 * gr + il) * D;
+        for (int c = 0; c < NB * 8; ++c) {
+            u32x4 v;
 #pragma unroll
-        for (int r = 0; r < NR; ++r) qreg[gr][r] = qg[16 * r + bl] * qscale;
+            for (int u = 0; u < 4; ++u) {
+                const int j = 128 * (c >> 3) + 32 * g + 4 * (c & 7) + u;
+                const uint32_t pr = bf16_split(qg[j] * qscale);
+                const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
+                v[u] = n < ROWS ? (half | (half << 16)) : 0u;
+            }
+            sm.qa[c][lane] = v;
+        }
     }
     __syncthreads();
 
-    float m_run[G], l_run[G];
-    f32x4 accv[NGRP][DPL];
+    // per lane: heads 2g and 2g+1 (when < G); inactive rows keep m = 0, p = 0
+    float m_run[2], l_run[2];
 #pragma unroll
-    for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; l_run[g] = 0.0f; }
-#pragma unroll
-    for (int gr = 0; gr < NGRP; ++gr)
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) accv[gr][k] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
-    const u32x4* kstream = reinterpret_cast<const u32x4*>(a.k_cache + stream_row * VB);
-    const u32x4* vstream = reinterpret_cast<const u32x4*>(a.v_cache + stream_row * VB);
-    u32x4* kd = reinterpret_cast<u32x4*>(sm.ktile[w]);
-    u32x4* vd = reinterpret_cast<u32x4*>(sm.vtile[w]);
-    float* pw = sm.pw[w];
-
-    // register prefetch of the next tile (tiles are in bounds: t0 + 64 <= capacity)
-    u32x4 kpre[NCH], vpre[NCH];
-    int t0 = start + w * kTile;
-    if (t0 < end) {
-        const u32x4* ks = kstream + static_cast<size_t>(t0) * VB / 16;
-        const u32x4* vs = vstream + static_cast<size_t>(t0) * VB / 16;
-#pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-            const int c = (lane + 64 * m) < CH ? lane + 64 * m : CH - 1;
-            kpre[m] = ks[c];
-            vpre[m] = vs[c];
-        }
+    for (int e = 0; e < 2; ++e) {
+        m_run[e] = (2 * g + e < G) ? -INFINITY : 0.0f;
+        l_run[e] = 0.0f;
     }
+    f32x4 acc[NB][8];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) acc[blk][cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const char* klo = reinterpret_cast<const char*>(sm.klo);
+    const char* khi = reinterpret_cast<const char*>(sm.khi);
+    const char* vlo = reinterpret_cast<const char*>(sm.vlo);
+    const char* vhi = reinterpret_cast<const char*>(sm.vhi);
+    // value-product A operand of this lane: row n (zero row when n >= ROWS), tokens 4g..4g+3
+    const uint32_t* wa_rd = n < ROWS ? wa + n * 16 + 4 * g : wa + C::WA - 16 + 4 * g;
+    const int wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
 
     for (; t0 < end; t0 += kSplitQuantum) {
         const int nv = min(kTile, end - t0);
+        const bool has_next = t0 + kSplitQuantum < end;
+        wait_vmcnt<NDMA>();  // this tile's keys (its values may still be in flight)
+
+        // ---- scores: column n = token 16 tb + n, k-group g = 32 coordinates per
+        // block.  Step S = (blk, c) multiplies chunk c of block blk (nibbles
+        // 4(c&1)..+3 of key word c/2) for the four token blocks; the lookups of
+        // step S+1 are issued before the products of step S.
+        uint32_t kw[NTB][NB][4];
+        float nk[NTB][NB];
 #pragma unroll
-        for (int m = 0; m < NCH; ++m) {
-            const int c = lane + 64 * m;
-            if (c < CH) { kd[c] = kpre[m]; vd[c] = vpre[m]; }
-        }
-        if (t0 + kSplitQuantum < end) {
-            const u32x4* ks = kstream + static_cast<size_t>(t0 + kSplitQuantum) * VB / 16;
-            const u32x4* vs = vstream + static_cast<size_t>(t0 + kSplitQuantum) * VB / 16;
+        for (int tb = 0; tb < NTB; ++tb) {
+            const uint8_t* kt = kbuf + (16 * tb + n) * VB;
 #pragma unroll
-            for (int m = 0; m < NCH; ++m) {
-                const int c = (lane + 64 * m) < CH ? lane + 64 * m : CH - 1;
-                kpre[m] = ks[c];
-                vpre[m] = vs[c];
+            for (int blk = 0; blk < NB; ++blk) {
+                nk[tb][blk] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(kt + 68 * blk));
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(kt + 68 * blk + 4 + 16 * g);
+#pragma unroll
+                for (int d = 0; d < 4; ++d) kw[tb][blk][d] = src[d];
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // ---- scores: lane = token, register i of group gr = head 4*gr+i
-        const bool valid = lane < nv;
-        f32x4 sc[NGRP];
+        f32x4 dsc[NTB][NB];
 #pragma unroll
-        for (int gr = 0; gr < NGRP; ++gr) sc[gr] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        const uint8_t* kb = sm.ktile[w] + lane * VB;
+        for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            const uint32_t* kw = reinterpret_cast<const uint32_t*>(kb + 68 * blk);
-            const float nk = half_bits_to_float(kw[0] & 0xFFFFu);
-            f32x4 part[NGRP][2];
-#pragma unroll
-            for (int gr = 0; gr < NGRP; ++gr) part[gr][0] = part[gr][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                // nibble * 4 = byte offset into the 16-entry table: even codes
-                // from (w << 2) & 0x3C.., odd codes from (w >> 2) & 0x3C..
-                const uint32_t w0 = kw[1 + 2 * rr], w1 = kw[2 + 2 * rr];
-                const uint32_t e0 = (w0 << 2) & 0x3C3C3C3Cu, o0 = (w0 >> 2) & 0x3C3C3C3Cu;
-                const uint32_t e1 = (w1 << 2) & 0x3C3C3C3Cu, o1 = (w1 >> 2) & 0x3C3C3C3Cu;
-                const char* kt = reinterpret_cast<const char*>(sm.ktab);
-                float cv[16];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    cv[2 * q] = *reinterpret_cast<const float*>(kt + ((e0 >> (8 * q)) & 0xFFu));
-                    cv[2 * q + 1] = *reinterpret_cast<const float*>(kt + ((o0 >> (8 * q)) & 0xFFu));
-                    cv[8 + 2 * q] = *reinterpret_cast<const float*>(kt + ((e1 >> (8 * q)) & 0xFFu));
-                    cv[8 + 2 * q + 1] = *reinterpret_cast<const float*>(kt + ((o1 >> (8 * q)) & 0xFFu));
+            for (int blk = 0; blk < NB; ++blk) dsc[tb][blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        {
+            // job J = S * NTB + tb: chunk S of token block tb, four lookups;
+            // the lookups run kLookahead jobs ahead of the products, which
+            // keeps the LDS results in flight within lgkmcnt's range of 15.
+            constexpr int NS = NB * 8, NJ = NS * NTB, R = kLookahead + 1;
+            uint32_t ring[R][4];
+            u32x4 qk[2];
+            static_for<NJ + kLookahead>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int S = J / NTB, TB = J % NTB, BLK = S / 8, CC = S % 8;
+                    if constexpr (TB == 0) qk[S & 1] = sm.qa[S][lane];
+                    const uint32_t x = kw[TB][BLK][CC >> 1];
+                    decode_half<CC & 1>(x << 2, x >> 1, klo, khi, ring[J % R]);
                 }
-                const int r = 8 * blk + rr;
-                static_for<16>([&](auto bc) {
-                    constexpr int B = decltype(bc)::value;
-                    const float val = cv[B];
-#pragma unroll
-                    for (int gr = 0; gr < NGRP; ++gr)
-                        part[gr][rr & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(qreg[gr][r], val, part[gr][rr & 1], 4, B, 0);
-                });
-            }
-#pragma unroll
-            for (int gr = 0; gr < NGRP; ++gr) sc[gr] += nk * (part[gr][0] + part[gr][1]);
-        }
-
-        // ---- online softmax per head; w = p * value norm to LDS, transposed
-        const float nvn = half_bits_to_float(*reinterpret_cast<const uint16_t*>(sm.vtile[w] + lane * VB));
-#pragma unroll
-        for (int gr = 0; gr < NGRP; ++gr) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int g = 4 * gr + i;
-                const float tv = valid ? sc[gr][i] : -INFINITY;
-                if (a.scores && valid)
-                    a.scores[(static_cast<size_t>(b) * a.hq + hq0 + g) * a.capacity + t0 + lane] = tv * kLn2;
-                const float mt = wave_max(tv);
-                const float mn = fmaxf(m_run[g], mt);
-                const float p = valid ? exp2f(tv - mn) : 0.0f;
-                const float alpha = exp2f(m_run[g] - mn);
-                l_run[g] = fmaf(l_run[g], alpha, p);  // per-lane partial sum, reduced once per split
-                m_run[g] = mn;
-#pragma unroll
-                for (int k = 0; k < DPL; ++k) accv[gr][k][i] *= alpha;
-                pw[g * kPwStride + lane] = valid ? p * nvn : 0.0f;
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float wreg[NGRP][4];
-#pragma unroll
-        for (int gr = 0; gr < NGRP; ++gr)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) wreg[gr][r] = pw[(4 * gr + il) * kPwStride + 16 * r + bl];
-
-        // ---- values: lane owns coordinates DPL*lane .. DPL*lane+DPL-1
-        const int vblk = (DPL * lane) / 128;
-        const int voff = 68 * vblk + 4 + ((DPL * lane) % 128) / 2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            static_for<16>([&](auto bc) {
-                constexpr int B = decltype(bc)::value;
-                const uint8_t* vb = sm.vtile[w] + (16 * r + B) * VB + voff;
-                const char* vt = reinterpret_cast<const char*>(sm.vtab);
-                float val[DPL];
-                if constexpr (DPL == 2) {
-                    const uint32_t by = vb[0];
-                    val[0] = *reinterpret_cast<const float*>(vt + ((by << 2) & 0x3Cu));
-                    val[1] = *reinterpret_cast<const float*>(vt + ((by >> 2) & 0x3Cu));
-                } else {
-                    const uint32_t two = *reinterpret_cast<const uint16_t*>(vb);
-                    val[0] = *reinterpret_cast<const float*>(vt + ((two << 2) & 0x3Cu));
-                    val[1] = *reinterpret_cast<const float*>(vt + ((two >> 2) & 0x3Cu));
-                    val[2] = *reinterpret_cast<const float*>(vt + ((two >> 6) & 0x3Cu));
-                    val[3] = *reinterpret_cast<const float*>(vt + ((two >> 10) & 0x3Cu));
+                if constexpr (J >= kLookahead) {
+                    constexpr int M = J - kLookahead, S = M / NTB, TB = M % NTB, BLK = S / 8;
+                    dsc[TB][BLK] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, qk[S & 1]),
+                        __builtin_bit_cast(bf16x8, u32x4{ring[M % R][0], ring[M % R][1], ring[M % R][2], ring[M % R][3]}),
+                        dsc[TB][BLK], 0, 0, 0);
                 }
-#pragma unroll
-                for (int gr = 0; gr < NGRP; ++gr)
-#pragma unroll
-                    for (int k = 0; k < DPL; ++k)
-                        accv[gr][k] = __builtin_amdgcn_mfma_f32_4x4x1f32(wreg[gr][r], val[k], accv[gr][k], 4, B, 0);
+                __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
             });
         }
+        lds_order();
+        // every key byte of this tile has been read: the next tile's keys may land
+        if (has_next) tile_to_lds<C::BYTES>(kstream + static_cast<size_t>(t0 + kSplitQuantum) * VB, kbuf, lane);
+
+        if (has_next) wait_vmcnt<NDMA>(); else wait_vmcnt<0>();  // this tile's values
+
+        // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
+        // (G is even, so both heads of a lane exist exactly when 2g < G)
+        const bool live = 2 * g < G;
+        float tv[NTB][2];
+        float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const bool ok = live && 16 * tb + n < nv;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                float sc = 0.0f;
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) sc += nk[tb][blk] * (dsc[tb][blk][2 * e] + dsc[tb][blk][2 * e + 1]);
+                tv[tb][e] = ok ? sc : -INFINITY;
+                mx[e] = fmaxf(mx[e], tv[tb][e]);
+            }
+        }
+        if (a.scores) {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    if (tv[tb][e] != -INFINITY)
+                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 2 * g + e) * a.capacity + t0 + 16 * tb + n] =
+                            tv[tb][e] * kLn2;
+        }
+        if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kRescaleSlack || mx[1] > m_run[1] + kRescaleSlack) != 0) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float mn = fmaxf(m_run[e], row16_max(mx[e]));
+                const float alpha = mn == m_run[e] ? 1.0f : __builtin_amdgcn_exp2f(m_run[e] - mn);  // -inf start gives 0
+                l_run[e] *= alpha;
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                    for (int cb = 0; cb < 8; ++cb) {
+                        acc[blk][cb][2 * e] *= alpha;
+                        acc[blk][cb][2 * e + 1] *= alpha;
+                    }
+                m_run[e] = mn;
+            }
+        }
+        float pw[NTB][2][NB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const bool tok = 16 * tb + n < nv;
+            const uint8_t* vt = vbuf + (16 * tb + n) * VB;
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                // rows past the sequence end hold whatever the cache held: their
+                // weight must be an exact 0, not 0 * (a stale norm that may be NaN)
+                const float nvn = tok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(vt + 68 * blk)) : 0.0f;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(tv[tb][e] - m_run[e]);  // 0 for invalid tokens and rows
+                    if (blk == 0) l_run[e] += p;
+                    pw[tb][e][blk] = p * nvn;
+                }
+            }
+        }
+        if (live) {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk) {
+                        const float wt = pw[tb][e][blk];
+                        const uint32_t bits = __float_as_uint(wt);
+                        const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
+                        uint32_t* dst = wa + ((blk * NTB + tb) * ROWS + 4 * g + 2 * e) * 16 + n;
+                        dst[0] = dup_hi16(bits);                 // row (h, hi)
+                        dst[16] = dup_hi16(__float_as_uint(lo));  // row (h, lo)
+                    }
+        }
+        lds_order();
+
+        // ---- values: column n = code word n (coordinates 8n..8n+7 of a block),
+        // k-group g = tokens 16 tb + 4g + u, one accumulator per nibble position
+        // cb.  Step S = (tb, blk, half) covers nibbles 4 half..+3 of the four
+        // tokens' words; the lookups of step S+1 precede the products of step S.
+        {
+            uint32_t vw[NTB][NB][4];
+            u32x4 av[NTB][NB];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) {
+                    av[tb][blk] = *reinterpret_cast<const u32x4*>(wa_rd + (blk * NTB + tb) * wa_step);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        vw[tb][blk][u] = *reinterpret_cast<const uint32_t*>(vbuf + (16 * tb + 4 * g + u) * VB + 68 * blk + 4 + 4 * n);
+                }
+            // job J = (tb, blk, cb): nibble cb of the four tokens' words, four
+            // lookups, kLookahead jobs ahead of the products
+            constexpr int NJ = NTB * NB * 8, R = kLookahead + 1;
+            uint32_t ring[R][4];
+            static_for<NJ + kLookahead>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int TB = J / (8 * NB), BLK = (J / 8) % NB, CB = J % 8;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t x = vw[TB][BLK][u];
+                        ring[J % R][u] = (CB & 1) ? *reinterpret_cast<const uint32_t*>(vhi + nibble_offset<CB / 2>(x >> 1))
+                                                  : *reinterpret_cast<const uint32_t*>(vlo + nibble_offset<CB / 2>(x << 2));
+                    }
+                }
+                if constexpr (J >= kLookahead) {
+                    constexpr int M = J - kLookahead, TB = M / (8 * NB), BLK = (M / 8) % NB, CB = M % 8;
+                    acc[BLK][CB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, av[TB][BLK]),
+                        __builtin_bit_cast(bf16x8, u32x4{ring[M % R][0], ring[M % R][1], ring[M % R][2], ring[M % R][3]}),
+                        acc[BLK][CB], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
+            });
+        }
+        lds_order();
+        if (has_next) tile_to_lds<C::BYTES>(vstream + static_cast<size_t>(t0 + kSplitQuantum) * VB, vbuf, lane);
     }
+    wait_vmcnt<0>();
 
     // ---- merge the wavefronts of the workgroup and write the split record
 #pragma unroll
-    for (int g = 0; g < G; ++g) l_run[g] = wave_sum(l_run[g]);
+    for (int e = 0; e < 2; ++e) l_run[e] = row16_sum(l_run[e]);
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&sm.ktile[0][0]);
-    static_assert(sizeof(sm.ktile) + sizeof(sm.vtile) >= sizeof(float) * kWaves * G * (2 + D), "merge buffer");
+    float* red = reinterpret_cast<float*>(&sm.kbuf[0][0]);
+    static_assert(sizeof(sm.kbuf) + sizeof(sm.vbuf) >= sizeof(float) * kWaves * G * (2 + D), "merge buffer");
 #pragma unroll
-    for (int gr = 0; gr < NGRP; ++gr)
+    for (int e = 0; e < 2; ++e) {
+        const int hh = 2 * g + e;
+        if (hh < G) {
+            float* r = red + (w * G + hh) * (2 + D);
+            if (n == 0) { r[0] = m_run[e]; r[1] = l_run[e]; }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int g = 4 * gr + i;
-            float* r = red + (w * G + g) * (2 + D);
-            if (lane == 0) { r[0] = m_run[g]; r[1] = l_run[g]; }
+            for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-            for (int k = 0; k < DPL; ++k) r[2 + lane * DPL + k] = accv[gr][k][i];
+                for (int cb = 0; cb < 8; ++cb) r[2 + 128 * blk + 8 * n + cb] = acc[blk][cb][2 * e] + acc[blk][cb][2 * e + 1];
         }
+    }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
-        const int g = idx / D, j = idx % D;
+        const int gg = idx / D, j = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * G + g) * (2 + D)]);
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * G + gg) * (2 + D)]);
         float L = 0.0f, A = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) {
-            const float* r = red + (ww * G + g) * (2 + D);
+            const float* r = red + (ww * G + gg) * (2 + D);
             const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
             L = fmaf(r[1], f, L);
             A = fmaf(r[2 + j], f, A);
         }
-        const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
+        const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
         a.acc[rec * D + j] = A;
         if (j == 0) a.ml[rec] = make_float2(M, L);
     }
@@ -758,11 +967,11 @@ int launch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& c
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
-template <int D, int NGRP>
-int launch_partial_mfma(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+template <int D, int G>
+int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                         hipStream_t st) {
     dim3 grid(a.splits, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_mfma_kernel<D, NGRP>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
                        to_dev(cbv));
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -771,8 +980,8 @@ template <int KF, int VF, int D>
 int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                    hipStream_t st) {
     if constexpr (KF == TQ_FMT_PQ4 && VF == TQ_FMT_PQ4) {
-        if (G == 4) return launch_partial_mfma<D, 1>(a, L, cbk, cbv, st);
-        if (G == 8) return launch_partial_mfma<D, 2>(a, L, cbk, cbv, st);
+        if (G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);
+        if (G == 8) return launch_partial_bf16<D, 8>(a, L, cbk, cbv, st);
     }
     switch (G) {
         case 1: return launch_partial<KF, VF, D, 1>(a, L, cbk, cbv, st);
