@@ -249,7 +249,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16x2",
         "data": "synthetic",
         "config": {
             "workload": "c4: batch 8, 32 query / 8 KV heads, d 128, context 65536 (65535 prefilled + 1 appended "
@@ -264,7 +264,7 @@ def main():
                               "decode_combine": combine_ms},
         "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "decode_partial_kernel<PQ4,PQ4,128,4>",
+            "kernel": "decode_partial_bf16_kernel<128, 4>",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
