@@ -426,30 +426,6 @@ __device__ __forceinline__ void decode_half(uint32_t xl, uint32_t xh, const char
     c[3] = *reinterpret_cast<const uint32_t*>(hi + nibble_offset<2 * H + 1>(xh));
 }
 
-// HBM -> LDS copy of one tile with global_load_lds_dwordx4: copy m moves
-// bytes [1024 m, 1024 m + 1024) and lands lane l's 16 bytes at dst + 1024 m
-// + 16 l.  The copies count in vmcnt until their data is in LDS.
-template <int BYTES>
-__device__ __forceinline__ void tile_to_lds(const uint8_t* src, uint8_t* dst, int lane) {
-    constexpr int N = (BYTES + 1023) / 1024, TAIL = (BYTES - 1024 * (N - 1)) / 16;
-    static_for<N>([&](auto mc) {
-        constexpr int m = decltype(mc)::value;
-        if (m < N - 1 || TAIL == 64 || lane < TAIL)
-            __builtin_amdgcn_global_load_lds(src + 1024 * m + 16 * lane,
-                                             reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                                 reinterpret_cast<uintptr_t>(dst + 1024 * m)),
-                                             16, 0, 0);
-    });
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Program-order point between phases that touch the same LDS bytes through
 // differently typed accesses (no instruction is emitted).
 __device__ __forceinline__ void lds_order() {
@@ -498,26 +474,71 @@ __device__ __forceinline__ float row16_max(float x) {
     return x;
 }
 
-template <int D, int G>
+template <int D, int G, int TT>
 struct Bf16Cfg {
     static constexpr int VB = 68 * (D / 128);     // bytes per token and tensor
     static constexpr int NB = D / 128;            // 68-byte blocks per vector
-    static constexpr int BYTES = kTile * VB;      // one tensor's tile, a multiple of 16
-    static constexpr int NDMA = (BYTES + 1023) / 1024;
-    static constexpr int NTB = kTile / 16;        // 16-token blocks per tile
+    static constexpr int NTB = TT / 16;           // 16-token blocks per tile
     static constexpr int ROWS = 2 * G;            // MFMA rows in use: (head, hi/lo)
     static constexpr int WA = NB * NTB * ROWS * 16 + (ROWS < 16 ? 16 : 0);  // weight words per wavefront (+ zero row)
 };
 
-template <int D, int G>
+template <int D, int G, int TT>
 struct SmemBf16 {
-    using C = Bf16Cfg<D, G>;
+    using C = Bf16Cfg<D, G, TT>;
     uint32_t klo[32], khi[32], vlo[32], vhi[32];  // centroid pairs: lo[k] = P[k & 15], hi[k] = P[k >> 1]
-    alignas(16) uint8_t kbuf[kWaves][C::BYTES];
-    alignas(16) uint8_t vbuf[kWaves][C::BYTES];
-    alignas(16) uint32_t wa[kWaves][C::WA];       // value-product A operand [blk][tb][row][token] (+ zero row)
-    alignas(16) u32x4 qa[8 * C::NB][64];          // score A operand per chunk and lane (shared by the wavefronts)
+    union {
+        struct {
+            alignas(16) uint32_t wa[kWaves][C::WA];  // value-product A operand [blk][tb][row][token] (+ zero row)
+            alignas(16) u32x4 qa[8 * C::NB][64];     // score A operand per chunk and lane (shared by the wavefronts)
+        } op;
+        float red[kWaves * G * (2 + D)];            // per-wavefront (m, l, acc) records after the tile loop
+    } u;
 };
+
+typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(4)));  // 16 bytes at a 4-byte boundary
+
+// Key bytes of one tile as the score products consume them: lane (n, g)
+// holds, for token 16 tb + n, the fp16 block norm and code words 4g..4g+3
+// (coordinates 32g..32g+31) of every 68-byte block.
+template <int NTB, int NB>
+struct KeyTile {
+    u32x4u w[NTB][NB];
+    uint16_t norm[NTB][NB];
+};
+// Value bytes of one tile: lane (n, g) holds code word n of tokens
+// 16 tb + 4g + u (u = 0..3) and the fp16 norm of token 16 tb + n.
+template <int NTB, int NB>
+struct ValueTile {
+    uint32_t w[NTB][NB][4];
+    uint16_t norm[NTB][NB];
+};
+
+template <int VB, int NTB, int NB>
+__device__ __forceinline__ void load_keys(KeyTile<NTB, NB>& k, const uint8_t* stream, int t0, int n, int g) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        const uint8_t* row = stream + static_cast<size_t>(t0 + 16 * tb + n) * VB;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            k.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(row + 68 * blk);
+            k.w[tb][blk] = *reinterpret_cast<const u32x4u*>(row + 68 * blk + 4 + 16 * g);
+        }
+    }
+}
+template <int VB, int NTB, int NB>
+__device__ __forceinline__ void load_values(ValueTile<NTB, NB>& v, const uint8_t* stream, int t0, int n, int g) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            v.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(stream + static_cast<size_t>(t0 + 16 * tb + n) * VB + 68 * blk);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                v.w[tb][blk][u] = *reinterpret_cast<const uint32_t*>(
+                    stream + static_cast<size_t>(t0 + 16 * tb + 4 * g + u) * VB + 68 * blk + 4 + 4 * n);
+        }
+}
 
 // ---------------------------------------------------------------------------
 // PQ4 keys and values, G = 4 or 8 query heads per KV head, on the bf16 matrix
@@ -532,18 +553,19 @@ struct SmemBf16 {
 //   values  D[(h,r)][n] += sum_{t,s} w_r[h][t] * c_s[vcode_t,8n+cb]
 //           with columns the 16 code words n of a 128-coordinate block, one
 //           accumulator per nibble position cb, k = (token, s).
-// Centroid pairs come from 32-entry LDS tables (lookup = one SDWA mask and
-// one ds_read_b32); the query pairs sit in registers for the whole split; the
-// softmax writes the weight pairs to LDS in the A-operand layout.  Tiles move
-// HBM -> LDS with direct-to-LDS loads, double buffered by tensor: the next
-// keys are requested once the scores are done with the current ones, the
-// next values after the value products.
-template <int D, int G>
-__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_partial_bf16_kernel(DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
+// Each lane loads exactly the code words it decodes straight from HBM into
+// registers (coalesced 16-byte and 4-byte loads); the next tile's keys are
+// requested as soon as the scores have consumed the current ones, the next
+// values after the value products.  Centroid pairs come from 32-entry LDS
+// tables (lookup = one SDWA mask and one ds_read_b32), the query pairs from
+// LDS (written once per split), and the softmax writes the weight pairs to
+// LDS in the A-operand layout of the value products.
+template <int D, int G, int TT>
+__global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D == 128 ? 4 : 2, D == 128 ? 4 : 2))) void decode_partial_bf16_kernel(DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
     static_assert(G == 4 || G == 8, "two heads per 16-lane row group");
-    using C = Bf16Cfg<D, G>;
-    using SM = SmemBf16<D, G>;
-    constexpr int VB = C::VB, NB = C::NB, NTB = C::NTB, ROWS = C::ROWS, NDMA = C::NDMA;
+    using C = Bf16Cfg<D, G, TT>;
+    using SM = SmemBf16<D, G, TT>;
+    constexpr int VB = C::VB, NB = C::NB, NTB = C::NTB, ROWS = C::ROWS;
     __shared__ __align__(16) SM sm;
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -568,15 +590,16 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
     const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
     const uint8_t* kstream = a.k_cache + stream_row * VB;
     const uint8_t* vstream = a.v_cache + stream_row * VB;
-    uint8_t* kbuf = sm.kbuf[w];
-    uint8_t* vbuf = sm.vbuf[w];
-    uint32_t* wa = sm.wa[w];
+    uint32_t* wa = sm.u.op.wa[w];
 
-    // first tile of this wavefront in flight before anything else
-    int t0 = start + w * kTile;
+    // the first tile of this wavefront in flight before anything else (tiles
+    // lie inside the cache: t0 + TT <= capacity because TT divides 64)
+    int t0 = start + w * TT;
+    KeyTile<NTB, NB> kt;
+    ValueTile<NTB, NB> vt;
     if (t0 < end) {
-        tile_to_lds<C::BYTES>(kstream + static_cast<size_t>(t0) * VB, kbuf, lane);
-        tile_to_lds<C::BYTES>(vstream + static_cast<size_t>(t0) * VB, vbuf, lane);
+        load_keys<VB>(kt, kstream, t0, n, g);
+        load_values<VB>(vt, vstream, t0, n, g);
     }
 
     if (tid < 32) {
@@ -604,7 +627,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
                 const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
                 v[u] = n < ROWS ? (half | (half << 16)) : 0u;
             }
-            sm.qa[c][lane] = v;
+            sm.u.op.qa[c][lane] = v;
         }
     }
     __syncthreads();
@@ -629,64 +652,54 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
     // value-product A operand of this lane: row n (zero row when n >= ROWS), tokens 4g..4g+3
     const uint32_t* wa_rd = n < ROWS ? wa + n * 16 + 4 * g : wa + C::WA - 16 + 4 * g;
     const int wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
+    constexpr int kStep = kWaves * TT;
 
-    for (; t0 < end; t0 += kSplitQuantum) {
-        const int nv = min(kTile, end - t0);
-        const bool has_next = t0 + kSplitQuantum < end;
-        wait_vmcnt<NDMA>();  // this tile's keys (its values may still be in flight)
+    for (; t0 < end; t0 += kStep) {
+        const int nv = min(TT, end - t0);
+        // the last tile reloads itself instead of reading past the split
+        const int t_next = t0 + kStep < end ? t0 + kStep : t0;
 
         // ---- scores: column n = token 16 tb + n, k-group g = 32 coordinates per
-        // block.  Step S = (blk, c) multiplies chunk c of block blk (nibbles
-        // 4(c&1)..+3 of key word c/2) for the four token blocks; the lookups of
-        // step S+1 are issued before the products of step S.
-        uint32_t kw[NTB][NB][4];
-        float nk[NTB][NB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const uint8_t* kt = kbuf + (16 * tb + n) * VB;
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk) {
-                nk[tb][blk] = half_bits_to_float(*reinterpret_cast<const uint16_t*>(kt + 68 * blk));
-                const uint32_t* src = reinterpret_cast<const uint32_t*>(kt + 68 * blk + 4 + 16 * g);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) kw[tb][blk][d] = src[d];
-            }
-        }
+        // block.  Job J = S * NTB + tb multiplies chunk S (nibbles 4(S&1)..+3 of
+        // key word (S%8)/2 of block S/8) for token block tb; the lookups run
+        // kLookahead jobs ahead of the products, which keeps the LDS results in
+        // flight within lgkmcnt's range of 15.
         f32x4 dsc[NTB][NB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) dsc[tb][blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float nk[NTB][NB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) nk[tb][blk] = half_bits_to_float(kt.norm[tb][blk]);
         {
-            // job J = S * NTB + tb: chunk S of token block tb, four lookups;
-            // the lookups run kLookahead jobs ahead of the products, which
-            // keeps the LDS results in flight within lgkmcnt's range of 15.
-            constexpr int NS = NB * 8, NJ = NS * NTB, R = kLookahead + 1;
+            // QB query chunks in flight: chunk S is loaded at job S*NTB and last
+            // read by the product of job S*NTB + NTB-1, kLookahead jobs later
+            constexpr int NS = NB * 8, NJ = NS * NTB, R = kLookahead + 1, QB = 1 + (kLookahead + NTB - 1) / NTB;
             uint32_t ring[R][4];
-            u32x4 qk[2];
+            u32x4 qk[QB];
             static_for<NJ + kLookahead>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 if constexpr (J < NJ) {
                     constexpr int S = J / NTB, TB = J % NTB, BLK = S / 8, CC = S % 8;
-                    if constexpr (TB == 0) qk[S & 1] = sm.qa[S][lane];
-                    const uint32_t x = kw[TB][BLK][CC >> 1];
+                    if constexpr (TB == 0) qk[S % QB] = sm.u.op.qa[S][lane];
+                    const uint32_t x = kt.w[TB][BLK][CC >> 1];
                     decode_half<CC & 1>(x << 2, x >> 1, klo, khi, ring[J % R]);
                 }
                 if constexpr (J >= kLookahead) {
                     constexpr int M = J - kLookahead, S = M / NTB, TB = M % NTB, BLK = S / 8;
                     dsc[TB][BLK] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, qk[S & 1]),
+                        __builtin_bit_cast(bf16x8, qk[S % QB]),
                         __builtin_bit_cast(bf16x8, u32x4{ring[M % R][0], ring[M % R][1], ring[M % R][2], ring[M % R][3]}),
                         dsc[TB][BLK], 0, 0, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
             });
         }
-        lds_order();
-        // every key byte of this tile has been read: the next tile's keys may land
-        if (has_next) tile_to_lds<C::BYTES>(kstream + static_cast<size_t>(t0 + kSplitQuantum) * VB, kbuf, lane);
-
-        if (has_next) wait_vmcnt<NDMA>(); else wait_vmcnt<0>();  // this tile's values
+        // the keys of this tile are consumed: request the next tile's
+        load_keys<VB>(kt, kstream, t_next, n, g);
 
         // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
         // (G is even, so both heads of a lane exist exactly when 2g < G)
@@ -734,12 +747,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             const bool tok = 16 * tb + n < nv;
-            const uint8_t* vt = vbuf + (16 * tb + n) * VB;
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) {
                 // rows past the sequence end hold whatever the cache held: their
                 // weight must be an exact 0, not 0 * (a stale norm that may be NaN)
-                const float nvn = tok ? half_bits_to_float(*reinterpret_cast<const uint16_t*>(vt + 68 * blk)) : 0.0f;
+                const float nvn = tok ? half_bits_to_float(vt.norm[tb][blk]) : 0.0f;
 #pragma unroll
                 for (int e = 0; e < 2; ++e) {
                     const float p = __builtin_amdgcn_exp2f(tv[tb][e] - m_run[e]);  // 0 for invalid tokens and rows
@@ -767,22 +779,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
 
         // ---- values: column n = code word n (coordinates 8n..8n+7 of a block),
         // k-group g = tokens 16 tb + 4g + u, one accumulator per nibble position
-        // cb.  Step S = (tb, blk, half) covers nibbles 4 half..+3 of the four
-        // tokens' words; the lookups of step S+1 precede the products of step S.
+        // cb.  Job J = (tb, blk, cb): nibble cb of the four tokens' words, four
+        // lookups, kLookahead jobs ahead of the products.
         {
-            uint32_t vw[NTB][NB][4];
             u32x4 av[NTB][NB];
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-                for (int blk = 0; blk < NB; ++blk) {
+                for (int blk = 0; blk < NB; ++blk)
                     av[tb][blk] = *reinterpret_cast<const u32x4*>(wa_rd + (blk * NTB + tb) * wa_step);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        vw[tb][blk][u] = *reinterpret_cast<const uint32_t*>(vbuf + (16 * tb + 4 * g + u) * VB + 68 * blk + 4 + 4 * n);
-                }
-            // job J = (tb, blk, cb): nibble cb of the four tokens' words, four
-            // lookups, kLookahead jobs ahead of the products
             constexpr int NJ = NTB * NB * 8, R = kLookahead + 1;
             uint32_t ring[R][4];
             static_for<NJ + kLookahead>([&](auto jc) {
@@ -791,7 +796,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
                     constexpr int TB = J / (8 * NB), BLK = (J / 8) % NB, CB = J % 8;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const uint32_t x = vw[TB][BLK][u];
+                        const uint32_t x = vt.w[TB][BLK][u];
                         ring[J % R][u] = (CB & 1) ? *reinterpret_cast<const uint32_t*>(vhi + nibble_offset<CB / 2>(x >> 1))
                                                   : *reinterpret_cast<const uint32_t*>(vlo + nibble_offset<CB / 2>(x << 2));
                     }
@@ -807,16 +812,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(3, 
             });
         }
         lds_order();
-        if (has_next) tile_to_lds<C::BYTES>(vstream + static_cast<size_t>(t0 + kSplitQuantum) * VB, vbuf, lane);
+        // the values of this tile are consumed: request the next tile's
+        load_values<VB>(vt, vstream, t_next, n, g);
     }
-    wait_vmcnt<0>();
 
     // ---- merge the wavefronts of the workgroup and write the split record
 #pragma unroll
     for (int e = 0; e < 2; ++e) l_run[e] = row16_sum(l_run[e]);
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&sm.kbuf[0][0]);
-    static_assert(sizeof(sm.kbuf) + sizeof(sm.vbuf) >= sizeof(float) * kWaves * G * (2 + D), "merge buffer");
+    float* red = sm.u.red;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int hh = 2 * g + e;
@@ -967,11 +971,14 @@ int launch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& c
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+// tokens per wavefront tile of the bf16 decode kernel (16 or a multiple of 16 dividing 64)
+constexpr int kBf16Tile = 32;
+
 template <int D, int G>
 int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                         hipStream_t st) {
     dim3 grid(a.splits, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
+    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, kBf16Tile>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
                        to_dev(cbv));
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
