@@ -514,29 +514,37 @@ struct ValueTile {
     uint16_t norm[NTB][NB];
 };
 
-template <int VB, int NTB, int NB>
-__device__ __forceinline__ void load_keys(KeyTile<NTB, NB>& k, const uint8_t* stream, int t0, int n, int g) {
-#pragma unroll
-    for (int tb = 0; tb < NTB; ++tb) {
-        const uint8_t* row = stream + static_cast<size_t>(t0 + 16 * tb + n) * VB;
-#pragma unroll
-        for (int blk = 0; blk < NB; ++blk) {
-            k.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(row + 68 * blk);
-            k.w[tb][blk] = *reinterpret_cast<const u32x4u*>(row + 68 * blk + 4 + 16 * g);
-        }
-    }
+// Raw buffer view of one cache stream: loads take a per-lane byte offset
+// fixed for the whole split plus a wave-uniform tile offset in an SGPR, so
+// a tile's loads cost no address arithmetic; reads past the stream return 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             0x00020000);
 }
+
 template <int VB, int NTB, int NB>
-__device__ __forceinline__ void load_values(ValueTile<NTB, NB>& v, const uint8_t* stream, int t0, int n, int g) {
+__device__ __forceinline__ void load_keys(KeyTile<NTB, NB>& k, __amdgpu_buffer_rsrc_t r, int norm_off, int word_off,
+                                          int tile_off) {
 #pragma unroll
     for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-            v.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(stream + static_cast<size_t>(t0 + 16 * tb + n) * VB + 68 * blk);
+            const int o = (16 * tb) * VB + 68 * blk;
+            k.norm[tb][blk] = __builtin_amdgcn_raw_buffer_load_b16(r, norm_off + o, tile_off, 0);
+            k.w[tb][blk] = __builtin_bit_cast(u32x4u, __builtin_amdgcn_raw_buffer_load_b128(r, word_off + o, tile_off, 0));
+        }
+}
+template <int VB, int NTB, int NB>
+__device__ __forceinline__ void load_values(ValueTile<NTB, NB>& v, __amdgpu_buffer_rsrc_t r, int norm_off, int word_off,
+                                            int tile_off) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk) {
+            v.norm[tb][blk] = __builtin_amdgcn_raw_buffer_load_b16(r, norm_off + (16 * tb) * VB + 68 * blk, tile_off, 0);
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                v.w[tb][blk][u] = *reinterpret_cast<const uint32_t*>(
-                    stream + static_cast<size_t>(t0 + 16 * tb + 4 * g + u) * VB + 68 * blk + 4 + 4 * n);
+                v.w[tb][blk][u] = __builtin_amdgcn_raw_buffer_load_b32(r, word_off + (16 * tb + u) * VB + 68 * blk, tile_off, 0);
         }
 }
 
@@ -588,18 +596,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     }
 
     const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
-    const uint8_t* kstream = a.k_cache + stream_row * VB;
-    const uint8_t* vstream = a.v_cache + stream_row * VB;
+    const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
+    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
+    const int k_norm = n * VB;                   // key norm of token n
+    const int k_word = n * VB + 4 + 16 * g;      // key words 4g..4g+3 of token n
+    const int v_norm = n * VB;                   // value norm of token n
+    const int v_word = 4 * g * VB + 4 + 4 * n;   // value word n of token 4g
     uint32_t* wa = sm.u.op.wa[w];
 
     // the first tile of this wavefront in flight before anything else (tiles
     // lie inside the cache: t0 + TT <= capacity because TT divides 64)
-    int t0 = start + w * TT;
+    int t0 = __builtin_amdgcn_readfirstlane(start + w * TT);
     KeyTile<NTB, NB> kt;
     ValueTile<NTB, NB> vt;
     if (t0 < end) {
-        load_keys<VB>(kt, kstream, t0, n, g);
-        load_values<VB>(vt, vstream, t0, n, g);
+        load_keys<VB>(kt, krs, k_norm, k_word, t0 * VB);
+        load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
     }
 
     if (tid < 32) {
@@ -613,12 +626,12 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     // query A operand: row m = n = (head m/2, r = m&1), k-group g holds
     // coordinates 128 blk + 32 g + 4 cc + u (u = 0..3) of chunk c = 8 blk + cc,
     // each as the bf16 half r of q * log2(e)/sqrt(d), duplicated for s = hi/lo.
-    if (w == 0) {
+    {
         const float qscale = kLog2e / sqrtf(static_cast<float>(D));
         const int hm = n >> 1, r = n & 1;
         const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + (hm < G ? hm : 0)) * D;
 #pragma unroll
-        for (int c = 0; c < NB * 8; ++c) {
+        for (int c = w; c < NB * 8; c += kWaves) {  // chunks split over the wavefronts
             u32x4 v;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -699,7 +712,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             });
         }
         // the keys of this tile are consumed: request the next tile's
-        load_keys<VB>(kt, kstream, t_next, n, g);
+        load_keys<VB>(kt, krs, k_norm, k_word, t_next * VB);
 
         // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
         // (G is even, so both heads of a lane exist exactly when 2g < G)
@@ -813,7 +826,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
         }
         lds_order();
         // the values of this tile are consumed: request the next tile's
-        load_values<VB>(vt, vstream, t_next, n, g);
+        load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
     }
 
     // ---- merge the wavefronts of the workgroup and write the split record
@@ -947,7 +960,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
 int auto_split_tokens(const tq_layout* L) {
     const long streams = static_cast<long>(L->batch) * L->n_kv_heads;
     const long max_splits = (L->capacity + kSplitQuantum - 1) / kSplitQuantum;
-    long want = (4096 + streams - 1) / streams;  // aim at >= 4096 workgroups
+    long want = (2048 + streams - 1) / streams;  // aim at >= 2048 workgroups (two rounds of four per CU)
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
     long len = (L->capacity + want - 1) / want;
@@ -987,8 +1000,10 @@ template <int KF, int VF, int D>
 int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                    hipStream_t st) {
     if constexpr (KF == TQ_FMT_PQ4 && VF == TQ_FMT_PQ4) {
-        if (G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);
-        if (G == 8) return launch_partial_bf16<D, 8>(a, L, cbk, cbv, st);
+        // the matrix-core kernel addresses a stream through a 32-bit buffer range
+        const bool fits = static_cast<size_t>(L->capacity) * vbytes<TQ_FMT_PQ4, D>() <= 0x7FFFFFFFu;
+        if (fits && G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);
+        if (fits && G == 8) return launch_partial_bf16<D, 8>(a, L, cbk, cbv, st);
     }
     switch (G) {
         case 1: return launch_partial<KF, VF, D, 1>(a, L, cbk, cbv, st);
