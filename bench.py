@@ -12,7 +12,9 @@ resident in HBM when timing starts.
 
 One step = append (K and V) + query rotation + decode partial + combine.
 Two cache copies (1.14 GB together) alternate between steps so that the
-256 MB Infinity Cache cannot hold the bytes a step reads.
+256 MB Infinity Cache cannot hold the bytes a step reads.  The default 200
+warm-up steps (about 35 ms of decode) let the GPU clock settle before the
+200 timed steps; a 10-step warm-up measures the kernel about 10% slower.
 
 Output: one JSON line.  ``value`` is compressed-KV tokens attended per second
 (batch * context / step time).  ``roofline`` reports the dominant kernel,
@@ -125,8 +127,8 @@ def cpu_baseline(w, target_seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--copies", type=int, default=2, help="cache copies rotated between steps")
