@@ -24,6 +24,13 @@ REDUCED = {
     "c5": synth.scaled(synth.C5, batch=2, n_q_heads=16, n_kv_heads=2, context=700, capacity=704),
     "pq3k_pq4v": synth.scaled(synth.C2, v_format=synth.PQ4, v_bits=4, batch=1, n_q_heads=4, n_kv_heads=1,
                               context=500, capacity=512),
+    # PQ4 with K and V on different centroid tables (the matrix-core kernel
+    # that reads two tables) and PQ4 with eight query heads per KV head
+    "c4_lloyd_v": synth.scaled(synth.C4, v_kind=synth.LLOYD_MAX, batch=2, n_q_heads=8, n_kv_heads=2, context=1111,
+                               capacity=1152),
+    "c4_g8": synth.scaled(synth.C4, batch=2, n_q_heads=16, n_kv_heads=2, context=1234, capacity=1280),
+    "c4_g8_lloyd_v": synth.scaled(synth.C4, v_kind=synth.LLOYD_MAX, batch=1, n_q_heads=16, n_kv_heads=2,
+                                  context=900, capacity=960),
 }
 
 
