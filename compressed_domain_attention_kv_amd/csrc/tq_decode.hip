@@ -577,7 +577,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     __shared__ __align__(16) SM sm;
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
     const int n = lane & 15, g = lane >> 4;  // MFMA column / row (A side) and k-group
     const int hq0 = h * G;
     int N = a.seq_lens[b];
@@ -607,7 +608,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 
     // the first tile of this wavefront in flight before anything else (tiles
     // lie inside the cache: t0 + TT <= capacity because TT divides 64)
-    int t0 = __builtin_amdgcn_readfirstlane(start + w * TT);
+    int t0 = start + w * TT;
     KeyTile<NTB, NB> kt;
     ValueTile<NTB, NB> vt;
     if (t0 < end) {
@@ -937,7 +938,8 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     __shared__ __align__(16) SM sm;
 
     const int h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wi = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
     const int sg = wi / kWaves, w = wi % kWaves;     // split within the workgroup, wavefront within the split
     const int s = blockIdx.x * kPairSub + sg;         // this wavefront's split
     const int n = lane & 15, g = lane >> 4;
@@ -954,7 +956,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int k_norm = n * VB, k_word = n * VB + 4 + 16 * g, v_norm = n * VB, v_word = 4 * g * VB + 4 + 4 * n;
     uint32_t* wa = sm.wa[wi];
 
-    int t0 = __builtin_amdgcn_readfirstlane(start + w * TT);
+    int t0 = start + w * TT;
     KeyTile<NTB, 1> kt;
     ValueTile<NTB, 1> vt;
     if (t0 < end) {
