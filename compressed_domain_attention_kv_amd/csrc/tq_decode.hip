@@ -1126,6 +1126,9 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                     pb[tb][p2][1] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
                 }
             }
+            // the value words now live in pb and the norms were used by the
+            // softmax: the next tile's values are requested a whole tile ahead
+            load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
             constexpr int NJ = NTB * 8, R = kPairLookahead + 1;
             uint2 ring[R][2];
             static_for<NJ + kPairLookahead>([&](auto jc) {
@@ -1150,7 +1153,6 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             });
         }
         lds_order();
-        load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
     }
 
     // ---- merge the four wavefronts of each split and write its record
@@ -1168,6 +1170,340 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int cb8 = 0; cb8 < 8; ++cb8) r[2 + 8 * n + cb8] = acc[cb8][2 * e] + acc[cb8][2 * e + 1];
         }
+    }
+    __syncthreads();
+    if (s < a.splits) {
+        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+        for (int idx = tid % (kWaves * 64); idx < G * D; idx += kWaves * 64) {
+            const int gg = idx / D, j = idx % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[((sg * kWaves + ww) * G + gg) * (2 + D)]);
+            float L = 0.0f, A = 0.0f;
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const float* r = red + ((sg * kWaves + ww) * G + gg) * (2 + D);
+                const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+                L = fmaf(r[1], f, L);
+                A = fmaf(r[2 + j], f, A);
+            }
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            a.acc[rec * D + j] = A;
+            if (j == 0) a.ml[rec] = make_float2(M, L);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// PQ4 decode on the 2:4-sparse matrix cores (d = 128, G = 4 or 8, K and V
+// sharing one centroid table).  v_smfmac_f32_16x16x64_bf16 multiplies a
+// 16 x 64 A operand with at most two nonzeros in every aligned group of four
+// k (stored compressed, their positions in an index register) by a dense
+// 64 x 16 B operand, at the issue cost of a dense 16 x 16 x 32 product.
+//
+// Both contractions take that shape with rows (head h, half r of the hi/lo
+// split, coordinate parity p), 16 rows per four heads:
+//   * a lookup of code byte m in the byte-pair table yields the k-group
+//     (c_hi[2m], c_lo[2m], c_hi[2m+1], c_lo[2m+1]);
+//   * row (h, r, p) holds its operand at positions 2p and 2p+1 of every
+//     group, so it accumulates coordinate 2m + p with both centroid halves.
+// Scores: D[(h,r,p)][t] = sum_m q_r[h][2m+p] c[2m+p, t], 16 coordinate pairs
+// per product; head h's score is the sum of its four rows times the key norm.
+// Values: D[(h,r,p)][n] = sum_t w_r[h][t] c[2m+p, t], 16 tokens per product,
+// column n standing for coordinate pair m = 4n + Q of product Q.  After the
+// score products lane (n, g) holds head g's score of token n, and after the
+// value products head g's coordinates 8n + 2Q + p, so the online softmax and
+// its rescaling never leave the lane.
+//
+// Operand lane layouts of the instruction (checked on the hardware): A lane
+// (row i, group g) holds k = 16g .. 16g+15, value 2q+s being the s-th nonzero
+// of group q at the position in index bits 4q+2s .. 4q+2s+1; B lane
+// (column n, group g) holds k = 8g .. 8g+7 in elements 0..7 and
+// k = 32+8g .. 32+8g+7 in elements 8..15.  Dense k-group gd (four k) thus
+// sits in A lane group gd / 4 and in B lane group (gd & 7) / 2, element
+// quad (gd & 1) + 2 (gd / 8).
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+
+__host__ __device__ constexpr int sp_lane_group(int gd) { return (gd & 7) >> 1; }
+__host__ __device__ constexpr int sp_quad(int gd) { return (gd & 1) + 2 * (gd >> 3); }
+__host__ __device__ constexpr int sp_group(int gb, int e) { return 2 * gb + (e & 1) + 8 * (e >> 1); }
+
+// lookup jobs (four lookups each) in flight ahead of the product consuming the oldest
+constexpr int kSpLookahead = 1;
+
+template <int G>
+struct SpCfg {
+    static constexpr int D = 128, VB = 68, TT = 32, NTB = TT / 16;
+    static constexpr int RB = G / 4;                   // 16-row blocks of (head, r, p)
+    static constexpr int WA = NTB * G * 2 * 16;         // weight words per wavefront: [tb][head][r][k-group]
+    static constexpr int RED = kPairWaves * G * (2 + D);
+};
+
+template <int G>
+struct SmemSp {
+    using C = SpCfg<G>;
+    union {
+        struct {
+            uint2 table[256 * kPairCopies];          // entry (byte b, copy c) at b * 32 + c
+            alignas(16) u32x4 qa[C::RB][4][64];      // compressed score A operand per row block, product, lane
+        } op;
+        float red[C::RED];                           // per-wavefront (m, l, acc) after the tile loop
+    } u;
+    alignas(16) uint32_t wa[kPairWaves][C::WA];
+};
+
+template <int G>
+__global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_partial_sparse_kernel(
+    DecodeArgs a, DevCodebook cb) {
+    static_assert(G == 4 || G == 8, "four heads per 16-row block");
+    using C = SpCfg<G>;
+    constexpr int D = C::D, VB = C::VB, NTB = C::NTB, RB = C::RB, TT = C::TT;
+    __shared__ __align__(16) SmemSp<G> sm;
+
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
+    const int sg = wi / kWaves, w = wi % kWaves;     // split within the workgroup, wavefront within the split
+    const int s = blockIdx.x * kPairSub + sg;
+    const int n = lane & 15, g = lane >> 4;
+    const int hq0 = h * G;
+    int N = a.seq_lens[b];
+    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
+    const int start = s * a.split_len;
+    const int end = s < a.splits ? min(start + a.split_len, N) : start;  // no tokens past the last split
+
+    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
+    const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
+    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
+    const int k_norm = n * VB, k_word = n * VB + 4 + 16 * g, v_norm = n * VB, v_word = 4 * g * VB + 4 + 4 * n;
+    uint32_t* wa = sm.wa[wi];
+
+    int t0 = start + w * TT;
+    KeyTile<NTB, 1> kt;
+    ValueTile<NTB, 1> vt;
+    if (t0 < end) {
+        load_keys<VB>(kt, krs, k_norm, k_word, t0 * VB);
+        load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
+    }
+
+    // the pair table: thread t writes copies 8 (t >> 8) .. +7 of byte t & 255
+    {
+        const int byte = tid & 255;
+        const uint2 e = make_uint2(bf16_split(cb.centroids[byte & 15]), bf16_split(cb.centroids[byte >> 4]));
+#pragma unroll
+        for (int c = 0; c < kPairCopies / 4; ++c) sm.u.op.table[byte * kPairCopies + (tid >> 8) * (kPairCopies / 4) + c] = e;
+    }
+    // compressed score A operand: wavefront wi < 4 RB builds product I = wi % 4 of row block wi / 4;
+    // lane (row n, group g) holds, per group q, the pair (q_r, q_r) of coordinate 2m + p, where
+    // m is the code byte that B lane group sp_lane_group(4g + q) reads as element quad sp_quad(4g + q)
+    if (wi < 4 * RB) {
+        const int rb = wi / 4, I = wi % 4;
+        const int hh = 4 * rb + (n >> 2), r = (n >> 1) & 1, p = n & 1;
+        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + hh) * D;
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int gd = 4 * g + q;
+            const int m = 16 * sp_lane_group(gd) + 4 * I + sp_quad(gd);
+            const uint32_t pr = bf16_split(qg[2 * m + p] * qscale);
+            const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
+            v[q] = half | (half << 16);
+        }
+        sm.u.op.qa[rb][I][lane] = v;
+    }
+    __syncthreads();
+
+    // row parity p = n & 1: nonzeros at positions 2p, 2p+1 of every group of four
+    const int sp_idx = (n & 1) ? 0xEEEE : 0x4444;
+    u32x4 qreg[RB == 1 ? 4 : 1];
+    if constexpr (RB == 1) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) qreg[I] = sm.u.op.qa[0][I][lane];
+    }
+
+    float m_run[RB], l_run[RB];
+    f32x4 acc[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = -INFINITY;
+        l_run[rb] = 0.0f;
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q) acc[rb][Q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    const char* tab = reinterpret_cast<const char*>(sm.u.op.table);
+    uint32_t addr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) addr[i] = (lane & 31) * 8u;  // bits 8..15 take the code byte
+    // weights: token n is written to k-group sp_group(n / 4, n % 4) of [tb][head][r]; the value
+    // A operand of lane (row n, group g) is the four groups 4g .. 4g+3 of its (head, r)
+    const int w_slot = sp_group(n >> 2, n & 3);
+    const uint32_t* wa_rd = wa + ((n >> 2) * 2 + ((n >> 1) & 1)) * 16 + 4 * g;
+    constexpr int kStep = kWaves * TT;
+    constexpr int LA = kSpLookahead, R = LA + 1;
+
+    for (; t0 < end; t0 += kStep) {
+        const int nv = min(TT, end - t0);
+        const int t_next = t0 + kStep < end ? t0 + kStep : t0;
+
+        // ---- scores: job J = I * NTB + tb reads bytes 0..3 of key word I of block tb
+        f32x4 dsc[NTB][RB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) dsc[tb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float nk[NTB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) nk[tb] = half_bits_to_float(kt.norm[tb][0]);
+        {
+            constexpr int NJ = 4 * NTB;
+            u32x8 ring[R];
+            static_for<NJ + LA>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int I = J / NTB, TB = J % NTB;
+                    const uint32_t x = kt.w[TB][0][I];
+                    put_byte1<0>(addr[0], x);
+                    put_byte1<1>(addr[1], x);
+                    put_byte1<2>(addr[2], x);
+                    put_byte1<3>(addr[3], x);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(tab + addr[e]);
+                        ring[J % R][2 * e] = v.x;
+                        ring[J % R][2 * e + 1] = v.y;
+                    }
+                }
+                if constexpr (J >= LA) {
+                    constexpr int M = J - LA, I = M / NTB, TB = M % NTB;
+                    const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) {
+                        const u32x4 aop = RB == 1 ? qreg[RB == 1 ? I : 0] : sm.u.op.qa[rb][I][lane];
+                        dsc[TB][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, aop), bop,
+                                                                               dsc[TB][rb], sp_idx, 0, 0);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        load_keys<VB>(kt, krs, k_norm, k_word, t_next * VB);
+
+        // ---- online softmax: lane (n, g) owns head 4 rb + g, token 16 tb + n
+        float tv[NTB][RB];
+        float mx[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) mx[rb] = -INFINITY;
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const bool ok = 16 * tb + n < nv;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const f32x4 d4 = dsc[tb][rb];
+                const float sc = nk[tb] * ((d4[0] + d4[1]) + (d4[2] + d4[3]));
+                tv[tb][rb] = ok ? sc : -INFINITY;
+                mx[rb] = fmaxf(mx[rb], tv[tb][rb]);
+            }
+        }
+        if (a.scores) {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    if (tv[tb][rb] != -INFINITY)
+                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 4 * rb + g) * a.capacity + t0 + 16 * tb + n] =
+                            tv[tb][rb] * kLn2;
+        }
+        bool grow = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) grow = grow || mx[rb] > m_run[rb] + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float mn = fmaxf(m_run[rb], row16_max(mx[rb]));
+                const float alpha = mn == m_run[rb] ? 1.0f : __builtin_amdgcn_exp2f(m_run[rb] - mn);
+                l_run[rb] *= alpha;
+#pragma unroll
+                for (int Q = 0; Q < 4; ++Q) acc[rb][Q] *= alpha;
+                m_run[rb] = mn;
+            }
+        }
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            // rows past the sequence end hold whatever the cache held: weight exactly 0
+            const float nvn = 16 * tb + n < nv ? half_bits_to_float(vt.norm[tb][0]) : 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                const float p = __builtin_amdgcn_exp2f(tv[tb][rb] - m_run[rb]);
+                l_run[rb] += p;
+                const float wt = p * nvn;
+                const uint32_t bits = __float_as_uint(wt);
+                const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
+                uint32_t* dst = wa + (tb * G + 4 * rb + g) * 32 + w_slot;
+                dst[0] = dup_hi16(bits);
+                dst[16] = dup_hi16(__float_as_uint(lo));
+            }
+        }
+        lds_order();
+
+        // ---- values: job J = tb * 4 + Q reads byte Q of code word n of tokens 4g .. 4g+3
+        {
+            u32x4 av[NTB][RB];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    av[tb][rb] = *reinterpret_cast<const u32x4*>(wa_rd + (tb * G + 4 * rb) * 32);
+            constexpr int NJ = 4 * NTB;
+            u32x8 ring[R];
+            static_for<NJ + LA>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int TB = J / 4, Q = J % 4;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB][0][u]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(tab + addr[u]);
+                        ring[J % R][2 * u] = v.x;
+                        ring[J % R][2 * u + 1] = v.y;
+                    }
+                }
+                if constexpr (J >= LA) {
+                    constexpr int M = J - LA, TB = M / 4, Q = M % 4;
+                    const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        acc[rb][Q] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av[TB][rb]), bop,
+                                                                              acc[rb][Q], sp_idx, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        lds_order();
+        load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
+    }
+
+    // ---- merge the four wavefronts of each split and write its record
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) l_run[rb] = row16_sum(l_run[rb]);
+
+    __syncthreads();  // every lookup of the workgroup is done: the table area becomes the merge buffer
+    float* red = sm.u.red;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        float* r = red + (wi * G + 4 * rb + g) * (2 + D);
+        if (n == 0) {
+            r[0] = m_run[rb];
+            r[1] = l_run[rb];
+        }
+#pragma unroll
+        for (int Q = 0; Q < 4; ++Q)
+#pragma unroll
+            for (int p = 0; p < 2; ++p) r[2 + 8 * n + 2 * Q + p] = acc[rb][Q][p] + acc[rb][Q][2 + p];
     }
     __syncthreads();
     if (s < a.splits) {
@@ -1320,6 +1656,13 @@ int launch_partial_pair(const DecodeArgs& a, const tq_layout* L, const tq_codebo
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+template <int G>
+int launch_partial_sparse(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cb, hipStream_t st) {
+    dim3 grid((a.splits + kPairSub - 1) / kPairSub, L->n_kv_heads, L->batch);
+    hipLaunchKernelGGL((decode_partial_sparse_kernel<G>), grid, dim3(kPairWaves * 64), 0, st, a, to_dev(cb));
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 // K and V decode through one table only when their centroids are identical
 bool same_centroids(const tq_codebook& x, const tq_codebook& y) {
     if (x.n_levels != y.n_levels) return false;
@@ -1345,8 +1688,8 @@ int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_code
         const bool fits = static_cast<size_t>(L->capacity) * vbytes<TQ_FMT_PQ4, D>() <= 0x7FFFFFFFu;
         if constexpr (D == 128) {
             if (fits && same_centroids(cbk, cbv)) {
-                if (G == 4) return launch_partial_pair<4>(a, L, cbk, st);
-                if (G == 8) return launch_partial_pair<8>(a, L, cbk, st);
+                if (G == 4) return launch_partial_sparse<4>(a, L, cbk, st);
+                if (G == 8) return launch_partial_sparse<8>(a, L, cbk, st);
             }
         }
         if (fits && G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);
