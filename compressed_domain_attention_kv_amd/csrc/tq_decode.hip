@@ -1240,12 +1240,13 @@ struct SpCfg {
     static constexpr int RED = kPairWaves * G * (2 + D);
 };
 
-template <int G>
+template <int G, bool VTAB>
 struct SmemSp {
     using C = SpCfg<G>;
     union {
         struct {
             uint2 table[256 * kPairCopies];          // entry (byte b, copy c) at b * 32 + c
+            uint2 vtable[VTAB ? 256 * kPairCopies : 1];  // the values' own table when their centroids differ
             alignas(16) u32x4 qa[C::RB][4][64];      // compressed score A operand per row block, product, lane
         } op;
         float red[C::RED];                           // per-wavefront (m, l, acc) after the tile loop
@@ -1253,13 +1254,14 @@ struct SmemSp {
     alignas(16) uint32_t wa[kPairWaves][C::WA];
 };
 
-template <int G>
+template <int G, bool VTAB>
 __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_partial_sparse_kernel(
-    DecodeArgs a, DevCodebook cb) {
+    DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
     static_assert(G == 4 || G == 8, "four heads per 16-row block");
+    static_assert(!VTAB || G == 4, "two tables fit the LDS at G = 4 only");
     using C = SpCfg<G>;
     constexpr int D = C::D, VB = C::VB, NTB = C::NTB, RB = C::RB, TT = C::TT;
-    __shared__ __align__(16) SmemSp<G> sm;
+    __shared__ __align__(16) SmemSp<G, VTAB> sm;
 
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1288,12 +1290,18 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
     }
 
-    // the pair table: thread t writes copies 8 (t >> 8) .. +7 of byte t & 255
+    // the pair tables: thread t writes copies 8 (t >> 8) .. +7 of byte t & 255
     {
         const int byte = tid & 255;
-        const uint2 e = make_uint2(bf16_split(cb.centroids[byte & 15]), bf16_split(cb.centroids[byte >> 4]));
+        const uint2 e = make_uint2(bf16_split(cbk.centroids[byte & 15]), bf16_split(cbk.centroids[byte >> 4]));
 #pragma unroll
         for (int c = 0; c < kPairCopies / 4; ++c) sm.u.op.table[byte * kPairCopies + (tid >> 8) * (kPairCopies / 4) + c] = e;
+        if constexpr (VTAB) {
+            const uint2 ev = make_uint2(bf16_split(cbv.centroids[byte & 15]), bf16_split(cbv.centroids[byte >> 4]));
+#pragma unroll
+            for (int c = 0; c < kPairCopies / 4; ++c)
+                sm.u.op.vtable[byte * kPairCopies + (tid >> 8) * (kPairCopies / 4) + c] = ev;
+        }
     }
     // compressed score A operand: wavefront wi < 4 RB builds product I = wi % 4 of row block wi / 4;
     // lane (row n, group g) holds, per group q, the pair (q_r, q_r) of coordinate 2m + p, where
@@ -1335,6 +1343,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
 
     const char* tab = reinterpret_cast<const char*>(sm.u.op.table);
+    const char* vtab = VTAB ? reinterpret_cast<const char*>(sm.u.op.vtable) : tab;
     uint32_t addr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) addr[i] = (lane & 31) * 8u;  // bits 8..15 take the code byte
@@ -1467,7 +1476,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                     for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB][0][u]);
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(tab + addr[u]);
+                        const uint2 v = *reinterpret_cast<const uint2*>(vtab + addr[u]);
                         ring[J % R][2 * u] = v.x;
                         ring[J % R][2 * u + 1] = v.y;
                     }
@@ -1622,7 +1631,14 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
 int auto_split_tokens(const tq_layout* L) {
     const long streams = static_cast<long>(L->batch) * L->n_kv_heads;
     const long max_splits = (L->capacity + kSplitQuantum - 1) / kSplitQuantum;
-    long want = (2048 + streams - 1) / streams;  // aim at >= 2048 workgroups (two rounds of four per CU)
+    // PQ4 at d = 128 and G = 4 or 8 runs four splits per 16-wavefront workgroup, one workgroup
+    // per CU: about 1024 splits fill the chip in a single round.  The other kernels run one split
+    // per 4-wavefront workgroup and do best with two rounds of four workgroups per CU.
+    const int G = L->n_kv_heads > 0 ? L->n_q_heads / L->n_kv_heads : 0;
+    const bool sparse_path = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && L->head_dim == 128 &&
+                             (G == 4 || G == 8);
+    const long target = sparse_path ? 1024 : 2048;
+    long want = (target + streams - 1) / streams;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
     long len = (L->capacity + want - 1) / want;
@@ -1656,10 +1672,12 @@ int launch_partial_pair(const DecodeArgs& a, const tq_layout* L, const tq_codebo
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
-template <int G>
-int launch_partial_sparse(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cb, hipStream_t st) {
+template <int G, bool VTAB>
+int launch_partial_sparse(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+                          hipStream_t st) {
     dim3 grid((a.splits + kPairSub - 1) / kPairSub, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_sparse_kernel<G>), grid, dim3(kPairWaves * 64), 0, st, a, to_dev(cb));
+    hipLaunchKernelGGL((decode_partial_sparse_kernel<G, VTAB>), grid, dim3(kPairWaves * 64), 0, st, a, to_dev(cbk),
+                       to_dev(cbv));
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
@@ -1687,9 +1705,11 @@ int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_code
         // the matrix-core kernel addresses a stream through a 32-bit buffer range
         const bool fits = static_cast<size_t>(L->capacity) * vbytes<TQ_FMT_PQ4, D>() <= 0x7FFFFFFFu;
         if constexpr (D == 128) {
-            if (fits && same_centroids(cbk, cbv)) {
-                if (G == 4) return launch_partial_sparse<4>(a, L, cbk, st);
-                if (G == 8) return launch_partial_sparse<8>(a, L, cbk, st);
+            if (fits) {
+                const bool same = same_centroids(cbk, cbv);
+                if (G == 4) return same ? launch_partial_sparse<4, false>(a, L, cbk, cbv, st)
+                                        : launch_partial_sparse<4, true>(a, L, cbk, cbv, st);
+                if (G == 8 && same) return launch_partial_sparse<8, false>(a, L, cbk, cbv, st);
             }
         }
         if (fits && G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);

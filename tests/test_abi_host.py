@@ -94,7 +94,9 @@ def test_layout_validation_codes():
 def test_splits_and_workspace_arithmetic():
     L = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
     s = tq.decode_splits(L)
-    assert s >= 1 and 8 * 8 * s >= 2048
+    assert s >= 1 and 8 * 8 * s >= 1024  # PQ4, d 128, G 4: four splits per workgroup, one per CU
+    other = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ3, tq.FMT_PQ3)
+    assert 8 * 8 * tq.decode_splits(other) >= 2048  # one split per workgroup elsewhere
     assert tq.decode_workspace_bytes(L) == 8 * 32 * s * (8 + 4 * 128)
     assert tq.decode_splits(L, 1024) == 64
     assert tq.decode_splits(L, 1000) == 0  # not a multiple of 256

@@ -111,7 +111,7 @@ def _check_unsampled_bounds(st, w, out, vc, L, lens, probe):
 def test_c4_full_size_with_append():
     w = synth.C4
     st, L, out, kc, vc, lens = _run_full(w, sample=[(0, 0), (7, 5), (3, 2)], append_step=0)
-    assert tq.decode_splits(L) >= 32
+    assert tq.decode_splits(L) >= 16  # split-K: one single-round grid of 16 splits per stream
 
 
 def test_c2_full_size():
