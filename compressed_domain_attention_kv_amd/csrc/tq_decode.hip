@@ -868,45 +868,19 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 }
 
 // ---------------------------------------------------------------------------
-// Byte-pair variant of the PQ4 matrix-core decode (d = 128, G = 4 or 8, K and
-// V sharing one centroid table).  A lookup decodes a whole code byte: entry
-// b of a 256-entry table holds the bf16 (hi, lo) pairs of both nibbles,
-// (P[b & 15], P[b >> 4]), 8 bytes read by one ds_read_b64.  The table is
-// replicated 32 times so that lane l always reads copy l % 32, which sits in
-// its own pair of LDS banks: any byte values, no bank conflicts.  Addresses
-// are byte * 256 + 8 * (l % 32); one v_mov_b32_sdwa drops the code byte into
-// bits 8..15 of a register whose low byte holds the lane part.
-//   scores: the byte's two nibbles are coordinates 2q and 2q+1 of one key,
-//           adjacent k-pairs of the B operand;
-//   values: the byte is built from nibble cb of two tokens' words (one
-//           v_bfi per four bytes), so its entry is that coordinate for two
-//           adjacent tokens, again adjacent k-pairs of the B operand.
-// One workgroup of 16 wavefronts runs four consecutive splits of one KV
-// stream (four wavefronts per split) and shares the 64 KB table and the
-// query operand.
+// Byte-pair centroid table of the PQ4 sparse-matrix decode.  A lookup decodes
+// a whole code byte: entry b of a 256-entry table holds the bf16 (hi, lo)
+// pairs of both nibbles, (P[b & 15], P[b >> 4]), 8 bytes read by one
+// ds_read_b64.  The table is replicated 32 times so that lane l always reads
+// copy l % 32, which sits in its own pair of LDS banks: any byte values, no
+// bank conflicts.  Addresses are byte * 256 + 8 * (l % 32); one
+// v_mov_b32_sdwa drops the code byte into bits 8..15 of a register whose low
+// byte holds the lane part.  One workgroup of 16 wavefronts runs four
+// consecutive splits of one KV stream (four wavefronts per split) and shares
+// the table and the query operand.
 constexpr int kPairSub = 4;                    // splits per workgroup
 constexpr int kPairWaves = kPairSub * kWaves;  // wavefronts per workgroup
 constexpr int kPairCopies = 32;                // table copies, one per LDS bank pair
-
-template <int G>
-struct PairCfg {
-    static constexpr int D = 128, VB = 68, TT = 32, NTB = TT / 16, ROWS = 2 * G;
-    static constexpr int WA = NTB * ROWS * 16 + (ROWS < 16 ? 16 : 0);  // weight words per wavefront (+ zero row)
-    static constexpr int RED = kPairWaves * G * (2 + D);              // merge floats
-};
-
-template <int G>
-struct SmemPair {
-    using C = PairCfg<G>;
-    union {
-        struct {
-            uint2 table[256 * kPairCopies];  // entry (byte b, copy c) at b * 32 + c
-            alignas(16) u32x4 qa[8][64];     // score A operand per chunk and lane
-        } op;
-        float red[C::RED];                   // per-wavefront (m, l, acc) after the tile loop
-    } u;
-    alignas(16) uint32_t wa[kPairWaves][C::WA];
-};
 
 // Write byte Q of w into bits 8..15 of addr, keeping its other bits.
 #define TQ_PUT_BYTE1(Q)                                                                                   \
@@ -923,280 +897,10 @@ TQ_PUT_BYTE1(2)
 TQ_PUT_BYTE1(3)
 #undef TQ_PUT_BYTE1
 
-// MFMA jobs whose pair lookups run ahead of the product consuming the oldest
-// (two ds_read_b64 each) and the address registers cycling through them.
-constexpr int kPairLookahead = 2;
-constexpr int kPairAddr = 4;
-
-template <int G>
-__global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_partial_pair_kernel(
-    DecodeArgs a, DevCodebook cb) {
-    static_assert(G == 4 || G == 8, "two heads per 16-lane row group");
-    using C = PairCfg<G>;
-    using SM = SmemPair<G>;
-    constexpr int D = C::D, VB = C::VB, NTB = C::NTB, ROWS = C::ROWS, TT = C::TT;
-    __shared__ __align__(16) SM sm;
-
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wi = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
-    const int sg = wi / kWaves, w = wi % kWaves;     // split within the workgroup, wavefront within the split
-    const int s = blockIdx.x * kPairSub + sg;         // this wavefront's split
-    const int n = lane & 15, g = lane >> 4;
-    const int hq0 = h * G;
-    int N = a.seq_lens[b];
-    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
-    const int start = s * a.split_len;
-    const int end = s < a.splits ? min(start + a.split_len, N) : start;  // no tokens past the last split
-
-    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
-    const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
-    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
-    const int k_norm = n * VB, k_word = n * VB + 4 + 16 * g, v_norm = n * VB, v_word = 4 * g * VB + 4 + 4 * n;
-    uint32_t* wa = sm.wa[wi];
-
-    int t0 = start + w * TT;
-    KeyTile<NTB, 1> kt;
-    ValueTile<NTB, 1> vt;
-    if (t0 < end) {
-        load_keys<VB>(kt, krs, k_norm, k_word, t0 * VB);
-        load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
-    }
-
-    // the pair table: thread t writes copies 8 (t >> 8) .. +7 of byte t & 255
-    {
-        const int byte = tid & 255;
-        const uint2 e = make_uint2(bf16_split(cb.centroids[byte & 15]), bf16_split(cb.centroids[byte >> 4]));
-#pragma unroll
-        for (int c = 0; c < kPairCopies / 4; ++c) sm.u.op.table[byte * kPairCopies + (tid >> 8) * (kPairCopies / 4) + c] = e;
-    }
-    if (ROWS < 16 && lane < 16) wa[C::WA - 16 + lane] = 0u;
-    // query A operand (as in decode_partial_bf16_kernel): wavefronts 0..7 build chunk wi
-    if (wi < 8) {
-        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
-        const int hm = n >> 1, r = n & 1;
-        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + (hm < G ? hm : 0)) * D;
-        u32x4 v;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t pr = bf16_split(qg[32 * g + 4 * wi + u] * qscale);
-            const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
-            v[u] = n < ROWS ? (half | (half << 16)) : 0u;
-        }
-        sm.u.op.qa[wi][lane] = v;
-    }
-    __syncthreads();
-
-    float m_run[2], l_run[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        m_run[e] = (2 * g + e < G) ? -INFINITY : 0.0f;
-        l_run[e] = 0.0f;
-    }
-    f32x4 acc[8];
-#pragma unroll
-    for (int cb8 = 0; cb8 < 8; ++cb8) acc[cb8] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const char* tab = reinterpret_cast<const char*>(sm.u.op.table);
-    uint32_t addr[kPairAddr];
-#pragma unroll
-    for (int i = 0; i < kPairAddr; ++i) addr[i] = (lane & 31) * 8u;  // bits 8..15 take the code byte
-    const uint32_t* wa_rd = n < ROWS ? wa + n * 16 + 4 * g : wa + C::WA - 16 + 4 * g;
-    const int wa_step = n < ROWS ? ROWS * 16 : 0;
-    constexpr int kStep = kWaves * TT;
-
-    for (; t0 < end; t0 += kStep) {
-        const int nv = min(TT, end - t0);
-        const int t_next = t0 + kStep < end ? t0 + kStep : t0;
-
-        // ---- scores: job J = S * NTB + tb, chunk S = bytes 2(S&1), 2(S&1)+1 of key word S/2
-        f32x4 dsc[NTB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) dsc[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        float nk[NTB];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) nk[tb] = half_bits_to_float(kt.norm[tb][0]);
-        {
-            constexpr int NS = 8, NJ = NS * NTB, R = kPairLookahead + 1, QB = 1 + (kPairLookahead + NTB - 1) / NTB;
-            uint2 ring[R][2];
-            u32x4 qk[QB];
-            static_for<NJ + kPairLookahead>([&](auto jc) {
-                constexpr int J = decltype(jc)::value;
-                if constexpr (J < NJ) {
-                    constexpr int S = J / NTB, TB = J % NTB, Q0 = 2 * (S & 1);
-                    if constexpr (TB == 0) qk[S % QB] = sm.u.op.qa[S][lane];
-                    const uint32_t x = kt.w[TB][0][S >> 1];
-                    uint32_t& a0 = addr[(2 * J) % kPairAddr];
-                    uint32_t& a1 = addr[(2 * J + 1) % kPairAddr];
-                    put_byte1<Q0>(a0, x);
-                    put_byte1<Q0 + 1>(a1, x);
-                    ring[J % R][0] = *reinterpret_cast<const uint2*>(tab + a0);
-                    ring[J % R][1] = *reinterpret_cast<const uint2*>(tab + a1);
-                }
-                if constexpr (J >= kPairLookahead) {
-                    constexpr int M = J - kPairLookahead, S = M / NTB, TB = M % NTB;
-                    const uint2 e0 = ring[M % R][0], e1 = ring[M % R][1];
-                    dsc[TB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qk[S % QB]),
-                                                                     __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y}),
-                                                                     dsc[TB], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
-        load_keys<VB>(kt, krs, k_norm, k_word, t_next * VB);
-
-        // ---- online softmax (as in decode_partial_bf16_kernel)
-        const bool live = 2 * g < G;
-        float tv[NTB][2];
-        float mx[2] = {-INFINITY, -INFINITY};
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const bool ok = live && 16 * tb + n < nv;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float sc = nk[tb] * (dsc[tb][2 * e] + dsc[tb][2 * e + 1]);
-                tv[tb][e] = ok ? sc : -INFINITY;
-                mx[e] = fmaxf(mx[e], tv[tb][e]);
-            }
-        }
-        if (a.scores) {
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-                for (int e = 0; e < 2; ++e)
-                    if (tv[tb][e] != -INFINITY)
-                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 2 * g + e) * a.capacity + t0 + 16 * tb + n] =
-                            tv[tb][e] * kLn2;
-        }
-        if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kRescaleSlack || mx[1] > m_run[1] + kRescaleSlack) != 0) {
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float mn = fmaxf(m_run[e], row16_max(mx[e]));
-                const float alpha = mn == m_run[e] ? 1.0f : __builtin_amdgcn_exp2f(m_run[e] - mn);
-                l_run[e] *= alpha;
-#pragma unroll
-                for (int cb8 = 0; cb8 < 8; ++cb8) {
-                    acc[cb8][2 * e] *= alpha;
-                    acc[cb8][2 * e + 1] *= alpha;
-                }
-                m_run[e] = mn;
-            }
-        }
-        float pw[NTB][2];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-            const bool tok = 16 * tb + n < nv;
-            // rows past the sequence end hold whatever the cache held: weight exactly 0
-            const float nvn = tok ? half_bits_to_float(vt.norm[tb][0]) : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float p = __builtin_amdgcn_exp2f(tv[tb][e] - m_run[e]);
-                l_run[e] += p;
-                pw[tb][e] = p * nvn;
-            }
-        }
-        if (live) {
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const float wt = pw[tb][e];
-                    const uint32_t bits = __float_as_uint(wt);
-                    const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                    uint32_t* dst = wa + (tb * ROWS + 4 * g + 2 * e) * 16 + n;
-                    dst[0] = dup_hi16(bits);
-                    dst[16] = dup_hi16(__float_as_uint(lo));
-                }
-        }
-        lds_order();
-
-        // ---- values: job J = (tb, cb); the pair bytes of tokens (4g, 4g+1) and
-        // (4g+2, 4g+3) for nibble cb; two lookups per job
-        {
-            u32x4 av[NTB];
-            uint32_t pb[NTB][2][2];  // [tb][token pair][even / odd nibbles]
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) {
-                av[tb] = *reinterpret_cast<const u32x4*>(wa_rd + tb * wa_step);
-#pragma unroll
-                for (int p2 = 0; p2 < 2; ++p2) {
-                    const uint32_t w0 = vt.w[tb][0][2 * p2], w1 = vt.w[tb][0][2 * p2 + 1];
-                    pb[tb][p2][0] = (w0 & 0x0F0F0F0Fu) | ((w1 << 4) & 0xF0F0F0F0u);
-                    pb[tb][p2][1] = ((w0 >> 4) & 0x0F0F0F0Fu) | (w1 & 0xF0F0F0F0u);
-                }
-            }
-            // the value words now live in pb and the norms were used by the
-            // softmax: the next tile's values are requested a whole tile ahead
-            load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
-            constexpr int NJ = NTB * 8, R = kPairLookahead + 1;
-            uint2 ring[R][2];
-            static_for<NJ + kPairLookahead>([&](auto jc) {
-                constexpr int J = decltype(jc)::value;
-                if constexpr (J < NJ) {
-                    constexpr int TB = J / 8, CB = J % 8;
-                    uint32_t& a0 = addr[(2 * J) % kPairAddr];
-                    uint32_t& a1 = addr[(2 * J + 1) % kPairAddr];
-                    put_byte1<CB / 2>(a0, pb[TB][0][CB & 1]);
-                    put_byte1<CB / 2>(a1, pb[TB][1][CB & 1]);
-                    ring[J % R][0] = *reinterpret_cast<const uint2*>(tab + a0);
-                    ring[J % R][1] = *reinterpret_cast<const uint2*>(tab + a1);
-                }
-                if constexpr (J >= kPairLookahead) {
-                    constexpr int M = J - kPairLookahead, TB = M / 8, CB = M % 8;
-                    const uint2 e0 = ring[M % R][0], e1 = ring[M % R][1];
-                    acc[CB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av[TB]),
-                                                                     __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y}),
-                                                                     acc[CB], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
-        }
-        lds_order();
-    }
-
-    // ---- merge the four wavefronts of each split and write its record
-#pragma unroll
-    for (int e = 0; e < 2; ++e) l_run[e] = row16_sum(l_run[e]);
-
-    __syncthreads();  // every lookup of the workgroup is done: the table area becomes the merge buffer
-    float* red = sm.u.red;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const int hh = 2 * g + e;
-        if (hh < G) {
-            float* r = red + (wi * G + hh) * (2 + D);
-            if (n == 0) { r[0] = m_run[e]; r[1] = l_run[e]; }
-#pragma unroll
-            for (int cb8 = 0; cb8 < 8; ++cb8) r[2 + 8 * n + cb8] = acc[cb8][2 * e] + acc[cb8][2 * e + 1];
-        }
-    }
-    __syncthreads();
-    if (s < a.splits) {
-        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
-        for (int idx = tid % (kWaves * 64); idx < G * D; idx += kWaves * 64) {
-            const int gg = idx / D, j = idx % D;
-            float M = -INFINITY;
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[((sg * kWaves + ww) * G + gg) * (2 + D)]);
-            float L = 0.0f, A = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const float* r = red + ((sg * kWaves + ww) * G + gg) * (2 + D);
-                const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-                L = fmaf(r[1], f, L);
-                A = fmaf(r[2 + j], f, A);
-            }
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-            a.acc[rec * D + j] = A;
-            if (j == 0) a.ml[rec] = make_float2(M, L);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// PQ4 decode on the 2:4-sparse matrix cores (d = 128, G = 4 or 8, K and V
-// sharing one centroid table).  v_smfmac_f32_16x16x64_bf16 multiplies a
+// PQ4 decode on the 2:4-sparse matrix cores (d = 128, G = 4 or 8; at G = 4
+// the values may bring centroids of their own, in a second pair table).
+// v_smfmac_f32_16x16x64_bf16 multiplies a
 // 16 x 64 A operand with at most two nonzeros in every aligned group of four
 // k (stored compressed, their positions in an index register) by a dense
 // 64 x 16 B operand, at the issue cost of a dense 16 x 16 x 32 product.
@@ -1664,13 +1368,6 @@ int launch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& c
 
 // tokens per wavefront tile of the bf16 decode kernel (16 or a multiple of 16 dividing 64)
 constexpr int kBf16Tile = 32;
-
-template <int G>
-int launch_partial_pair(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cb, hipStream_t st) {
-    dim3 grid((a.splits + kPairSub - 1) / kPairSub, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_pair_kernel<G>), grid, dim3(kPairWaves * 64), 0, st, a, to_dev(cb));
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-}
 
 template <int G, bool VTAB>
 int launch_partial_sparse(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
