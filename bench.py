@@ -266,7 +266,7 @@ def main():
                               "decode_combine": combine_ms},
         "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
         "roofline": {
-            "kernel": "decode_partial_pair_kernel<4>",
+            "kernel": "decode_partial_sparse_kernel<4, false>",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
