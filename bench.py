@@ -195,34 +195,47 @@ def main():
     ws = torch.empty(tq.decode_workspace_bytes(L, args.split_tokens), dtype=torch.uint8, device=dev)
     splits = tq.decode_splits(L, args.split_tokens)
 
+    # Timed steps carry two events, around decode_partial (the roofline kernel); every event is a
+    # packet on the stream that delays the next kernel by a few microseconds.  The per-kernel
+    # breakdown of the whole step comes from the last warm-up steps, which carry five.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
+    n_probe = min(args.warmup, 50)
 
-    def step(s):
+    def step(s, marks):
         kc, vc = caches[s % args.copies]
         e = ev[s]
-        e[0].record()
+        if marks == 5:
+            e[0].record()
         tq.quantize_append(L, cbk, cbv, None, k_new[s], v_new[s], dst_row, kc, vc)
-        e[1].record()
+        if marks == 5:
+            e[1].record()
         tq.rotate_sketch_query(L, cbk, None, qs[s], q_rot, None)
         e[2].record()
         tq.decode_partial(L, cbk, cbv, q_rot, None, kc, vc, seq_lens, ws, split_tokens=args.split_tokens)
         e[3].record()
         tq.decode_combine(L, cbv, ws, out, split_tokens=args.split_tokens)
-        e[4].record()
+        if marks == 5:
+            e[4].record()
 
     for s in range(args.warmup):
-        step(s)
+        step(s, 5 if s >= args.warmup - n_probe else 2)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.warmup, total):
-        step(s)
+        step(s, 2)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
 
-    def mean_ms(i, j):
-        return float(np.mean([ev[s][i].elapsed_time(ev[s][j]) for s in range(args.warmup, total)]))
+    def mean_ms(i, j, steps):
+        if len(steps) == 0:
+            return None
+        return float(np.mean([ev[s][i].elapsed_time(ev[s][j]) for s in steps]))
 
-    append_ms, rot_ms, partial_ms, combine_ms = mean_ms(0, 1), mean_ms(1, 2), mean_ms(2, 3), mean_ms(3, 4)
+    probe_steps = range(args.warmup - n_probe, args.warmup)
+    timed_steps = range(args.warmup, total)
+    partial_ms = mean_ms(2, 3, timed_steps)
+    append_ms, rot_ms, combine_ms = (mean_ms(0, 1, probe_steps), mean_ms(1, 2, probe_steps),
+                                     mean_ms(3, 4, probe_steps))
     ms_step = t_total / args.steps * 1e3
     alg_bytes = B * Hkv * N * (tq.vector_bytes(tq.FMT_PQ4, d) * 2)
     achieved = alg_bytes / (partial_ms * 1e-3) / 1e9
@@ -264,6 +277,9 @@ def main():
         },
         "step_breakdown_ms": {"append": append_ms, "rotate_query": rot_ms, "decode_partial": partial_ms,
                               "decode_combine": combine_ms},
+        "step_breakdown_note": (f"decode_partial: HIP events around each of the {args.steps} timed launches; "
+                                f"append, rotate_query and decode_combine: the last {n_probe} warm-up steps, "
+                                "which carry events around every kernel"),
         "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
         "roofline": {
             "kernel": "decode_partial_sparse_kernel<4, false>",

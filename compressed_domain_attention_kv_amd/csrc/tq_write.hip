@@ -60,8 +60,9 @@ constexpr int vec_bytes_c() {
                               : 12 * (D / kGroup);
 }
 
+// The rows of workgroup `block` of one quantize grid.
 template <int FMT, int D, Src SRC>
-__global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, DevCodebook cb) {
+__device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodebook& cb, int block) {
     constexpr int LPV = D / 8;                  // lanes per vector
     constexpr int VPB = kWriteThreads / LPV;    // vectors per workgroup
     constexpr int VB = vec_bytes_c<FMT, D>();
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, De
     const int tid = threadIdx.x;
     const int l = tid % LPV;
     const int slot = tid / LPV;
-    const int vec = blockIdx.x * VPB + slot;
+    const int vec = block * VPB + slot;
     bool active = vec < a.nvec;
 
     // destination byte offset of this vector
@@ -228,6 +229,22 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, De
     }
 }
 
+template <int FMT, int D, Src SRC>
+__global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, DevCodebook cb) {
+    quantize_rows<FMT, D, SRC>(a, cb, blockIdx.x);
+}
+
+// Keys and values of one append in one launch when they share a format: the
+// first kblocks workgroups take the keys, the rest the values.
+template <int FMT, int D>
+__global__ __launch_bounds__(kWriteThreads) void quantize_kv_kernel(WriteArgs ak, WriteArgs av, DevCodebook cbk,
+                                                                    DevCodebook cbv, int kblocks) {
+    if (static_cast<int>(blockIdx.x) < kblocks)
+        quantize_rows<FMT, D, Src::kFp16Rows>(ak, cbk, blockIdx.x);
+    else
+        quantize_rows<FMT, D, Src::kFp16Rows>(av, cbv, blockIdx.x - kblocks);
+}
+
 // q_rot = Pi q = H (s * q) / sqrt(d); for TQ3K keys also q_sketch = S q.
 template <int D, bool SKETCH>
 __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float* __restrict__ q, float* __restrict__ q_rot,
@@ -288,6 +305,16 @@ int launch_quantize(const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+template <int FMT, int D>
+int launch_quantize_kv(const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk, const tq_codebook& cbv,
+                       hipStream_t st) {
+    constexpr int VPB = kWriteThreads / (D / 8);
+    const int kblocks = (ak.nvec + VPB - 1) / VPB;
+    hipLaunchKernelGGL((quantize_kv_kernel<FMT, D>), dim3(2 * kblocks), dim3(kWriteThreads), 0, st, ak, av, to_dev(cbk),
+                       to_dev(cbv), kblocks);
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 template <Src SRC>
 int dispatch_quantize(int fmt, int d, const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
 #define TQ_Q(F)                                                                        \
@@ -336,12 +363,22 @@ int tq_quantize_append(const tq_layout* L, const tq_codebook* cbk, const tq_code
     a.hkv = L->n_kv_heads;
     a.capacity = L->capacity;
     a.batch = L->batch;
+    WriteArgs av = a;
     a.x = k_new;
     a.out = static_cast<uint8_t*>(k_cache);
+    av.x = v_new;
+    av.out = static_cast<uint8_t*>(v_cache);
+    // one launch for both tensors when they share the format (PQ4, PQ3)
+    if (L->k_format == L->v_format && (L->k_format == TQ_FMT_PQ4 || L->k_format == TQ_FMT_PQ3)) {
+        const bool d128 = L->head_dim == 128;
+        if (L->k_format == TQ_FMT_PQ4)
+            return d128 ? launch_quantize_kv<TQ_FMT_PQ4, 128>(a, av, *cbk, *cbv, stream)
+                        : launch_quantize_kv<TQ_FMT_PQ4, 256>(a, av, *cbk, *cbv, stream);
+        return d128 ? launch_quantize_kv<TQ_FMT_PQ3, 128>(a, av, *cbk, *cbv, stream)
+                    : launch_quantize_kv<TQ_FMT_PQ3, 256>(a, av, *cbk, *cbv, stream);
+    }
     if ((st = dispatch_quantize<Src::kFp16Rows>(L->k_format, L->head_dim, a, *cbk, stream)) != TQ_OK) return st;
-    a.x = v_new;
-    a.out = static_cast<uint8_t*>(v_cache);
-    return dispatch_quantize<Src::kFp16Rows>(L->v_format, L->head_dim, a, *cbv, stream);
+    return dispatch_quantize<Src::kFp16Rows>(L->v_format, L->head_dim, av, *cbv, stream);
 }
 
 int tq_quantize_rotated(int format, const tq_codebook* cb, const float* S_dev, const float* y, const uint16_t* norm16,
