@@ -195,10 +195,16 @@ def main():
     ws = torch.empty(tq.decode_workspace_bytes(L, args.split_tokens), dtype=torch.uint8, device=dev)
     splits = tq.decode_splits(L, args.split_tokens)
 
-    # Timed steps carry two events, around decode_partial (the roofline kernel); every event is a
-    # packet on the stream that delays the next kernel by a few microseconds.  The per-kernel
-    # breakdown of the whole step comes from the last warm-up steps, which carry five.
+    # decode_partial (the roofline kernel) runs through tq_decode_partial_timed in every step: the
+    # runtime records its two events on the kernel's own dispatch, so their interval is the kernel
+    # alone and adds no packet to the stream.  Recorded events are packets that delay the next
+    # kernel by a few microseconds, so only the last warm-up steps carry them, around the other
+    # kernels, for the per-kernel breakdown of the step.
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
+    for e in ev:  # create the HIP events now (torch creates them on first record)
+        e[2].record()
+        e[3].record()
+    torch.cuda.synchronize()
     n_probe = min(args.warmup, 50)
 
     def step(s, marks):
@@ -210,9 +216,8 @@ def main():
         if marks == 5:
             e[1].record()
         tq.rotate_sketch_query(L, cbk, None, qs[s], q_rot, None)
-        e[2].record()
-        tq.decode_partial(L, cbk, cbv, q_rot, None, kc, vc, seq_lens, ws, split_tokens=args.split_tokens)
-        e[3].record()
+        tq.decode_partial(L, cbk, cbv, q_rot, None, kc, vc, seq_lens, ws, split_tokens=args.split_tokens,
+                          events=(e[2].cuda_event, e[3].cuda_event))
         tq.decode_combine(L, cbv, ws, out, split_tokens=args.split_tokens)
         if marks == 5:
             e[4].record()
@@ -277,9 +282,10 @@ def main():
         },
         "step_breakdown_ms": {"append": append_ms, "rotate_query": rot_ms, "decode_partial": partial_ms,
                               "decode_combine": combine_ms},
-        "step_breakdown_note": (f"decode_partial: HIP events around each of the {args.steps} timed launches; "
-                                f"append, rotate_query and decode_combine: the last {n_probe} warm-up steps, "
-                                "which carry events around every kernel"),
+        "step_breakdown_note": (f"decode_partial: HIP events on the kernel's own dispatch in each of the "
+                                f"{args.steps} timed steps (tq_decode_partial_timed); append, rotate_query and "
+                                f"decode_combine: the last {n_probe} warm-up steps, with events between kernels "
+                                "(rotate_query includes the dispatch of decode_partial)"),
         "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
         "roofline": {
             "kernel": "decode_partial_sparse_kernel<4, false>",

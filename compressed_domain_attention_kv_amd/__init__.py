@@ -6,7 +6,7 @@ the library's HIP kernels; PyTorch provides device memory (tensors) and the
 stream (``torch.cuda.current_stream()``).  Importing this package without a
 built ``libtq.so`` raises: there is no fallback.
 
-Build the library with ``python -m compressed_domain_attention_kv_amd.build``.
+Build the library with ``python compressed_domain_attention_kv_amd/build.py``.
 """
 
 from ._binding import (  # noqa: F401

@@ -18,7 +18,7 @@ library_path = os.path.join(_HERE, "libtq.so")
 
 if not os.path.exists(library_path):
     raise ImportError(
-        f"{library_path} is missing: build it with `python -m compressed_domain_attention_kv_amd.build`")
+        f"{library_path} is missing: build it with `python compressed_domain_attention_kv_amd/build.py`")
 
 # torch ships its own HIP runtime with the same SONAME (libamdhip64.so.7) as
 # the system one libtq links against.  Loading torch first makes the dynamic
@@ -106,6 +106,8 @@ lib.tq_decode_attention.restype = _I
 lib.tq_decode_attention.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]
 lib.tq_decode_partial.restype = _I
 lib.tq_decode_partial.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]
+lib.tq_decode_partial_timed.restype = _I
+lib.tq_decode_partial_timed.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P, _P, _P]
 lib.tq_decode_combine.restype = _I
 lib.tq_decode_combine.argtypes = [_PL, _PC, _I, _P, _SZ, _P, _P]
 
@@ -198,11 +200,18 @@ def decode_attention(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, o
 
 
 def decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, ws, scores=None, split_tokens=0,
-                   stream=None):
-    _check(lib.tq_decode_partial(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q_rot),
-                                 _ptr(q_sketch), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), _ptr(scores),
-                                 split_tokens, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "tq_decode_partial")
+                   stream=None, events=None):
+    """events: optional (start, stop) raw hipEvent_t handles, recorded at the
+    kernel's own start and end (tq_decode_partial_timed)."""
+    args = (ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q_rot), _ptr(q_sketch), _ptr(k_cache),
+            _ptr(v_cache), _ptr(seq_lens), _ptr(scores), split_tokens, _ptr(ws), ws.numel() * ws.element_size(),
+            _stream(stream))
+    if events is None:
+        _check(lib.tq_decode_partial(*args), "tq_decode_partial")
+    else:
+        start, stop = events
+        _check(lib.tq_decode_partial_timed(*args, ctypes.c_void_p(start), ctypes.c_void_p(stop)),
+               "tq_decode_partial_timed")
 
 
 def decode_combine(L, cbv, ws, out, split_tokens=0, stream=None):

@@ -1,6 +1,8 @@
 """Build libtq.so in-tree for gfx950 with hipcc.
 
-    python -m compressed_domain_attention_kv_amd.build [--jobs N]
+    python compressed_domain_attention_kv_amd/build.py [--jobs N]
+
+Run it as a file: importing the package loads the library it rebuilds.
 
 Every HIP source is compiled with packed-FP32 instructions disabled; the host
 core is plain C++17.  The library lands next to this file as ``libtq.so``.

@@ -18,6 +18,7 @@
 // normalizes and, for rotated value formats, applies Pi^T once.
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <utility>
@@ -1357,13 +1358,27 @@ int resolve_splits(const tq_layout* L, int split_tokens, int* split_len) {
     return (L->capacity + len - 1) / len;
 }
 
+// Stream of a decode launch, and optionally events that the runtime attaches to
+// the kernel's own dispatch (start and end of the kernel itself).
+struct Launch {
+    hipStream_t st;
+    hipEvent_t start, stop;
+};
+
+template <typename K, typename... Args>
+int launch_kernel(K kernel, dim3 grid, dim3 block, const Launch& l, Args... args) {
+    if (l.start || l.stop)
+        hipExtLaunchKernelGGL(kernel, grid, block, 0, l.st, l.start, l.stop, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, 0, l.st, args...);
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 template <int KF, int VF, int D, int G>
 int launch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                   hipStream_t st) {
+                   const Launch& l) {
     dim3 grid(a.splits, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_kernel<KF, VF, D, G>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
-                       to_dev(cbv));
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+    return launch_kernel(decode_partial_kernel<KF, VF, D, G>, grid, dim3(kWaves * 64), l, a, to_dev(cbk), to_dev(cbv));
 }
 
 // tokens per wavefront tile of the bf16 decode kernel (16 or a multiple of 16 dividing 64)
@@ -1371,11 +1386,10 @@ constexpr int kBf16Tile = 32;
 
 template <int G, bool VTAB>
 int launch_partial_sparse(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                          hipStream_t st) {
+                          const Launch& l) {
     dim3 grid((a.splits + kPairSub - 1) / kPairSub, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_sparse_kernel<G, VTAB>), grid, dim3(kPairWaves * 64), 0, st, a, to_dev(cbk),
-                       to_dev(cbv));
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+    return launch_kernel(decode_partial_sparse_kernel<G, VTAB>, grid, dim3(kPairWaves * 64), l, a, to_dev(cbk),
+                         to_dev(cbv));
 }
 
 // K and V decode through one table only when their centroids are identical
@@ -1388,16 +1402,15 @@ bool same_centroids(const tq_codebook& x, const tq_codebook& y) {
 
 template <int D, int G>
 int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                        hipStream_t st) {
+                        const Launch& l) {
     dim3 grid(a.splits, L->n_kv_heads, L->batch);
-    hipLaunchKernelGGL((decode_partial_bf16_kernel<D, G, kBf16Tile>), grid, dim3(kWaves * 64), 0, st, a, to_dev(cbk),
-                       to_dev(cbv));
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+    return launch_kernel(decode_partial_bf16_kernel<D, G, kBf16Tile>, grid, dim3(kWaves * 64), l, a, to_dev(cbk),
+                         to_dev(cbv));
 }
 
 template <int KF, int VF, int D>
 int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                   hipStream_t st) {
+                   const Launch& st) {
     if constexpr (KF == TQ_FMT_PQ4 && VF == TQ_FMT_PQ4) {
         // the matrix-core kernel addresses a stream through a 32-bit buffer range
         const bool fits = static_cast<size_t>(L->capacity) * vbytes<TQ_FMT_PQ4, D>() <= 0x7FFFFFFFu;
@@ -1424,7 +1437,7 @@ int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_code
 
 template <int KF, int VF>
 int dispatch_dim(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                 hipStream_t st) {
+                 const Launch& st) {
     const int G = L->n_q_heads / L->n_kv_heads;
     return L->head_dim == 128 ? dispatch_group<KF, VF, 128>(G, a, L, cbk, cbv, st)
                               : dispatch_group<KF, VF, 256>(G, a, L, cbk, cbv, st);
@@ -1458,10 +1471,14 @@ size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens) {
     return recs * sizeof(float2) + recs * L->head_dim * sizeof(float);
 }
 
-int tq_decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
-                      const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                      float* scores, int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream) {
-    using namespace tq;
+}  // extern "C"
+
+namespace tq {
+namespace {
+
+int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                   const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream) {
     int st = check_decode(L, cbk, cbv);
     if (st != TQ_OK) return st;
     int len = 0;
@@ -1494,6 +1511,27 @@ int tq_decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codeb
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
     if (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V) return dispatch_dim<TQ_FMT_TQ3K, TQ_FMT_GQ2V>(a, L, *cbk, *cbv, stream);
     return TQ_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+int tq_decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                      const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                      float* scores, int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return tq::decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
+                              ws_bytes, tq::Launch{stream, nullptr, nullptr});
+}
+
+int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                            const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                            float* scores, int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop) {
+    if (!start || !stop) return TQ_ERR_INVALID;
+    return tq::decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
+                              ws_bytes, tq::Launch{stream, start, stop});
 }
 
 int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_tokens, const void* ws, size_t ws_bytes,

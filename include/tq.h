@@ -249,6 +249,18 @@ int tq_decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codeb
                       const void* v_cache, const int32_t* seq_lens, float* scores,
                       int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* tq_decode_partial with HIP events attached to the kernel's own dispatch
+ * (hipExtLaunchKernel): start and stop, created by the caller, are recorded
+ * when the kernel begins and ends, so hipEventElapsedTime(start, stop) is the
+ * kernel's duration without the queue and event-packet gaps around it.  For
+ * profiling callers.  Errors: those of tq_decode_partial, and TQ_ERR_INVALID
+ * for a null event.                                                        */
+int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
+                            const float* q_rot, const float* q_sketch, const void* k_cache,
+                            const void* v_cache, const int32_t* seq_lens, float* scores,
+                            int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream,
+                            hipEvent_t start, hipEvent_t stop);
+
 /* Second half: merge the split records (m = max m_p, l = sum l_p 2^(m_p-m),
  * acc = sum acc_p 2^(m_p - m)), normalize o = acc / l (o = 0 when l = 0) and
  * rotate back with the V codebook's signs for PQ4/PQ3 values.              */

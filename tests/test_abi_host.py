@@ -129,5 +129,10 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert tq.lib.tq_decode_partial(r(Lg), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
                                     1 << 30, None) == -2
     assert tq.lib.tq_decode_combine(r(L), r(cb), 0, fake, need - 1, fake, None) == -3
+    # the timed variant needs both events, and checks its arguments like the plain call
+    assert tq.lib.tq_decode_partial_timed(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
+                                          need, None, None, fake) == -1
+    assert tq.lib.tq_decode_partial_timed(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
+                                          need - 1, None, fake, fake) == -3
     assert tq.lib.tq_quantize_rotated(9, r(cb), None, fake, fake, 1, fake, None) == -2
     assert tq.strerror(-3).startswith("workspace")

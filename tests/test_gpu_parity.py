@@ -235,6 +235,30 @@ def test_decode_edge_lengths():
             assert np.all(np.isnan(scores[b, :, n:]))
 
 
+def test_timed_partial_matches_untimed():
+    """tq_decode_partial_timed writes the same records as tq_decode_partial and
+    its events span a positive kernel time."""
+    w = REDUCED["c4"]
+    st = P.Setup(w)
+    L = st.layout()
+    lens = _lens(w)
+    kb, vb, _, _ = _oracle_cache(st, w, lens)
+    kc = _garbage_cache(st, L, synth.K_TENSOR, kb)
+    vc = _garbage_cache(st, L, synth.V_TENSOR, vb)
+    q_rot = torch.empty((L.batch, L.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    tq.rotate_sketch_query(L, st.cbk, None, torch.from_numpy(synth.queries(w)).cuda(), q_rot, None)
+    sl = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    wss = [torch.zeros(tq.decode_workspace_bytes(L), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    tq.decode_partial(L, st.cbk, st.cbv, q_rot, None, kc, vc, sl, wss[0])
+    tq.decode_partial(L, st.cbk, st.cbv, q_rot, None, kc, vc, sl, wss[1], events=(e0.cuda_event, e1.cuda_event))
+    torch.cuda.synchronize()
+    assert torch.equal(wss[0], wss[1])
+    assert e0.elapsed_time(e1) > 0.0
+
+
 def test_single_key_returns_its_value_on_gpu():
     w = synth.scaled(REDUCED["c4"], batch=1, capacity=64, context=1)
     st = P.Setup(w)
