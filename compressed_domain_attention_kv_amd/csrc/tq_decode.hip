@@ -987,45 +987,61 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int k_norm = n * VB, k_word = n * VB + 4 + 16 * g, v_norm = n * VB, v_word = 4 * g * VB + 4 + 4 * n;
     uint32_t* wa = sm.wa[wi];
 
-    int t0 = start + w * TT;
-    KeyTile<NTB, 1> kt;
-    ValueTile<NTB, 1> vt;
-    if (t0 < end) {
-        load_keys<VB>(kt, krs, k_norm, k_word, t0 * VB);
-        load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
-    }
-
-    // the pair tables: thread t writes copies 8 (t >> 8) .. +7 of byte t & 255
-    {
-        const int byte = tid & 255;
-        const uint2 e = make_uint2(bf16_split(cbk.centroids[byte & 15]), bf16_split(cbk.centroids[byte >> 4]));
+    // The small global reads of the prologue come first: a tile load issued before them would
+    // have to complete before their values can be used (the memory counter drains in order).
+    //   * table entries: thread t writes entries t + 1024 k (k = 0..7) of every table, so each
+    //     store instruction covers 512 contiguous bytes (no bank conflicts); entry i is byte
+    //     i / 32, whose low nibble is the same for all k and whose high nibble is t / 512 + 2k;
+    //   * compressed score A operand: wavefront wi < 4 RB builds product I = wi % 4 of row block
+    //     wi / 4; lane (row n, group g) holds, per group q, the pair (q_r, q_r) of coordinate
+    //     2m + p, where m is the code byte that B lane group sp_lane_group(4g + q) reads as
+    //     element quad sp_quad(4g + q).
+    static_assert(kPairWaves * 64 == 1024, "the table fill assumes 1024 threads");
+    const int lo_nib = (tid >> 5) & 15, hi_base = tid >> 9;
+    float ck_lo = cbk.centroids[lo_nib], ck_hi[8], cv_lo = 0.0f, cv_hi[8];
 #pragma unroll
-        for (int c = 0; c < kPairCopies / 4; ++c) sm.u.op.table[byte * kPairCopies + (tid >> 8) * (kPairCopies / 4) + c] = e;
-        if constexpr (VTAB) {
-            const uint2 ev = make_uint2(bf16_split(cbv.centroids[byte & 15]), bf16_split(cbv.centroids[byte >> 4]));
+    for (int k = 0; k < 8; ++k) ck_hi[k] = cbk.centroids[hi_base + 2 * k];
+    if constexpr (VTAB) {
+        cv_lo = cbv.centroids[lo_nib];
 #pragma unroll
-            for (int c = 0; c < kPairCopies / 4; ++c)
-                sm.u.op.vtable[byte * kPairCopies + (tid >> 8) * (kPairCopies / 4) + c] = ev;
-        }
+        for (int k = 0; k < 8; ++k) cv_hi[k] = cbv.centroids[hi_base + 2 * k];
     }
-    // compressed score A operand: wavefront wi < 4 RB builds product I = wi % 4 of row block wi / 4;
-    // lane (row n, group g) holds, per group q, the pair (q_r, q_r) of coordinate 2m + p, where
-    // m is the code byte that B lane group sp_lane_group(4g + q) reads as element quad sp_quad(4g + q)
+    float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int qrb = wi / 4, qI = wi % 4, qhh = 4 * qrb + (n >> 2), qr = (n >> 1) & 1, qp = n & 1;
     if (wi < 4 * RB) {
-        const int rb = wi / 4, I = wi % 4;
-        const int hh = 4 * rb + (n >> 2), r = (n >> 1) & 1, p = n & 1;
-        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
-        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + hh) * D;
-        u32x4 v;
+        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + qhh) * D;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int gd = 4 * g + q;
-            const int m = 16 * sp_lane_group(gd) + 4 * I + sp_quad(gd);
-            const uint32_t pr = bf16_split(qg[2 * m + p] * qscale);
-            const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
+            qv[q] = qg[2 * (16 * sp_lane_group(gd) + 4 * qI + sp_quad(gd)) + qp];
+        }
+    }
+
+    // the first tile, requested unconditionally: a wavefront without tiles reads bytes it never
+    // uses (the buffer range returns zeros past the stream), and the loads stay on one path, so
+    // the waits of the table fill below count only the small reads above
+    int t0 = start + w * TT;
+    KeyTile<NTB, 1> kt;
+    ValueTile<NTB, 1> vt;
+    load_keys<VB>(kt, krs, k_norm, k_word, t0 * VB);
+    load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        sm.u.op.table[tid + 1024 * k] = make_uint2(bf16_split(ck_lo), bf16_split(ck_hi[k]));
+        if constexpr (VTAB) sm.u.op.vtable[tid + 1024 * k] = make_uint2(bf16_split(cv_lo), bf16_split(cv_hi[k]));
+    }
+    if (wi < 4 * RB) {
+        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+        u32x4 v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t pr = bf16_split(qv[q] * qscale);
+            const uint32_t half = qr ? (pr >> 16) : (pr & 0xFFFFu);
             v[q] = half | (half << 16);
         }
-        sm.u.op.qa[rb][I][lane] = v;
+        sm.u.op.qa[qrb][qI][lane] = v;
     }
     __syncthreads();
 
