@@ -18,11 +18,14 @@ from ._binding import (  # noqa: F401
     FMT_TQ3K,
     Codebook,
     Layout,
+    RING_CAP_MAX,
     TQError,
     build_codebook,
     cache_bytes,
     decode_attention,
+    decode_attention_hybrid,
     decode_combine,
+    decode_hybrid_workspace_bytes,
     decode_partial,
     decode_splits,
     decode_workspace_bytes,
@@ -30,6 +33,9 @@ from ._binding import (  # noqa: F401
     library_path,
     quantize_append,
     quantize_rotated,
+    ring_append,
+    ring_bytes,
+    ring_flush,
     rotate_sketch_query,
     strerror,
     vector_bytes,

@@ -110,6 +110,18 @@ lib.tq_decode_partial_timed.restype = _I
 lib.tq_decode_partial_timed.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P, _P, _P]
 lib.tq_decode_combine.restype = _I
 lib.tq_decode_combine.argtypes = [_PL, _PC, _I, _P, _SZ, _P, _P]
+lib.tq_ring_bytes.restype = _SZ
+lib.tq_ring_bytes.argtypes = [_PL, _I]
+lib.tq_ring_append.restype = _I
+lib.tq_ring_append.argtypes = [_PL, _I, _P, _P, _P, _P, _P, _P]
+lib.tq_ring_flush.restype = _I
+lib.tq_ring_flush.argtypes = [_PL, _PC, _PC, _P, _I, _P, _P, _P, _I, _P, _P, _P]
+lib.tq_decode_hybrid_workspace_bytes.restype = _SZ
+lib.tq_decode_hybrid_workspace_bytes.argtypes = [_PL, _I]
+lib.tq_decode_attention_hybrid.restype = _I
+lib.tq_decode_attention_hybrid.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _SZ, _P]
+
+RING_CAP_MAX = 256
 
 
 class TQError(RuntimeError):
@@ -217,3 +229,31 @@ def decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, ws,
 def decode_combine(L, cbv, ws, out, split_tokens=0, stream=None):
     _check(lib.tq_decode_combine(ctypes.byref(L), ctypes.byref(cbv), split_tokens, _ptr(ws),
                                  ws.numel() * ws.element_size(), _ptr(out), _stream(stream)), "tq_decode_combine")
+
+
+def ring_bytes(L, ring_cap):
+    return int(lib.tq_ring_bytes(ctypes.byref(L), ring_cap))
+
+
+def ring_append(L, ring_cap, k_new, v_new, pos, k_ring, v_ring, stream=None):
+    _check(lib.tq_ring_append(ctypes.byref(L), ring_cap, _ptr(k_new), _ptr(v_new), _ptr(pos), _ptr(k_ring),
+                              _ptr(v_ring), _stream(stream)), "tq_ring_append")
+
+
+def ring_flush(L, cbk, cbv, S_dev, ring_cap, k_ring, v_ring, first, count, k_cache, v_cache, stream=None):
+    _check(lib.tq_ring_flush(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), _ptr(S_dev), ring_cap,
+                             _ptr(k_ring), _ptr(v_ring), _ptr(first), count, _ptr(k_cache), _ptr(v_cache),
+                             _stream(stream)), "tq_ring_flush")
+
+
+def decode_hybrid_workspace_bytes(L, split_tokens=0):
+    return int(lib.tq_decode_hybrid_workspace_bytes(ctypes.byref(L), split_tokens))
+
+
+def decode_attention_hybrid(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, comp_lens, ring_cap, k_ring, v_ring,
+                            ring_lens, out, ws, split_tokens=0, stream=None):
+    _check(lib.tq_decode_attention_hybrid(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q_rot),
+                                          _ptr(q_sketch), _ptr(k_cache), _ptr(v_cache), _ptr(comp_lens), ring_cap,
+                                          _ptr(k_ring), _ptr(v_ring), _ptr(ring_lens), _ptr(out), split_tokens,
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "tq_decode_attention_hybrid")

@@ -53,6 +53,7 @@ struct DecodeArgs {
     int capacity;
     int splits;
     int split_len;
+    int rec_stride;  // records per (b, query head) row of the workspace (splits, or more for hybrid)
 };
 
 // Lane exchange inside a row of 16 lanes through DPP (no LDS traffic).
@@ -123,11 +124,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
     N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
     const int start = s * a.split_len;
     const int end = min(start + a.split_len, N);
-    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;  // record of query head hq0
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.rec_stride + s;  // record of query head hq0
 
     if (start >= end) {  // empty split: (m, l, acc) = (-inf, 0, 0)
         for (int g = 0; g < G; ++g) {
-            const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
+            const size_t rec = rec0 + static_cast<size_t>(g) * a.rec_stride;
             if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
             for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
         }
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
             L = fmaf(r[1], f, L);
             A = fmaf(r[2 + j], f, A);
         }
-        const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
+        const size_t rec = rec0 + static_cast<size_t>(g) * a.rec_stride;
         a.acc[rec * D + j] = A;
         if (j == 0) a.ml[rec] = make_float2(M, L);
     }
@@ -586,11 +587,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
     const int start = s * a.split_len;
     const int end = min(start + a.split_len, N);
-    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.rec_stride + s;
 
     if (start >= end) {
         for (int gg = 0; gg < G; ++gg) {
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.rec_stride;
             if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
             for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
         }
@@ -862,7 +863,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             L = fmaf(r[1], f, L);
             A = fmaf(r[2 + j], f, A);
         }
-        const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+        const size_t rec = rec0 + static_cast<size_t>(gg) * a.rec_stride;
         a.acc[rec * D + j] = A;
         if (j == 0) a.ml[rec] = make_float2(M, L);
     }
@@ -1237,7 +1238,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     __syncthreads();
     if (s < a.splits) {
-        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.rec_stride + s;
         for (int idx = tid % (kWaves * 64); idx < G * D; idx += kWaves * 64) {
             const int gg = idx / D, j = idx % D;
             float M = -INFINITY;
@@ -1251,7 +1252,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 L = fmaf(r[1], f, L);
                 A = fmaf(r[2 + j], f, A);
             }
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.rec_stride;
             a.acc[rec * D + j] = A;
             if (j == 0) a.ml[rec] = make_float2(M, L);
         }
@@ -1347,6 +1348,165 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
     }
 #pragma unroll
     for (int k = 0; k < DPL; ++k) out[static_cast<size_t>(row) * D + DPL * lane + k] = v[k];
+}
+
+// ---------------------------------------------------------------------------
+// Ring part of hybrid attention.  The capture ring keeps the newest tokens of
+// every stream exact (fp16) and the hybrid read attends over them and over
+// the compressed blocks together ([P2] "write path": recent tokens stay exact
+// in a ring buffer until a batch is flushed into compressed blocks; the hybrid
+// mode reads both).  One workgroup per (batch row, KV head) turns the ring's n
+// tokens into one more split record for each of its G query heads, in the
+// units of the compressed records (scores and m in log2 units, acc in the
+// rotated basis for rotated value formats), so decode_combine merges it
+// unchanged.
+constexpr int kRingThreads = 256;
+static_assert(kRingCapMax <= kRingThreads, "one thread per ring token");
+constexpr int kRingMax = kRingCapMax;  // one thread per ring token
+
+struct RingArgs {
+    const float* q_rot;
+    const uint16_t* k_ring;
+    const uint16_t* v_ring;
+    const int32_t* comp_lens;
+    const int32_t* ring_lens;
+    float2* ml;
+    float* acc;
+    int hq;
+    int hkv;
+    int ring_cap;
+    int rec_stride;
+    int ring_rec;  // record index of the ring within its row
+};
+
+// Unnormalized Sylvester Walsh-Hadamard transform of a vector spread over one
+// wavefront: element j = DPL * lane + k sits in v[k].
+template <int DPL>
+__device__ __forceinline__ void wht_wave(float (&v)[DPL], int lane) {
+#pragma unroll
+    for (int st = 1; st < DPL; st <<= 1)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+            if ((k & st) == 0) {
+                const float x = v[k], y = v[k + st];
+                v[k] = x + y;
+                v[k + st] = x - y;
+            }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            const float p = __shfl_xor(v[k], m, 64);
+            v[k] = upper ? (p - v[k]) : (v[k] + p);
+        }
+    }
+}
+
+template <int D, int G, bool ROT>
+__global__ __launch_bounds__(kRingThreads) void ring_partial_kernel(RingArgs r, DevCodebook cbk, DevCodebook cbv) {
+    constexpr int DPL = D / 64;
+    constexpr int NW = kRingThreads / 64;
+    constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
+    __shared__ float qs[G][D];            // unrotated query times log2(e)/sqrt(d)
+    __shared__ float pw[G][kRingMax];     // 2^(s - m) per head and ring token
+    __shared__ float accs[G][D];          // value sums in the unrotated basis
+    __shared__ float red_m[NW][G], red_l[NW][G];
+
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int hq0 = h * G;
+    int n = r.ring_lens[b];
+    n = n < 0 ? 0 : (n > r.ring_cap ? r.ring_cap : n);
+    const int first = max(r.comp_lens[b], 0);  // absolute position of the oldest ring token
+    const size_t row0 = (static_cast<size_t>(b) * r.hkv + h) * r.ring_cap;
+
+    // q = Pi_k^T q_rot = diag(s_k) H q_rot / sqrt(d), one wavefront per head
+    for (int g = w; g < G; g += NW) {
+        const float* src = r.q_rot + (static_cast<size_t>(b) * r.hq + hq0 + g) * D;
+        float v[DPL];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[k] = src[DPL * lane + k];
+        wht_wave<DPL>(v, lane);
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+            qs[g][DPL * lane + k] = v[k] * kInvSqrtD * rotation_sign(cbk, DPL * lane + k) * (kLog2e * kInvSqrtD);
+    }
+    __syncthreads();
+
+    // exact scores, one thread per ring token
+    float sc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) sc[g] = -INFINITY;
+    if (tid < n) {
+        const int slot = (first + tid) % r.ring_cap;
+        const uint4* kr = reinterpret_cast<const uint4*>(r.k_ring + (row0 + slot) * D);
+#pragma unroll
+        for (int g = 0; g < G; ++g) sc[g] = 0.0f;
+        for (int c = 0; c < D / 8; ++c) {
+            const uint4 raw = kr[c];
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float kv = half_bits_to_float((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+#pragma unroll
+                for (int g = 0; g < G; ++g) sc[g] = fmaf(qs[g][8 * c + e], kv, sc[g]);
+            }
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float mw = wave_max(sc[g]);
+        if (lane == 0) red_m[w][g] = mw;
+    }
+    __syncthreads();
+    float M[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        M[g] = red_m[0][g];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) M[g] = fmaxf(M[g], red_m[i][g]);
+        const float p = tid < n ? exp2f(sc[g] - M[g]) : 0.0f;
+        pw[g][tid] = p;
+        const float lw = wave_sum(p);
+        if (lane == 0) red_l[w][g] = lw;
+    }
+    __syncthreads();
+
+    // value sums acc[g][j] = sum_t p[g][t] v_t[j], exact fp16 values
+    for (int idx = tid; idx < G * D; idx += kRingThreads) {
+        const int g = idx / D, j = idx % D;
+        float a = 0.0f;
+        for (int t = 0; t < n; ++t) {
+            const int slot = (first + t) % r.ring_cap;
+            a = fmaf(pw[g][t], half_bits_to_float(r.v_ring[(row0 + slot) * D + j]), a);
+        }
+        accs[g][j] = a;
+    }
+    __syncthreads();
+
+    // record: (m, l) and acc, rotated into the values' basis (Pi_v acc = H diag(s_v) acc / sqrt(d))
+    for (int g = w; g < G; g += NW) {
+        const size_t rec = (static_cast<size_t>(b) * r.hq + hq0 + g) * r.rec_stride + r.ring_rec;
+        float v[DPL];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[k] = accs[g][DPL * lane + k];
+        if constexpr (ROT) {
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) v[k] *= rotation_sign(cbv, DPL * lane + k);
+            wht_wave<DPL>(v, lane);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) v[k] *= kInvSqrtD;
+        }
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) r.acc[rec * D + DPL * lane + k] = v[k];
+        if (lane == 0) {
+            float L = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NW; ++i) L += red_l[i][g];
+            r.ml[rec] = n > 0 ? make_float2(M[g], L) : make_float2(-INFINITY, 0.0f);
+        }
+    }
 }
 
 int auto_split_tokens(const tq_layout* L) {
@@ -1469,6 +1629,16 @@ int check_decode(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* 
     return TQ_OK;
 }
 
+// Workspace of `splits + extra_recs` records per (b, query head) row.
+size_t workspace_bytes(const tq_layout* L, int split_tokens, int extra_recs) {
+    if (check_layout(L) != TQ_OK) return 0;
+    int len = 0;
+    const int splits = resolve_splits(L, split_tokens, &len);
+    if (splits <= 0) return 0;
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * (splits + extra_recs);
+    return recs * sizeof(float2) + recs * L->head_dim * sizeof(float);
+}
+
 }  // namespace
 }  // namespace tq
 
@@ -1481,10 +1651,11 @@ int tq_decode_splits(const tq_layout* L, int split_tokens) {
 }
 
 size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens) {
-    const int splits = tq_decode_splits(L, split_tokens);
-    if (splits <= 0) return 0;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
-    return recs * sizeof(float2) + recs * L->head_dim * sizeof(float);
+    return tq::workspace_bytes(L, split_tokens, 0);
+}
+
+size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens) {
+    return tq::workspace_bytes(L, split_tokens, 1);
 }
 
 }  // extern "C"
@@ -1492,9 +1663,12 @@ size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens) {
 namespace tq {
 namespace {
 
+// Split records of the compressed cache; with extra_recs > 0 every (b, query head)
+// row of the workspace keeps that many more records after the splits.
 int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
                    const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream) {
+                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream,
+                   int extra_recs = 0) {
     int st = check_decode(L, cbk, cbv);
     if (st != TQ_OK) return st;
     int len = 0;
@@ -1505,7 +1679,7 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(ws, 16) || !aligned(q_rot, 4) ||
         !aligned(seq_lens, 4) || (scores && !aligned(scores, 4)) || (q_sketch && !aligned(q_sketch, 4)))
         return TQ_ERR_INVALID;
-    if (ws_bytes < tq_decode_workspace_bytes(L, split_tokens)) return TQ_ERR_WORKSPACE;
+    if (ws_bytes < workspace_bytes(L, split_tokens, extra_recs)) return TQ_ERR_WORKSPACE;
     DecodeArgs a{};
     a.q_rot = q_rot;
     a.q_sk = q_sketch;
@@ -1513,7 +1687,7 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     a.v_cache = static_cast<const uint8_t*>(v_cache);
     a.seq_lens = seq_lens;
     a.scores = scores;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * (splits + extra_recs);
     a.ml = static_cast<float2*>(ws);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
     a.hq = L->n_q_heads;
@@ -1521,12 +1695,55 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     a.capacity = L->capacity;
     a.splits = splits;
     a.split_len = len;
+    a.rec_stride = splits + extra_recs;
     const int kf = L->k_format, vf = L->v_format;
     if (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ4, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ3>(a, L, *cbk, *cbv, stream);
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
     if (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V) return dispatch_dim<TQ_FMT_TQ3K, TQ_FMT_GQ2V>(a, L, *cbk, *cbv, stream);
     return TQ_ERR_UNSUPPORTED;
+}
+
+// Merge `records` records per (b, query head) row, normalize, rotate back.
+int combine(const tq_layout* L, const tq_codebook& cbv, int records, const void* ws, float* out, hipStream_t stream) {
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * records;
+    const float2* ml = static_cast<const float2*>(ws);
+    const float* acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + recs * sizeof(float2));
+    const int rows = L->batch * L->n_q_heads;
+    const bool rot = L->v_format != TQ_FMT_GQ2V;
+    const DevCodebook c = to_dev(cbv);
+    if (L->head_dim == 128) {
+        if (rot) hipLaunchKernelGGL((decode_combine_kernel<128, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
+        else hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
+    } else {
+        if (rot) hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
+        else hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
+    }
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <int D, int G>
+int launch_ring(const RingArgs& r, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+                hipStream_t st) {
+    const dim3 grid(L->n_kv_heads, L->batch);
+    if (L->v_format == TQ_FMT_GQ2V)
+        hipLaunchKernelGGL((ring_partial_kernel<D, G, false>), grid, dim3(kRingThreads), 0, st, r, to_dev(cbk), to_dev(cbv));
+    else
+        hipLaunchKernelGGL((ring_partial_kernel<D, G, true>), grid, dim3(kRingThreads), 0, st, r, to_dev(cbk), to_dev(cbv));
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+template <int D>
+int dispatch_ring(const RingArgs& r, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+                  hipStream_t st) {
+    switch (L->n_q_heads / L->n_kv_heads) {
+        case 1: return launch_ring<D, 1>(r, L, cbk, cbv, st);
+        case 2: return launch_ring<D, 2>(r, L, cbk, cbv, st);
+        case 4: return launch_ring<D, 4>(r, L, cbk, cbv, st);
+        case 5: return launch_ring<D, 5>(r, L, cbk, cbv, st);
+        case 8: return launch_ring<D, 8>(r, L, cbk, cbv, st);
+        default: return TQ_ERR_UNSUPPORTED;
+    }
 }
 
 }  // namespace
@@ -1560,20 +1777,7 @@ int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_toke
     const int splits = resolve_splits(L, split_tokens, &len);
     if (splits <= 0 || !ws || !out || !aligned(ws, 16) || !aligned(out, 4)) return TQ_ERR_INVALID;
     if (ws_bytes < tq_decode_workspace_bytes(L, split_tokens)) return TQ_ERR_WORKSPACE;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
-    const float2* ml = static_cast<const float2*>(ws);
-    const float* acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + recs * sizeof(float2));
-    const int rows = L->batch * L->n_q_heads;
-    const bool rot = L->v_format != TQ_FMT_GQ2V;
-    const DevCodebook c = to_dev(*cbv);
-    if (L->head_dim == 128) {
-        if (rot) hipLaunchKernelGGL((decode_combine_kernel<128, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
-        else hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
-    } else {
-        if (rot) hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
-        else hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, splits, c);
-    }
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+    return combine(L, *cbv, splits, ws, out, stream);
 }
 
 int tq_decode_attention(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
@@ -1584,6 +1788,40 @@ int tq_decode_attention(const tq_layout* L, const tq_codebook* cbk, const tq_cod
                                ws_bytes, stream);
     if (st != TQ_OK) return st;
     return tq_decode_combine(L, cbv, split_tokens, ws, ws_bytes, out, stream);
+}
+
+int tq_decode_attention_hybrid(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                               const float* q_sketch, const void* k_cache, const void* v_cache,
+                               const int32_t* comp_lens, int ring_cap, const void* k_ring, const void* v_ring,
+                               const int32_t* ring_lens, float* out, int split_tokens, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    using namespace tq;
+    if (!out || !k_ring || !v_ring || !ring_lens || !aligned(out, 4) || !aligned(ring_lens, 4) ||
+        !aligned(k_ring, 16) || !aligned(v_ring, 16))
+        return TQ_ERR_INVALID;
+    if (ring_cap < 1 || ring_cap > kRingMax) return TQ_ERR_INVALID;
+    int st = decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, comp_lens, nullptr, split_tokens, ws,
+                            ws_bytes, Launch{stream, nullptr, nullptr}, 1);
+    if (st != TQ_OK) return st;
+    int len = 0;
+    const int splits = resolve_splits(L, split_tokens, &len);
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * (splits + 1);
+    RingArgs r{};
+    r.q_rot = q_rot;
+    r.k_ring = static_cast<const uint16_t*>(k_ring);
+    r.v_ring = static_cast<const uint16_t*>(v_ring);
+    r.comp_lens = comp_lens;
+    r.ring_lens = ring_lens;
+    r.ml = static_cast<float2*>(ws);
+    r.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
+    r.hq = L->n_q_heads;
+    r.hkv = L->n_kv_heads;
+    r.ring_cap = ring_cap;
+    r.rec_stride = splits + 1;
+    r.ring_rec = splits;
+    st = L->head_dim == 128 ? dispatch_ring<128>(r, L, *cbk, *cbv, stream) : dispatch_ring<256>(r, L, *cbk, *cbv, stream);
+    if (st != TQ_OK) return st;
+    return combine(L, *cbv, splits + 1, ws, out, stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@ constexpr int kTile = 64;         // tokens per wavefront tile in the decode ker
 constexpr int kWaves = 4;         // wavefronts per decode workgroup
 constexpr int kSplitQuantum = kTile * kWaves;
 constexpr float kFp16Max = 65504.0f;
+constexpr int kRingCapMax = TQ_RING_CAP_MAX;  // capture ring slots per stream
 
 // Codebook data a kernel needs, passed by value as a kernel argument.
 struct DevCodebook {

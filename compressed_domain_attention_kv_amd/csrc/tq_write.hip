@@ -17,7 +17,10 @@ namespace {
 
 constexpr int kWriteThreads = 256;
 
-enum class Src { kFp16Rows, kRotated };
+// kFp16Rows: fp16 rows x[nvec][d], destination row from dst_row (append);
+// kRotated: fp32 rotated rows y with given norms, dense output (code test);
+// kRing: fp16 rows gathered from the capture ring (flush).
+enum class Src { kFp16Rows, kRotated, kRing };
 
 struct WriteArgs {
     const uint16_t* x;        // fp16 rows [nvec][d] (Src::kFp16Rows)
@@ -30,6 +33,10 @@ struct WriteArgs {
     int hkv;
     int capacity;
     int batch;
+    // kRing: vector (t, h) with t = b * count + i is token first[b] + i of the ring
+    const int32_t* first;
+    int ring_cap;
+    int count;
 };
 
 // Index of the first fp32 boundary not below y, i.e. #{k : bounds[k] < y}.
@@ -76,7 +83,16 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
 
     // destination byte offset of this vector
     size_t off = 0;
-    if (active) {
+    size_t src_row = static_cast<size_t>(vec < a.nvec ? vec : 0);  // fp16 source row
+    if constexpr (SRC == Src::kRing) {
+        const int t = vec / a.hkv, h = vec % a.hkv;
+        const int bb = (vec < a.nvec ? t : 0) / a.count, i = t % a.count;
+        const int f = a.first[bb];
+        const int pos = f + i;
+        if (!active || f < 0 || pos >= a.capacity) active = false;
+        else off = ((static_cast<size_t>(bb) * a.hkv + h) * a.capacity + pos) * VB;
+        src_row = active ? (static_cast<size_t>(bb) * a.hkv + h) * a.ring_cap + pos % a.ring_cap : 0;
+    } else if (active) {
         if (a.dst_row) {
             const int t = vec / a.hkv, h = vec % a.hkv;
             const int r = a.dst_row[t];
@@ -94,8 +110,9 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
 
     float v[8];
     uint32_t n16 = 0;
-    if constexpr (SRC == Src::kFp16Rows) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(a.x + static_cast<size_t>(vsrc) * D + 8 * l);
+    if constexpr (SRC != Src::kRotated) {
+        const size_t row = SRC == Src::kRing ? src_row : static_cast<size_t>(vsrc);
+        const uint4 raw = *reinterpret_cast<const uint4*>(a.x + row * D + 8 * l);
         const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
@@ -142,7 +159,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
         return;
     } else {
         constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
-        if constexpr (SRC == Src::kFp16Rows) {
+        if constexpr (SRC != Src::kRotated) {
             float ss = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
@@ -236,13 +253,33 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, De
 
 // Keys and values of one append in one launch when they share a format: the
 // first kblocks workgroups take the keys, the rest the values.
-template <int FMT, int D>
+template <int FMT, int D, Src SRC>
 __global__ __launch_bounds__(kWriteThreads) void quantize_kv_kernel(WriteArgs ak, WriteArgs av, DevCodebook cbk,
                                                                     DevCodebook cbv, int kblocks) {
     if (static_cast<int>(blockIdx.x) < kblocks)
-        quantize_rows<FMT, D, Src::kFp16Rows>(ak, cbk, blockIdx.x);
+        quantize_rows<FMT, D, SRC>(ak, cbk, blockIdx.x);
     else
-        quantize_rows<FMT, D, Src::kFp16Rows>(av, cbv, blockIdx.x - kblocks);
+        quantize_rows<FMT, D, SRC>(av, cbv, blockIdx.x - kblocks);
+}
+
+// Capture ring append: row (b, h) of the new token goes to ring slot pos[b] % ring_cap.
+// One thread moves 16 bytes; a sequence with pos < 0 is skipped.
+__global__ __launch_bounds__(kWriteThreads) void ring_append_kernel(const uint4* __restrict__ k_new,
+                                                                    const uint4* __restrict__ v_new,
+                                                                    const int32_t* __restrict__ pos, uint4* k_ring,
+                                                                    uint4* v_ring, int batch, int hkv, int chunks,
+                                                                    int ring_cap) {
+    const int i = blockIdx.x * kWriteThreads + threadIdx.x;  // over 2 tensors x batch x hkv x chunks
+    const int per_tensor = batch * hkv * chunks;
+    if (i >= 2 * per_tensor) return;
+    const int tensor = i / per_tensor, j = i % per_tensor;
+    const int row = j / chunks, c = j % chunks;
+    const int b = row / hkv, h = row % hkv;
+    const int p = pos[b];
+    if (p < 0) return;
+    const size_t dst = ((static_cast<size_t>(b) * hkv + h) * ring_cap + p % ring_cap) * chunks + c;
+    if (tensor == 0) k_ring[dst] = k_new[j];
+    else v_ring[dst] = v_new[j];
 }
 
 // q_rot = Pi q = H (s * q) / sqrt(d); for TQ3K keys also q_sketch = S q.
@@ -305,15 +342,20 @@ int launch_quantize(const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
-template <int FMT, int D>
+template <int FMT, int D, Src SRC>
 int launch_quantize_kv(const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk, const tq_codebook& cbv,
                        hipStream_t st) {
     constexpr int VPB = kWriteThreads / (D / 8);
     const int kblocks = (ak.nvec + VPB - 1) / VPB;
-    hipLaunchKernelGGL((quantize_kv_kernel<FMT, D>), dim3(2 * kblocks), dim3(kWriteThreads), 0, st, ak, av, to_dev(cbk),
-                       to_dev(cbv), kblocks);
+    hipLaunchKernelGGL((quantize_kv_kernel<FMT, D, SRC>), dim3(2 * kblocks), dim3(kWriteThreads), 0, st, ak, av,
+                       to_dev(cbk), to_dev(cbv), kblocks);
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
+
+// Keys and values of one write: one launch when they share a format (PQ4, PQ3), else two.
+template <Src SRC>
+int quantize_pair(const tq_layout* L, const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk,
+                  const tq_codebook& cbv, hipStream_t stream);
 
 template <Src SRC>
 int dispatch_quantize(int fmt, int d, const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
@@ -326,13 +368,29 @@ int dispatch_quantize(int fmt, int d, const WriteArgs& a, const tq_codebook& cb,
         TQ_Q(TQ_FMT_TQ3K)
         default: break;
     }
-    if constexpr (SRC == Src::kFp16Rows) {
+    if constexpr (SRC != Src::kRotated) {
         if (fmt == TQ_FMT_GQ2V)
             return d == 128 ? launch_quantize<TQ_FMT_GQ2V, 128, SRC>(a, cb, st)
                             : launch_quantize<TQ_FMT_GQ2V, 256, SRC>(a, cb, st);
     }
 #undef TQ_Q
     return TQ_ERR_UNSUPPORTED;
+}
+
+template <Src SRC>
+int quantize_pair(const tq_layout* L, const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk,
+                  const tq_codebook& cbv, hipStream_t stream) {
+    if (L->k_format == L->v_format && (L->k_format == TQ_FMT_PQ4 || L->k_format == TQ_FMT_PQ3)) {
+        const bool d128 = L->head_dim == 128;
+        if (L->k_format == TQ_FMT_PQ4)
+            return d128 ? launch_quantize_kv<TQ_FMT_PQ4, 128, SRC>(ak, av, cbk, cbv, stream)
+                        : launch_quantize_kv<TQ_FMT_PQ4, 256, SRC>(ak, av, cbk, cbv, stream);
+        return d128 ? launch_quantize_kv<TQ_FMT_PQ3, 128, SRC>(ak, av, cbk, cbv, stream)
+                    : launch_quantize_kv<TQ_FMT_PQ3, 256, SRC>(ak, av, cbk, cbv, stream);
+    }
+    const int st = dispatch_quantize<SRC>(L->k_format, L->head_dim, ak, cbk, stream);
+    if (st != TQ_OK) return st;
+    return dispatch_quantize<SRC>(L->v_format, L->head_dim, av, cbv, stream);
 }
 
 }  // namespace
@@ -368,17 +426,63 @@ int tq_quantize_append(const tq_layout* L, const tq_codebook* cbk, const tq_code
     a.out = static_cast<uint8_t*>(k_cache);
     av.x = v_new;
     av.out = static_cast<uint8_t*>(v_cache);
-    // one launch for both tensors when they share the format (PQ4, PQ3)
-    if (L->k_format == L->v_format && (L->k_format == TQ_FMT_PQ4 || L->k_format == TQ_FMT_PQ3)) {
-        const bool d128 = L->head_dim == 128;
-        if (L->k_format == TQ_FMT_PQ4)
-            return d128 ? launch_quantize_kv<TQ_FMT_PQ4, 128>(a, av, *cbk, *cbv, stream)
-                        : launch_quantize_kv<TQ_FMT_PQ4, 256>(a, av, *cbk, *cbv, stream);
-        return d128 ? launch_quantize_kv<TQ_FMT_PQ3, 128>(a, av, *cbk, *cbv, stream)
-                    : launch_quantize_kv<TQ_FMT_PQ3, 256>(a, av, *cbk, *cbv, stream);
-    }
-    if ((st = dispatch_quantize<Src::kFp16Rows>(L->k_format, L->head_dim, a, *cbk, stream)) != TQ_OK) return st;
-    return dispatch_quantize<Src::kFp16Rows>(L->v_format, L->head_dim, av, *cbv, stream);
+    return quantize_pair<Src::kFp16Rows>(L, a, av, *cbk, *cbv, stream);
+}
+
+size_t tq_ring_bytes(const tq_layout* L, int ring_cap) {
+    using namespace tq;
+    if (check_layout(L) != TQ_OK || ring_cap < 1 || ring_cap > kRingCapMax) return 0;
+    return static_cast<size_t>(L->batch) * L->n_kv_heads * ring_cap * L->head_dim * sizeof(uint16_t);
+}
+
+int tq_ring_append(const tq_layout* L, int ring_cap, const uint16_t* k_new, const uint16_t* v_new, const int32_t* pos,
+                   void* k_ring, void* v_ring, hipStream_t stream) {
+    using namespace tq;
+    int st = check_layout(L);
+    if (st != TQ_OK) return st;
+    if (ring_cap < 1 || ring_cap > kRingCapMax) return TQ_ERR_INVALID;
+    if (!k_new || !v_new || !pos || !k_ring || !v_ring) return TQ_ERR_INVALID;
+    if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_ring, 16) || !aligned(v_ring, 16) || !aligned(pos, 4))
+        return TQ_ERR_INVALID;
+    const int chunks = L->head_dim / 8;  // 16-byte pieces of one fp16 row
+    const int total = 2 * L->batch * L->n_kv_heads * chunks;
+    hipLaunchKernelGGL(ring_append_kernel, dim3((total + kWriteThreads - 1) / kWriteThreads), dim3(kWriteThreads), 0,
+                       stream, static_cast<const uint4*>(static_cast<const void*>(k_new)),
+                       static_cast<const uint4*>(static_cast<const void*>(v_new)), pos, static_cast<uint4*>(k_ring),
+                       static_cast<uint4*>(v_ring), L->batch, L->n_kv_heads, chunks, ring_cap);
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+int tq_ring_flush(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* S_dev, int ring_cap,
+                  const void* k_ring, const void* v_ring, const int32_t* first, int count, void* k_cache,
+                  void* v_cache, hipStream_t stream) {
+    using namespace tq;
+    int st = check_layout(L);
+    if (st != TQ_OK) return st;
+    if ((st = check_codebook(cbk, L->k_format, L->head_dim)) != TQ_OK) return st;
+    if ((st = check_codebook(cbv, L->v_format, L->head_dim)) != TQ_OK) return st;
+    if (ring_cap < 1 || ring_cap > kRingCapMax || count < 0 || count > ring_cap) return TQ_ERR_INVALID;
+    if (count == 0) return TQ_OK;
+    if (!k_ring || !v_ring || !first || !k_cache || !v_cache) return TQ_ERR_INVALID;
+    if (!aligned(k_ring, 16) || !aligned(v_ring, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(first, 4))
+        return TQ_ERR_INVALID;
+    if (L->k_format == TQ_FMT_TQ3K && (!S_dev || !aligned(S_dev, 16))) return TQ_ERR_INVALID;
+    WriteArgs a{};
+    a.S = S_dev;
+    a.nvec = L->batch * count * L->n_kv_heads;
+    a.hkv = L->n_kv_heads;
+    a.capacity = L->capacity;
+    a.batch = L->batch;
+    a.first = first;
+    a.ring_cap = ring_cap;
+    a.count = count;
+    WriteArgs av = a;
+    a.x = static_cast<const uint16_t*>(k_ring);
+    a.out = static_cast<uint8_t*>(k_cache);
+    av.x = static_cast<const uint16_t*>(v_ring);
+    av.out = static_cast<uint8_t*>(v_cache);
+    return quantize_pair<Src::kRing>(L, a, av, *cbk, *cbv, stream);
 }
 
 int tq_quantize_rotated(int format, const tq_codebook* cb, const float* S_dev, const float* y, const uint16_t* norm16,

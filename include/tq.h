@@ -267,6 +267,63 @@ int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq
 int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_tokens, const void* ws,
                       size_t ws_bytes, float* out, hipStream_t stream);
 
+/* ---- Capture ring and hybrid attention --------------------------------
+ * [P2] "write path": the capture step keeps the newest tokens exact in a
+ * ring buffer and quantizes the oldest batch into compressed blocks only
+ * when the ring is full, so no per-token quantization runs on the decode
+ * path; [P2] "limits" names the hybrid mode, which attends over the exact
+ * recent tokens and the compressed history together.
+ *
+ * Ring: fp16 k_ring[B][Hkv][ring_cap][d] and v_ring alike, caller-owned
+ * (tq_ring_bytes each), 16-byte aligned.  The token at absolute position pos
+ * of sequence b lives in slot pos % ring_cap.  1 <= ring_cap <=
+ * TQ_RING_CAP_MAX.  The caller keeps, per sequence, comp_len (tokens
+ * 0 .. comp_len-1 are in the compressed cache) and ring_len (tokens
+ * comp_len .. comp_len+ring_len-1 are in the ring).                        */
+#define TQ_RING_CAP_MAX 256
+
+/* Bytes of one ring tensor; 0 for an invalid layout or capacity.           */
+size_t tq_ring_bytes(const tq_layout* L, int ring_cap);
+
+/* Copy one new fp16 K and V row per (sequence, KV head), k_new/v_new
+ * [B][Hkv][d], into ring slot pos[b] % ring_cap (pos: device int32 [B], the
+ * token's absolute position; pos < 0 skips the sequence).  No
+ * quantization.  Errors: TQ_ERR_INVALID (null or misaligned pointer, bad
+ * ring_cap), TQ_ERR_HIP.                                                  */
+int tq_ring_append(const tq_layout* L, int ring_cap, const uint16_t* k_new, const uint16_t* v_new,
+                   const int32_t* pos, void* k_ring, void* v_ring, hipStream_t stream);
+
+/* Flush: quantize ring tokens first[b] .. first[b]+count-1 of every
+ * sequence (first: device int32 [B]; normally the oldest count tokens) and
+ * write their blocks at those positions of the compressed caches, exactly
+ * as tq_quantize_append would.  A sequence with first < 0, and positions
+ * at or past capacity, are skipped.  0 <= count <= ring_cap; count = 0
+ * enqueues nothing.  Errors: as tq_quantize_append, TQ_ERR_INVALID for a
+ * bad ring_cap or count.                                                   */
+int tq_ring_flush(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* S_dev,
+                  int ring_cap, const void* k_ring, const void* v_ring, const int32_t* first, int count,
+                  void* k_cache, void* v_cache, hipStream_t stream);
+
+/* Workspace of tq_decode_attention_hybrid: the split records plus one ring
+ * record per (b, query head).                                              */
+size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens);
+
+/* Hybrid decode: softmax attention of every query over the compressed
+ * tokens 0 .. comp_lens[b]-1 and the exact ring tokens comp_lens[b] ..
+ * comp_lens[b]+ring_lens[b]-1 together (comp_lens, ring_lens: device int32
+ * [B]; ring_lens is clamped to [0, ring_cap]).  The compressed part runs
+ * the split-K decode; the ring part scores exact fp16 keys against the
+ * unrotated query (Pi^T q_rot) and sums exact fp16 values, then adds one
+ * record per (b, query head) that the combine merges with the splits.  Both
+ * empty: out = 0.  ws: tq_decode_hybrid_workspace_bytes.  Errors: as
+ * tq_decode_attention, TQ_ERR_INVALID for a bad ring argument.              */
+int tq_decode_attention_hybrid(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
+                               const float* q_rot, const float* q_sketch, const void* k_cache,
+                               const void* v_cache, const int32_t* comp_lens, int ring_cap,
+                               const void* k_ring, const void* v_ring, const int32_t* ring_lens,
+                               float* out, int split_tokens, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

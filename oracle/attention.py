@@ -11,6 +11,9 @@ of dequantized values.
 
 Grouped-query attention: query head g reads KV head g // (Hq / Hkv).
 
+``hybrid_attention`` is the same softmax over the compressed history and the
+exact tokens of the capture ring taken together.
+
 Besides the plain path, two helpers restate the identities the fast path
 relies on, so that tests can pin them:
 
@@ -36,6 +39,18 @@ def softmax_attention(q, khat, vhat):
     p = np.exp(s - s.max())
     p /= p.sum()
     return p @ vhat, s
+
+
+def hybrid_attention(q, khat, vhat, k_exact, v_exact):
+    """Hybrid read of one query: the compressed history (dequantized khat,
+    vhat) and the exact recent tokens of the capture ring (k_exact, v_exact,
+    their stored fp16 values as they are) form one key set ("TurboQuant Triton
+    deep dive": the write path keeps the newest tokens exact in a ring buffer;
+    the hybrid mode in its limits section reads both).  Returns (o, logits)."""
+    d = np.asarray(q).shape[-1]
+    k = np.concatenate([np.asarray(khat, np.float64).reshape(-1, d), np.asarray(k_exact, np.float64).reshape(-1, d)])
+    v = np.concatenate([np.asarray(vhat, np.float64).reshape(-1, d), np.asarray(v_exact, np.float64).reshape(-1, d)])
+    return softmax_attention(q, k, v)
 
 
 def decode_attention(q, kv_k, kv_v, seq_lens, G):

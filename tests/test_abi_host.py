@@ -136,3 +136,30 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
                                           need - 1, None, fake, fake) == -3
     assert tq.lib.tq_quantize_rotated(9, r(cb), None, fake, fake, 1, fake, None) == -2
     assert tq.strerror(-3).startswith("workspace")
+
+
+def test_ring_calls_check_their_arguments_before_any_launch():
+    L = tq.Layout(2, 8, 2, 128, 256, tq.FMT_PQ4, tq.FMT_PQ4)
+    cb, _ = tq.build_codebook(128, 4, 0, 1, 2)
+    r = ctypes.byref
+    fake = ctypes.c_void_p(1 << 20)
+    assert tq.ring_bytes(L, 128) == 2 * 2 * 128 * 128 * 2
+    assert tq.ring_bytes(L, 0) == 0 and tq.ring_bytes(L, tq.RING_CAP_MAX + 1) == 0
+    assert tq.lib.tq_ring_append(r(L), 0, fake, fake, fake, fake, fake, None) == -1
+    assert tq.lib.tq_ring_append(r(L), 64, None, fake, fake, fake, fake, None) == -1
+    assert tq.lib.tq_ring_append(r(L), 64, fake, fake, fake, ctypes.c_void_p((1 << 20) + 8), fake, None) == -1
+    assert tq.lib.tq_ring_flush(r(L), r(cb), r(cb), None, 64, fake, fake, fake, 65, fake, fake, None) == -1
+    assert tq.lib.tq_ring_flush(r(L), r(cb), r(cb), None, 64, fake, fake, fake, -1, fake, fake, None) == -1
+    assert tq.lib.tq_ring_flush(r(L), r(cb), r(cb), None, 64, None, None, None, 0, None, None, None) == 0
+    need = tq.decode_hybrid_workspace_bytes(L)
+    assert need == tq.decode_workspace_bytes(L) + 2 * 8 * (8 + 4 * 128)  # one more record per (b, query head)
+    args = [r(L), r(cb), r(cb), fake, None, fake, fake, fake]
+    assert tq.lib.tq_decode_attention_hybrid(*args, 0, fake, fake, fake, fake, 0, fake, need, None) == -1
+    assert tq.lib.tq_decode_attention_hybrid(*args, 64, None, fake, fake, fake, 0, fake, need, None) == -1
+    assert tq.lib.tq_decode_attention_hybrid(*args, 64, fake, fake, fake, fake, 0, fake, need - 1, None) == -3
+
+
+def test_ring_capacity_limit_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define TQ_RING_CAP_MAX (\d+)", text)
+    assert m and int(m.group(1)) == tq.RING_CAP_MAX
