@@ -1363,6 +1363,7 @@ __global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const f
 constexpr int kRingThreads = 256;
 static_assert(kRingCapMax <= kRingThreads, "one thread per ring token");
 constexpr int kRingMax = kRingCapMax;  // one thread per ring token
+constexpr int kRingChunk = 32;         // value rows staged in LDS at a time
 
 struct RingArgs {
     const float* q_rot;
@@ -1412,6 +1413,7 @@ __global__ __launch_bounds__(kRingThreads) void ring_partial_kernel(RingArgs r, 
     __shared__ float pw[G][kRingMax];     // 2^(s - m) per head and ring token
     __shared__ float accs[G][D];          // value sums in the unrotated basis
     __shared__ float red_m[NW][G], red_l[NW][G];
+    __shared__ uint4 vst[kRingChunk][D / 8];  // a chunk of value rows
 
     const int h = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1473,15 +1475,35 @@ __global__ __launch_bounds__(kRingThreads) void ring_partial_kernel(RingArgs r, 
     }
     __syncthreads();
 
-    // value sums acc[g][j] = sum_t p[g][t] v_t[j], exact fp16 values
-    for (int idx = tid; idx < G * D; idx += kRingThreads) {
-        const int g = idx / D, j = idx % D;
-        float a = 0.0f;
-        for (int t = 0; t < n; ++t) {
-            const int slot = (first + t) % r.ring_cap;
-            a = fmaf(pw[g][t], half_bits_to_float(r.v_ring[(row0 + slot) * D + j]), a);
+    // value sums acc[g][j] = sum_t p[g][t] v_t[j] over exact fp16 values: chunks of kRingChunk
+    // rows are staged in LDS with 16-byte loads, then every thread sums its (g, j) pairs
+    constexpr int NP = (G * D + kRingThreads - 1) / kRingThreads;  // (g, j) pairs per thread
+    float a[NP];
+#pragma unroll
+    for (int k = 0; k < NP; ++k) a[k] = 0.0f;
+    for (int t0 = 0; t0 < n; t0 += kRingChunk) {
+        const int nc = min(kRingChunk, n - t0);
+        for (int c = tid; c < nc * (D / 8); c += kRingThreads) {
+            const int t = c / (D / 8), part = c % (D / 8);
+            const int slot = (first + t0 + t) % r.ring_cap;
+            vst[t][part] = reinterpret_cast<const uint4*>(r.v_ring + (row0 + slot) * D)[part];
         }
-        accs[g][j] = a;
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int idx = tid + k * kRingThreads;
+            if (idx < G * D) {
+                const int g = idx / D, j = idx % D;
+                const uint16_t* vs = reinterpret_cast<const uint16_t*>(&vst[0][0]);
+                for (int t = 0; t < nc; ++t) a[k] = fmaf(pw[g][t0 + t], half_bits_to_float(vs[t * D + j]), a[k]);
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+        const int idx = tid + k * kRingThreads;
+        if (idx < G * D) accs[idx / D][idx % D] = a[k];
     }
     __syncthreads();
 
