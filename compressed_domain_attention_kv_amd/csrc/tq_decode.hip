@@ -53,7 +53,6 @@ struct DecodeArgs {
     int capacity;
     int splits;
     int split_len;
-    int rec_stride;  // records per (b, query head) row of the workspace (splits, or more for hybrid)
 };
 
 // Lane exchange inside a row of 16 lanes through DPP (no LDS traffic).
@@ -124,11 +123,11 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
     N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
     const int start = s * a.split_len;
     const int end = min(start + a.split_len, N);
-    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.rec_stride + s;  // record of query head hq0
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;  // record of query head hq0
 
     if (start >= end) {  // empty split: (m, l, acc) = (-inf, 0, 0)
         for (int g = 0; g < G; ++g) {
-            const size_t rec = rec0 + static_cast<size_t>(g) * a.rec_stride;
+            const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
             if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
             for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
         }
@@ -364,7 +363,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
             L = fmaf(r[1], f, L);
             A = fmaf(r[2 + j], f, A);
         }
-        const size_t rec = rec0 + static_cast<size_t>(g) * a.rec_stride;
+        const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
         a.acc[rec * D + j] = A;
         if (j == 0) a.ml[rec] = make_float2(M, L);
     }
@@ -587,11 +586,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
     const int start = s * a.split_len;
     const int end = min(start + a.split_len, N);
-    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.rec_stride + s;
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
 
     if (start >= end) {
         for (int gg = 0; gg < G; ++gg) {
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.rec_stride;
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
             if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
             for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
         }
@@ -863,7 +862,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             L = fmaf(r[1], f, L);
             A = fmaf(r[2 + j], f, A);
         }
-        const size_t rec = rec0 + static_cast<size_t>(gg) * a.rec_stride;
+        const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
         a.acc[rec * D + j] = A;
         if (j == 0) a.ml[rec] = make_float2(M, L);
     }
@@ -1238,7 +1237,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     }
     __syncthreads();
     if (s < a.splits) {
-        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.rec_stride + s;
+        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
         for (int idx = tid % (kWaves * 64); idx < G * D; idx += kWaves * 64) {
             const int gg = idx / D, j = idx % D;
             float M = -INFINITY;
@@ -1252,133 +1251,12 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 L = fmaf(r[1], f, L);
                 A = fmaf(r[2 + j], f, A);
             }
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.rec_stride;
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
             a.acc[rec * D + j] = A;
             if (j == 0) a.ml[rec] = make_float2(M, L);
         }
     }
 }
-
-// One workgroup per (b, query head): merge the split records, normalize and,
-// for rotated value formats, rotate back once.  Each thread owns four
-// coordinates of one split group, so the record rows stream in with 16-byte
-// loads from many splits at once.
-constexpr int kCombineThreads = 256;
-
-template <int D, bool ROTATED>
-__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(const float2* __restrict__ ml,
-                                                                        const float* __restrict__ acc,
-                                                                        float* __restrict__ out, int splits,
-                                                                        DevCodebook cbv) {
-    constexpr int TPR = D / 4;                    // threads per record row
-    constexpr int NGS = kCombineThreads / TPR;    // split groups
-    constexpr int DPL = D / 64;
-    __shared__ float wave_m[kCombineThreads / 64];
-    __shared__ float4 part[NGS][TPR];
-    __shared__ float part_l[NGS];
-    __shared__ float o_sh[D];
-    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
-    const float2* mr = ml + static_cast<size_t>(row) * splits;
-    float M = -INFINITY;
-    for (int s = tid; s < splits; s += kCombineThreads) M = fmaxf(M, mr[s].x);
-    M = wave_max(M);
-    if (lane == 0) wave_m[tid >> 6] = M;
-    __syncthreads();
-    M = fmaxf(fmaxf(wave_m[0], wave_m[1]), fmaxf(wave_m[2], wave_m[3]));
-    const int grp = tid / TPR, c = tid % TPR;
-    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    float L = 0.0f;
-    if (M != -INFINITY) {
-        const float4* ar = reinterpret_cast<const float4*>(acc) + static_cast<size_t>(row) * splits * TPR + c;
-#pragma unroll 4
-        for (int s = grp; s < splits; s += NGS) {
-            const float2 r = mr[s];
-            const float f = r.x == -INFINITY ? 0.0f : exp2f(r.x - M);
-            const float4 v = ar[static_cast<size_t>(s) * TPR];
-            L = fmaf(r.y, f, L);
-            o.x = fmaf(v.x, f, o.x); o.y = fmaf(v.y, f, o.y); o.z = fmaf(v.z, f, o.z); o.w = fmaf(v.w, f, o.w);
-        }
-    }
-    part[grp][c] = o;
-    if (c == 0) part_l[grp] = L;
-    __syncthreads();
-    if (tid < TPR) {
-        float4 t = part[0][tid];
-        float Lt = part_l[0];
-#pragma unroll
-        for (int g = 1; g < NGS; ++g) {
-            const float4 u = part[g][tid];
-            t.x += u.x; t.y += u.y; t.z += u.z; t.w += u.w;
-            Lt += part_l[g];
-        }
-        const float inv = Lt > 0.0f ? 1.0f / Lt : 0.0f;
-        o_sh[4 * tid] = t.x * inv;
-        o_sh[4 * tid + 1] = t.y * inv;
-        o_sh[4 * tid + 2] = t.z * inv;
-        o_sh[4 * tid + 3] = t.w * inv;
-    }
-    __syncthreads();
-    if (tid >= 64) return;
-    float v[DPL];
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) v[k] = o_sh[DPL * lane + k];
-    if constexpr (ROTATED) {
-        // o <- Pi^T o = diag(s) H o / sqrt(d); element j = DPL*lane + k
-#pragma unroll
-        for (int st = 1; st < DPL; st <<= 1)
-#pragma unroll
-            for (int k = 0; k < DPL; ++k)
-                if ((k & st) == 0) {
-                    const float x = v[k], y = v[k + st];
-                    v[k] = x + y;
-                    v[k + st] = x - y;
-                }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const bool upper = (lane & m) != 0;
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) {
-                const float p = __shfl_xor(v[k], m, 64);
-                v[k] = upper ? (p - v[k]) : (v[k] + p);
-            }
-        }
-        constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) v[k] *= kInvSqrtD * rotation_sign(cbv, DPL * lane + k);
-    }
-#pragma unroll
-    for (int k = 0; k < DPL; ++k) out[static_cast<size_t>(row) * D + DPL * lane + k] = v[k];
-}
-
-// ---------------------------------------------------------------------------
-// Ring part of hybrid attention.  The capture ring keeps the newest tokens of
-// every stream exact (fp16) and the hybrid read attends over them and over
-// the compressed blocks together ([P2] "write path": recent tokens stay exact
-// in a ring buffer until a batch is flushed into compressed blocks; the hybrid
-// mode reads both).  One workgroup per (batch row, KV head) turns the ring's n
-// tokens into one more split record for each of its G query heads, in the
-// units of the compressed records (scores and m in log2 units, acc in the
-// rotated basis for rotated value formats), so decode_combine merges it
-// unchanged.
-constexpr int kRingThreads = 256;
-static_assert(kRingCapMax <= kRingThreads, "one thread per ring token");
-constexpr int kRingMax = kRingCapMax;  // one thread per ring token
-constexpr int kRingChunk = 32;         // value rows staged in LDS at a time
-
-struct RingArgs {
-    const float* q_rot;
-    const uint16_t* k_ring;
-    const uint16_t* v_ring;
-    const int32_t* comp_lens;
-    const int32_t* ring_lens;
-    float2* ml;
-    float* acc;
-    int hq;
-    int hkv;
-    int ring_cap;
-    int rec_stride;
-    int ring_rec;  // record index of the ring within its row
-};
 
 // Unnormalized Sylvester Walsh-Hadamard transform of a vector spread over one
 // wavefront: element j = DPL * lane + k sits in v[k].
@@ -1404,130 +1282,297 @@ __device__ __forceinline__ void wht_wave(float (&v)[DPL], int lane) {
     }
 }
 
-template <int D, int G, bool ROT>
-__global__ __launch_bounds__(kRingThreads) void ring_partial_kernel(RingArgs r, DevCodebook cbk, DevCodebook cbv) {
+// ---------------------------------------------------------------------------
+// Merge of the split records, and the ring part of hybrid attention.
+//
+// One workgroup per (b, query head) row merges the row's split records,
+// normalizes and, for rotated value formats, rotates back once.  Each thread
+// owns four coordinates of one split group and merges its records with a
+// running maximum of its own, so every record load is issued before any
+// maximum is known.
+//
+// With a capture ring (RMAX > 0) the same workgroup also attends over the
+// ring's exact fp16 tokens ([P2] "write path": the newest tokens stay exact in
+// a ring buffer until a batch is flushed into compressed blocks, and the
+// hybrid mode reads both): exact scores against q = Pi_k^T q_rot in the log2
+// units of the records, a softmax over the ring, and value sums in the
+// unrotated basis, which join the merge after the rotation back (the rotation
+// is linear).  The ring's rows are staged in LDS: key rows with their 16-byte
+// pieces swizzled by the token (piece c of token t at c ^ (t & 15)), so that
+// the one or two threads of a token read them free of bank conflicts; value
+// rows in plain order.  When both do not fit (d = 256 with 256 ring tokens)
+// the value rows are loaded after the scores, into the key buffer.
+constexpr int kCombineThreads = 256;
+static_assert(kRingCapMax <= kCombineThreads, "one or two threads per ring token");
+
+struct CombineArgs {
+    const float2* ml;
+    const float* acc;
+    float* out;
+    int splits;  // records per row
+    // capture ring, hybrid read only
+    const float* q_rot;
+    const uint16_t* k_ring;
+    const uint16_t* v_ring;
+    const int32_t* comp_lens;
+    const int32_t* ring_lens;
+    int hq;
+    int hkv;
+    int ring_cap;
+};
+
+template <int D, int RMAX>
+struct RingStage {
+    static constexpr int KPT = D / 8;                        // 16-byte pieces per row
+    static constexpr int PPT = RMAX * KPT / kCombineThreads;  // pieces per thread
+    static constexpr bool VLATE = 2 * RMAX * KPT * 16 > 128 * 1024;
+    static constexpr int TPT = RMAX > 0 ? kCombineThreads / RMAX : 1;  // threads per ring token
+    static_assert(RMAX == 0 || (RMAX * KPT) % kCombineThreads == 0, "whole pieces per thread");
+    static_assert(RMAX == 0 || (TPT * RMAX == kCombineThreads && KPT % TPT == 0), "ring split over threads");
+};
+
+// 16-byte piece e of a ring's rows (key or value) in token order; tokens past n
+// read the newest row (the oldest when the ring is empty), which keeps every
+// load inside the ring.
+template <int D>
+__device__ __forceinline__ uint4 load_ring_piece(const uint16_t* ring, int ring_cap, size_t row0, int first, int nl,
+                                                 int e) {
+    const int t = min(e / (D / 8), nl);
+    const int slot = (first + t) % ring_cap;
+    return reinterpret_cast<const uint4*>(ring + (row0 + slot) * D)[e % (D / 8)];
+}
+
+template <int D, bool ROTATED, int RMAX>
+__global__ __launch_bounds__(kCombineThreads) void decode_combine_kernel(CombineArgs a, DevCodebook cbk,
+                                                                        DevCodebook cbv) {
+    constexpr int TPR = D / 4;                    // threads per record row
+    constexpr int NGS = kCombineThreads / TPR;    // split groups
     constexpr int DPL = D / 64;
-    constexpr int NW = kRingThreads / 64;
+    constexpr int NW = kCombineThreads / 64;
     constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
-    __shared__ float qs[G][D];            // unrotated query times log2(e)/sqrt(d)
-    __shared__ float pw[G][kRingMax];     // 2^(s - m) per head and ring token
-    __shared__ float accs[G][D];          // value sums in the unrotated basis
-    __shared__ float red_m[NW][G], red_l[NW][G];
-    __shared__ uint4 vst[kRingChunk][D / 8];  // a chunk of value rows
+    using S = RingStage<D, RMAX>;
+    constexpr int KPT = S::KPT, PPT = S::PPT, TPT = S::TPT;
+    constexpr bool RING = RMAX > 0, VLATE = S::VLATE;
+    constexpr int NTG = kCombineThreads / (D / 2);  // token groups of the ring's value sums
+    constexpr int KR = RING ? RMAX : 1, KC = RING ? KPT : 1;
+    __shared__ float4 part[NGS][TPR];
+    __shared__ float part_m[NGS], part_l[NGS];
+    __shared__ float fin_ml[2];
+    __shared__ float o_sh[D];
+    __shared__ float qs[RING ? D : 1];               // q = Pi_k^T q_rot times log2(e)/sqrt(d)
+    __shared__ float pw[KR];                         // 2^(s - m) per ring token
+    __shared__ float red_m[NW], red_l[NW];
+    __shared__ float accp[RING ? NTG : 1][RING ? D : 1];  // ring value sums per token group
+    __shared__ uint4 kst[KR][KC];                    // ring key rows, swizzled
+    __shared__ uint4 vst_own[RING && !VLATE ? RMAX : 1][KC];
+    uint4(*vst)[KC] = VLATE ? kst : vst_own;
 
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int hq0 = h * G;
-    int n = r.ring_lens[b];
-    n = n < 0 ? 0 : (n > r.ring_cap ? r.ring_cap : n);
-    const int first = max(r.comp_lens[b], 0);  // absolute position of the oldest ring token
-    const size_t row0 = (static_cast<size_t>(b) * r.hkv + h) * r.ring_cap;
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // q = Pi_k^T q_rot = diag(s_k) H q_rot / sqrt(d), one wavefront per head
-    for (int g = w; g < G; g += NW) {
-        const float* src = r.q_rot + (static_cast<size_t>(b) * r.hq + hq0 + g) * D;
-        float v[DPL];
+    // ---- ring loads first: they are in flight while the records merge
+    int n = 0, nl = 0, first = 0;
+    size_t row0 = 0;
+    float qv[DPL];
+    uint4 kraw[RING ? PPT : 1], vraw[RING && !VLATE ? PPT : 1];
+    if constexpr (RING) {
+        const int b = row / a.hq, h = (row % a.hq) / (a.hq / a.hkv);
+        n = a.ring_lens[b];
+        n = n < 0 ? 0 : (n > a.ring_cap ? a.ring_cap : n);
+        nl = max(n - 1, 0);
+        first = max(a.comp_lens[b], 0);  // absolute position of the oldest ring token
+        row0 = (static_cast<size_t>(b) * a.hkv + h) * a.ring_cap;
 #pragma unroll
-        for (int k = 0; k < DPL; ++k) v[k] = src[DPL * lane + k];
+        for (int k = 0; k < DPL; ++k) qv[k] = a.q_rot[static_cast<size_t>(row) * D + DPL * lane + k];
+#pragma unroll
+        for (int i = 0; i < PPT; ++i)
+            kraw[i] = load_ring_piece<D>(a.k_ring, a.ring_cap, row0, first, nl, i * kCombineThreads + tid);
+        if constexpr (!VLATE) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                vraw[i] = load_ring_piece<D>(a.v_ring, a.ring_cap, row0, first, nl, i * kCombineThreads + tid);
+        }
+    }
+
+    // ---- split records: running maximum per thread, batches of SPT records whose
+    // loads are all issued first (indexes past the last record reread it, weight 0)
+    constexpr int SPT = 4;
+    const int grp = tid / TPR, c = tid % TPR;
+    const float2* mr = a.ml + static_cast<size_t>(row) * a.splits;
+    const float4* ar = reinterpret_cast<const float4*>(a.acc) + static_cast<size_t>(row) * a.splits * TPR + c;
+    float Mt = -INFINITY, Lt = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s0 = grp; s0 < a.splits; s0 += SPT * NGS) {
+        float2 r[SPT];
+        float4 v[SPT];
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const int s = min(s0 + u * NGS, a.splits - 1);
+            r[u] = mr[s];
+            v[u] = ar[static_cast<size_t>(s) * TPR];
+        }
+        float mb = Mt;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            if (s0 + u * NGS >= a.splits) r[u].x = -INFINITY;  // empty splits and the reread weigh nothing
+            mb = fmaxf(mb, r[u].x);
+        }
+        // selects, not branches, keep the value loads ahead of the maxima
+        const bool none = mb == -INFINITY;
+        const float so = none ? 1.0f : exp2f(Mt - mb);  // 0 while nothing has been merged
+        Lt *= so;
+        o.x *= so; o.y *= so; o.z *= so; o.w *= so;
+#pragma unroll
+        for (int u = 0; u < SPT; ++u) {
+            const float f = r[u].x == -INFINITY ? 0.0f : exp2f(r[u].x - mb);
+            Lt = fmaf(r[u].y, f, Lt);
+            o.x = fmaf(v[u].x, f, o.x); o.y = fmaf(v[u].y, f, o.y);
+            o.z = fmaf(v[u].z, f, o.z); o.w = fmaf(v[u].w, f, o.w);
+        }
+        Mt = mb;
+    }
+    part[grp][c] = o;
+    if (c == 0) {
+        part_m[grp] = Mt;
+        part_l[grp] = Lt;
+    }
+
+    float Mr = -INFINITY, Lr = 0.0f;
+    if constexpr (RING) {
+        if (w == 0) {
+            wht_wave<DPL>(qv, lane);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k)
+                qs[DPL * lane + k] = qv[k] * kInvSqrtD * rotation_sign(cbk, DPL * lane + k) * (kLog2e * kInvSqrtD);
+        }
+#pragma unroll
+        for (int i = 0; i < PPT; ++i) {
+            const int e = i * kCombineThreads + tid, t = e / KPT, cc = e % KPT;
+            kst[t][cc ^ (t & 15)] = kraw[i];
+        }
+        if constexpr (!VLATE) {
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int e = i * kCombineThreads + tid;
+                vst[e / KPT][e % KPT] = vraw[i];
+            }
+        }
+    }
+    __syncthreads();
+
+    if constexpr (RING) {
+        // exact scores: TPT adjacent lanes per token, each over KPT / TPT pieces
+        const int t = tid / TPT, hf = tid % TPT;
+        float sc = 0.0f;
+#pragma unroll 4
+        for (int i = 0; i < KPT / TPT; ++i) {
+            const int cc = hf * (KPT / TPT) + i;
+            const uint4 kp = kst[t][cc ^ (t & 15)];
+            const uint32_t wd[4] = {kp.x, kp.y, kp.z, kp.w};
+            const float4 q0 = *reinterpret_cast<const float4*>(&qs[8 * cc]);
+            const float4 q1 = *reinterpret_cast<const float4*>(&qs[8 * cc + 4]);
+            const float qq[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sc = fmaf(qq[e], half_bits_to_float((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu), sc);
+        }
+        if constexpr (TPT == 2) sc += __shfl_xor(sc, 1, 64);
+        const bool live = t < n;
+        const float mw = wave_max(live ? sc : -INFINITY);
+        if (lane == 0) red_m[w] = mw;
+        __syncthreads();
+        Mr = red_m[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) Mr = fmaxf(Mr, red_m[i]);
+        const float p = live ? exp2f(sc - Mr) : 0.0f;
+        if (hf == 0) pw[t] = p;
+        const float lw = wave_sum(hf == 0 ? p : 0.0f);
+        if (lane == 0) red_l[w] = lw;
+        if constexpr (VLATE) {  // the key rows have been read: the value rows take their place
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                kraw[i] = load_ring_piece<D>(a.v_ring, a.ring_cap, row0, first, nl, i * kCombineThreads + tid);
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                const int e = i * kCombineThreads + tid;
+                vst[e / KPT][e % KPT] = kraw[i];
+            }
+        }
+        __syncthreads();
+        Lr = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) Lr += red_l[i];
+
+        // value sums over the exact fp16 rows: coordinate pair jp, tokens tg, tg + NTG, ...
+        const int jp = tid % (D / 2), tg = tid / (D / 2);
+        const uint32_t* vs = reinterpret_cast<const uint32_t*>(&vst[0][0]);
+        float2 av = make_float2(0.0f, 0.0f);
+#pragma unroll 4
+        for (int tt = tg; tt < n; tt += NTG) {
+            const float pp = pw[tt];
+            const uint32_t v2 = vs[tt * (D / 2) + jp];
+            av.x = fmaf(pp, half_bits_to_float(v2 & 0xFFFFu), av.x);
+            av.y = fmaf(pp, half_bits_to_float(v2 >> 16), av.y);
+        }
+        accp[tg][2 * jp] = av.x;
+        accp[tg][2 * jp + 1] = av.y;
+    }
+
+    // ---- merge of the split groups (in the records' basis)
+    if (tid < TPR) {
+        float M = part_m[0];
+#pragma unroll
+        for (int g = 1; g < NGS; ++g) M = fmaxf(M, part_m[g]);
+        float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float L = 0.0f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int g = 0; g < NGS; ++g) {
+                const float f = exp2f(part_m[g] - M);
+                const float4 u = part[g][tid];
+                t.x = fmaf(u.x, f, t.x); t.y = fmaf(u.y, f, t.y);
+                t.z = fmaf(u.z, f, t.z); t.w = fmaf(u.w, f, t.w);
+                L = fmaf(part_l[g], f, L);
+            }
+        }
+        o_sh[4 * tid] = t.x;
+        o_sh[4 * tid + 1] = t.y;
+        o_sh[4 * tid + 2] = t.z;
+        o_sh[4 * tid + 3] = t.w;
+        if (tid == 0) {
+            fin_ml[0] = M;
+            fin_ml[1] = L;
+        }
+    }
+    __syncthreads();
+    if (tid >= 64) return;
+    float v[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) v[k] = o_sh[DPL * lane + k];
+    if constexpr (ROTATED) {  // o <- Pi^T o = diag(s) H o / sqrt(d)
         wht_wave<DPL>(v, lane);
 #pragma unroll
-        for (int k = 0; k < DPL; ++k)
-            qs[g][DPL * lane + k] = v[k] * kInvSqrtD * rotation_sign(cbk, DPL * lane + k) * (kLog2e * kInvSqrtD);
+        for (int k = 0; k < DPL; ++k) v[k] *= kInvSqrtD * rotation_sign(cbv, DPL * lane + k);
     }
-    __syncthreads();
-
-    // exact scores, one thread per ring token
-    float sc[G];
+    const float Mc = fin_ml[0], Lc = fin_ml[1];
+    float wc = 1.0f, wr = 0.0f, L = Lc;
+    if constexpr (RING) {
+        const float M = fmaxf(Mc, Mr);
+        wc = Mc == -INFINITY ? 0.0f : exp2f(Mc - M);
+        wr = Mr == -INFINITY ? 0.0f : exp2f(Mr - M);
+        L = Lc * wc + Lr * wr;
+    }
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
-    for (int g = 0; g < G; ++g) sc[g] = -INFINITY;
-    if (tid < n) {
-        const int slot = (first + tid) % r.ring_cap;
-        const uint4* kr = reinterpret_cast<const uint4*>(r.k_ring + (row0 + slot) * D);
+    for (int k = 0; k < DPL; ++k) {
+        float x = v[k] * wc;
+        if constexpr (RING) {
+            float r = 0.0f;
 #pragma unroll
-        for (int g = 0; g < G; ++g) sc[g] = 0.0f;
-        for (int c = 0; c < D / 8; ++c) {
-            const uint4 raw = kr[c];
-            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float kv = half_bits_to_float((wd[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-#pragma unroll
-                for (int g = 0; g < G; ++g) sc[g] = fmaf(qs[g][8 * c + e], kv, sc[g]);
-            }
+            for (int g = 0; g < NTG; ++g) r += accp[g][DPL * lane + k];
+            x = fmaf(r, wr, x);
         }
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const float mw = wave_max(sc[g]);
-        if (lane == 0) red_m[w][g] = mw;
-    }
-    __syncthreads();
-    float M[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        M[g] = red_m[0][g];
-#pragma unroll
-        for (int i = 1; i < NW; ++i) M[g] = fmaxf(M[g], red_m[i][g]);
-        const float p = tid < n ? exp2f(sc[g] - M[g]) : 0.0f;
-        pw[g][tid] = p;
-        const float lw = wave_sum(p);
-        if (lane == 0) red_l[w][g] = lw;
-    }
-    __syncthreads();
-
-    // value sums acc[g][j] = sum_t p[g][t] v_t[j] over exact fp16 values: chunks of kRingChunk
-    // rows are staged in LDS with 16-byte loads, then every thread sums its (g, j) pairs
-    constexpr int NP = (G * D + kRingThreads - 1) / kRingThreads;  // (g, j) pairs per thread
-    float a[NP];
-#pragma unroll
-    for (int k = 0; k < NP; ++k) a[k] = 0.0f;
-    for (int t0 = 0; t0 < n; t0 += kRingChunk) {
-        const int nc = min(kRingChunk, n - t0);
-        for (int c = tid; c < nc * (D / 8); c += kRingThreads) {
-            const int t = c / (D / 8), part = c % (D / 8);
-            const int slot = (first + t0 + t) % r.ring_cap;
-            vst[t][part] = reinterpret_cast<const uint4*>(r.v_ring + (row0 + slot) * D)[part];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const int idx = tid + k * kRingThreads;
-            if (idx < G * D) {
-                const int g = idx / D, j = idx % D;
-                const uint16_t* vs = reinterpret_cast<const uint16_t*>(&vst[0][0]);
-                for (int t = 0; t < nc; ++t) a[k] = fmaf(pw[g][t0 + t], half_bits_to_float(vs[t * D + j]), a[k]);
-            }
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int k = 0; k < NP; ++k) {
-        const int idx = tid + k * kRingThreads;
-        if (idx < G * D) accs[idx / D][idx % D] = a[k];
-    }
-    __syncthreads();
-
-    // record: (m, l) and acc, rotated into the values' basis (Pi_v acc = H diag(s_v) acc / sqrt(d))
-    for (int g = w; g < G; g += NW) {
-        const size_t rec = (static_cast<size_t>(b) * r.hq + hq0 + g) * r.rec_stride + r.ring_rec;
-        float v[DPL];
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) v[k] = accs[g][DPL * lane + k];
-        if constexpr (ROT) {
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) v[k] *= rotation_sign(cbv, DPL * lane + k);
-            wht_wave<DPL>(v, lane);
-#pragma unroll
-            for (int k = 0; k < DPL; ++k) v[k] *= kInvSqrtD;
-        }
-#pragma unroll
-        for (int k = 0; k < DPL; ++k) r.acc[rec * D + DPL * lane + k] = v[k];
-        if (lane == 0) {
-            float L = 0.0f;
-#pragma unroll
-            for (int i = 0; i < NW; ++i) L += red_l[i][g];
-            r.ml[rec] = n > 0 ? make_float2(M[g], L) : make_float2(-INFINITY, 0.0f);
-        }
+        a.out[static_cast<size_t>(row) * D + DPL * lane + k] = x * inv;
     }
 }
 
@@ -1651,13 +1696,13 @@ int check_decode(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* 
     return TQ_OK;
 }
 
-// Workspace of `splits + extra_recs` records per (b, query head) row.
-size_t workspace_bytes(const tq_layout* L, int split_tokens, int extra_recs) {
+// Workspace of `splits` records per (b, query head) row.
+size_t workspace_bytes(const tq_layout* L, int split_tokens) {
     if (check_layout(L) != TQ_OK) return 0;
     int len = 0;
     const int splits = resolve_splits(L, split_tokens, &len);
     if (splits <= 0) return 0;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * (splits + extra_recs);
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
     return recs * sizeof(float2) + recs * L->head_dim * sizeof(float);
 }
 
@@ -1673,11 +1718,11 @@ int tq_decode_splits(const tq_layout* L, int split_tokens) {
 }
 
 size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens) {
-    return tq::workspace_bytes(L, split_tokens, 0);
+    return tq::workspace_bytes(L, split_tokens);
 }
 
 size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens) {
-    return tq::workspace_bytes(L, split_tokens, 1);
+    return tq::workspace_bytes(L, split_tokens);  // the ring is merged in the combine: no record of its own
 }
 
 }  // extern "C"
@@ -1685,12 +1730,10 @@ size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens) {
 namespace tq {
 namespace {
 
-// Split records of the compressed cache; with extra_recs > 0 every (b, query head)
-// row of the workspace keeps that many more records after the splits.
+// Split records of the compressed cache.
 int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
                    const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream,
-                   int extra_recs = 0) {
+                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream) {
     int st = check_decode(L, cbk, cbv);
     if (st != TQ_OK) return st;
     int len = 0;
@@ -1701,7 +1744,7 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(ws, 16) || !aligned(q_rot, 4) ||
         !aligned(seq_lens, 4) || (scores && !aligned(scores, 4)) || (q_sketch && !aligned(q_sketch, 4)))
         return TQ_ERR_INVALID;
-    if (ws_bytes < workspace_bytes(L, split_tokens, extra_recs)) return TQ_ERR_WORKSPACE;
+    if (ws_bytes < workspace_bytes(L, split_tokens)) return TQ_ERR_WORKSPACE;
     DecodeArgs a{};
     a.q_rot = q_rot;
     a.q_sk = q_sketch;
@@ -1709,7 +1752,7 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     a.v_cache = static_cast<const uint8_t*>(v_cache);
     a.seq_lens = seq_lens;
     a.scores = scores;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * (splits + extra_recs);
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
     a.ml = static_cast<float2*>(ws);
     a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
     a.hq = L->n_q_heads;
@@ -1717,7 +1760,6 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     a.capacity = L->capacity;
     a.splits = splits;
     a.split_len = len;
-    a.rec_stride = splits + extra_recs;
     const int kf = L->k_format, vf = L->v_format;
     if (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ4, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ3>(a, L, *cbk, *cbv, stream);
@@ -1726,46 +1768,59 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     return TQ_ERR_UNSUPPORTED;
 }
 
-// Merge `records` records per (b, query head) row, normalize, rotate back.
-int combine(const tq_layout* L, const tq_codebook& cbv, int records, const void* ws, float* out, hipStream_t stream) {
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * records;
-    const float2* ml = static_cast<const float2*>(ws);
-    const float* acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + recs * sizeof(float2));
+// The capture ring a hybrid read attends over besides the compressed records.
+struct RingView {
+    const float* q_rot;
+    const void* k_ring;
+    const void* v_ring;
+    const int32_t* comp_lens;
+    const int32_t* ring_lens;
+    int ring_cap;
+};
+
+template <int D, bool ROT>
+void launch_combine(const CombineArgs& a, int rows, int rmax, const DevCodebook& ck, const DevCodebook& cv,
+                    hipStream_t st) {
+    const dim3 grid(rows), block(kCombineThreads);
+    if (rmax == 0) hipLaunchKernelGGL((decode_combine_kernel<D, ROT, 0>), grid, block, 0, st, a, ck, cv);
+    else if (rmax == 128) hipLaunchKernelGGL((decode_combine_kernel<D, ROT, 128>), grid, block, 0, st, a, ck, cv);
+    else hipLaunchKernelGGL((decode_combine_kernel<D, ROT, 256>), grid, block, 0, st, a, ck, cv);
+}
+
+// Merge the `splits` records of every (b, query head) row, and the capture ring
+// when one is given; normalize, rotate back.
+int combine(const tq_layout* L, const tq_codebook* cbk, const tq_codebook& cbv, int splits, const void* ws, float* out,
+            hipStream_t stream, const RingView* ring = nullptr) {
+    static_assert(kRingCapMax <= 256, "combine kernels are built for up to 256 ring tokens");
+    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
+    CombineArgs a{};
+    a.ml = static_cast<const float2*>(ws);
+    a.acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + recs * sizeof(float2));
+    a.out = out;
+    a.splits = splits;
+    a.hq = L->n_q_heads;
+    a.hkv = L->n_kv_heads;
+    int rmax = 0;
+    if (ring) {
+        a.q_rot = ring->q_rot;
+        a.k_ring = static_cast<const uint16_t*>(ring->k_ring);
+        a.v_ring = static_cast<const uint16_t*>(ring->v_ring);
+        a.comp_lens = ring->comp_lens;
+        a.ring_lens = ring->ring_lens;
+        a.ring_cap = ring->ring_cap;
+        rmax = ring->ring_cap <= 128 ? 128 : 256;
+    }
     const int rows = L->batch * L->n_q_heads;
     const bool rot = L->v_format != TQ_FMT_GQ2V;
-    const DevCodebook c = to_dev(cbv);
+    const DevCodebook cv = to_dev(cbv), ck = cbk ? to_dev(*cbk) : cv;
     if (L->head_dim == 128) {
-        if (rot) hipLaunchKernelGGL((decode_combine_kernel<128, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
-        else hipLaunchKernelGGL((decode_combine_kernel<128, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
+        if (rot) launch_combine<128, true>(a, rows, rmax, ck, cv, stream);
+        else launch_combine<128, false>(a, rows, rmax, ck, cv, stream);
     } else {
-        if (rot) hipLaunchKernelGGL((decode_combine_kernel<256, true>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
-        else hipLaunchKernelGGL((decode_combine_kernel<256, false>), dim3(rows), dim3(kCombineThreads), 0, stream, ml, acc, out, records, c);
+        if (rot) launch_combine<256, true>(a, rows, rmax, ck, cv, stream);
+        else launch_combine<256, false>(a, rows, rmax, ck, cv, stream);
     }
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-}
-
-template <int D, int G>
-int launch_ring(const RingArgs& r, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                hipStream_t st) {
-    const dim3 grid(L->n_kv_heads, L->batch);
-    if (L->v_format == TQ_FMT_GQ2V)
-        hipLaunchKernelGGL((ring_partial_kernel<D, G, false>), grid, dim3(kRingThreads), 0, st, r, to_dev(cbk), to_dev(cbv));
-    else
-        hipLaunchKernelGGL((ring_partial_kernel<D, G, true>), grid, dim3(kRingThreads), 0, st, r, to_dev(cbk), to_dev(cbv));
-    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-}
-
-template <int D>
-int dispatch_ring(const RingArgs& r, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
-                  hipStream_t st) {
-    switch (L->n_q_heads / L->n_kv_heads) {
-        case 1: return launch_ring<D, 1>(r, L, cbk, cbv, st);
-        case 2: return launch_ring<D, 2>(r, L, cbk, cbv, st);
-        case 4: return launch_ring<D, 4>(r, L, cbk, cbv, st);
-        case 5: return launch_ring<D, 5>(r, L, cbk, cbv, st);
-        case 8: return launch_ring<D, 8>(r, L, cbk, cbv, st);
-        default: return TQ_ERR_UNSUPPORTED;
-    }
 }
 
 }  // namespace
@@ -1799,7 +1854,7 @@ int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_toke
     const int splits = resolve_splits(L, split_tokens, &len);
     if (splits <= 0 || !ws || !out || !aligned(ws, 16) || !aligned(out, 4)) return TQ_ERR_INVALID;
     if (ws_bytes < tq_decode_workspace_bytes(L, split_tokens)) return TQ_ERR_WORKSPACE;
-    return combine(L, *cbv, splits, ws, out, stream);
+    return combine(L, nullptr, *cbv, splits, ws, out, stream);
 }
 
 int tq_decode_attention(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
@@ -1821,29 +1876,14 @@ int tq_decode_attention_hybrid(const tq_layout* L, const tq_codebook* cbk, const
     if (!out || !k_ring || !v_ring || !ring_lens || !aligned(out, 4) || !aligned(ring_lens, 4) ||
         !aligned(k_ring, 16) || !aligned(v_ring, 16))
         return TQ_ERR_INVALID;
-    if (ring_cap < 1 || ring_cap > kRingMax) return TQ_ERR_INVALID;
+    if (ring_cap < 1 || ring_cap > kRingCapMax) return TQ_ERR_INVALID;
     int st = decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, comp_lens, nullptr, split_tokens, ws,
-                            ws_bytes, Launch{stream, nullptr, nullptr}, 1);
+                            ws_bytes, Launch{stream, nullptr, nullptr});
     if (st != TQ_OK) return st;
     int len = 0;
     const int splits = resolve_splits(L, split_tokens, &len);
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * (splits + 1);
-    RingArgs r{};
-    r.q_rot = q_rot;
-    r.k_ring = static_cast<const uint16_t*>(k_ring);
-    r.v_ring = static_cast<const uint16_t*>(v_ring);
-    r.comp_lens = comp_lens;
-    r.ring_lens = ring_lens;
-    r.ml = static_cast<float2*>(ws);
-    r.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
-    r.hq = L->n_q_heads;
-    r.hkv = L->n_kv_heads;
-    r.ring_cap = ring_cap;
-    r.rec_stride = splits + 1;
-    r.ring_rec = splits;
-    st = L->head_dim == 128 ? dispatch_ring<128>(r, L, *cbk, *cbv, stream) : dispatch_ring<256>(r, L, *cbk, *cbv, stream);
-    if (st != TQ_OK) return st;
-    return combine(L, *cbv, splits + 1, ws, out, stream);
+    const RingView ring{q_rot, k_ring, v_ring, comp_lens, ring_lens, ring_cap};
+    return combine(L, cbk, *cbv, splits, ws, out, stream, &ring);
 }
 
 }  // extern "C"

@@ -304,8 +304,8 @@ int tq_ring_flush(const tq_layout* L, const tq_codebook* cbk, const tq_codebook*
                   int ring_cap, const void* k_ring, const void* v_ring, const int32_t* first, int count,
                   void* k_cache, void* v_cache, hipStream_t stream);
 
-/* Workspace of tq_decode_attention_hybrid: the split records plus one ring
- * record per (b, query head).                                              */
+/* Workspace of tq_decode_attention_hybrid: the split records alone (equal
+ * to tq_decode_workspace_bytes; the ring needs no record of its own).      */
 size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens);
 
 /* Hybrid decode: softmax attention of every query over the compressed
@@ -313,8 +313,8 @@ size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens);
  * comp_lens[b]+ring_lens[b]-1 together (comp_lens, ring_lens: device int32
  * [B]; ring_lens is clamped to [0, ring_cap]).  The compressed part runs
  * the split-K decode; the ring part scores exact fp16 keys against the
- * unrotated query (Pi^T q_rot) and sums exact fp16 values, then adds one
- * record per (b, query head) that the combine merges with the splits.  Both
+ * unrotated query (Pi^T q_rot) and sums exact fp16 values inside the
+ * combine, which merges them with the split records (two launches).  Both
  * empty: out = 0.  ws: tq_decode_hybrid_workspace_bytes.  Errors: as
  * tq_decode_attention, TQ_ERR_INVALID for a bad ring argument.              */
 int tq_decode_attention_hybrid(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,

@@ -152,7 +152,7 @@ def test_ring_calls_check_their_arguments_before_any_launch():
     assert tq.lib.tq_ring_flush(r(L), r(cb), r(cb), None, 64, fake, fake, fake, -1, fake, fake, None) == -1
     assert tq.lib.tq_ring_flush(r(L), r(cb), r(cb), None, 64, None, None, None, 0, None, None, None) == 0
     need = tq.decode_hybrid_workspace_bytes(L)
-    assert need == tq.decode_workspace_bytes(L) + 2 * 8 * (8 + 4 * 128)  # one more record per (b, query head)
+    assert need == tq.decode_workspace_bytes(L)  # the ring is merged in the combine, with no record of its own
     args = [r(L), r(cb), r(cb), fake, None, fake, fake, fake]
     assert tq.lib.tq_decode_attention_hybrid(*args, 0, fake, fake, fake, fake, 0, fake, need, None) == -1
     assert tq.lib.tq_decode_attention_hybrid(*args, 64, None, fake, fake, fake, 0, fake, need, None) == -1

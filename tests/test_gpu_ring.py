@@ -165,6 +165,17 @@ def test_hybrid_matches_oracle(name):
     _hybrid_case(name, comp, n, cap)
 
 
+@pytest.mark.parametrize("name,cap", [("c4", 256), ("c4", 201), ("c5", 256), ("c5", 130)])
+def test_hybrid_long_rings(name, cap):
+    """Rings longer than 128 tokens (the 256-token kernels; at d = 256 and 256
+    tokens the value rows are staged after the scores), full and partial,
+    with lengths that are not multiples of four."""
+    w = WORKLOADS[name]
+    comp = [w.context - cap - 11 * b for b in range(w.batch)]
+    n = [cap - 37 * b for b in range(w.batch)]
+    _hybrid_case(name, comp, n, cap)
+
+
 def test_hybrid_edge_lengths():
     """Empty ring, empty compressed part, both empty, a full ring that wraps,
     and a single ring token, in one batch of six sequences."""
