@@ -38,7 +38,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partial_pq4_c4_counters.txt")
-DECODE_SRC = os.path.join(ROOT, "compressed_domain_attention_kv_amd", "csrc", "tq_decode.hip")
+# the sources the decode_partial kernels are compiled from
+DECODE_SRCS = [os.path.join(ROOT, "compressed_domain_attention_kv_amd", "csrc", f)
+               for f in ("tq_decode.hip", "tq_device.h", "tq_internal.h")]
 
 
 def _log(msg):
@@ -46,8 +48,11 @@ def _log(msg):
 
 
 def decode_source_hash():
-    with open(DECODE_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in DECODE_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

@@ -28,7 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-mcode-object-version=5", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-ffp-contract=fast", "-munsafe-fp-atomics"]
 
-HIP_SOURCES = ["tq_write.hip", "tq_decode.hip"]
+HIP_SOURCES = ["tq_write.hip", "tq_decode.hip", "tq_combine.hip"]
 CPP_SOURCES = ["tq_host.cpp"]
 
 

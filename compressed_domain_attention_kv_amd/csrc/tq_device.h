@@ -9,6 +9,64 @@
 
 namespace tq {
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Lane exchange inside a row of 16 lanes through DPP (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
+__device__ __forceinline__ float lane_value(float x, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+// Maximum / sum over the 64 lanes; every lane receives the same value (the
+// butterfly is symmetric, so the sum is bit-identical in all lanes).
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<kDppXor1>(x));
+    x = fmaxf(x, dpp<kDppXor2>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppMirror>(x));
+    return fmaxf(fmaxf(lane_value(x, 0), lane_value(x, 16)), fmaxf(lane_value(x, 32), lane_value(x, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp<kDppXor1>(x);
+    x += dpp<kDppXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    x += dpp<kDppMirror>(x);
+    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+// Unnormalized Sylvester Walsh-Hadamard transform of a vector spread over one
+// wavefront: element j = DPL * lane + k sits in v[k].
+template <int DPL>
+__device__ __forceinline__ void wht_wave(float (&v)[DPL], int lane) {
+#pragma unroll
+    for (int st = 1; st < DPL; st <<= 1)
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+            if ((k & st) == 0) {
+                const float x = v[k], y = v[k + st];
+                v[k] = x + y;
+                v[k + st] = x - y;
+            }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) {
+            const float p = __shfl_xor(v[k], m, 64);
+            v[k] = upper ? (p - v[k]) : (v[k] + p);
+        }
+    }
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     _Float16 h;
     const uint16_t b = static_cast<uint16_t>(bits16);

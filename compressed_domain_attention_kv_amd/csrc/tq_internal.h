@@ -33,6 +33,21 @@ inline DevCodebook to_dev(const tq_codebook& cb) {
     return d;
 }
 
+// The capture ring a hybrid read attends over besides the compressed records.
+struct RingView {
+    const float* q_rot;
+    const void* k_ring;
+    const void* v_ring;
+    const int32_t* comp_lens;
+    const int32_t* ring_lens;
+    int ring_cap;
+};
+
+// Merge the `splits` records of every (b, query head) row of the decode workspace,
+// and the capture ring when one is given; normalize, rotate back (tq_combine.hip).
+int combine(const tq_layout* L, const tq_codebook* cbk, const tq_codebook& cbv, int splits, const void* ws,
+            float* out, hipStream_t stream, const RingView* ring = nullptr);
+
 size_t vector_bytes(int format, int d);
 bool is_rotated(int format);
 int format_bits(int format);  // code bits per coordinate a format stores in its table
