@@ -57,6 +57,14 @@ __device__ __forceinline__ uint32_t byte_at(const uint32_t (&w)[N], int k) {
     return (w[k >> 2] >> (8 * (k & 3))) & 0xFFu;
 }
 
+// 16 bytes of a cache stream, read with the non-temporal policy (each byte is read
+// once per decode; streaming reads measured faster with it)
+__device__ __forceinline__ uint4 stream_load16(const uint4* p) {
+    typedef uint32_t v4 __attribute__((ext_vector_type(4)));
+    const v4 x = __builtin_nontemporal_load(reinterpret_cast<const v4*>(p));
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 template <int KF, int VF, int D, int G>
 struct Smem {
     static constexpr int VBK = vbytes<KF, D>();
@@ -143,9 +151,9 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
             uint4* vd = reinterpret_cast<uint4*>(sm.vtile[w]);
             constexpr int CK = kTile * VBK / 16, CV = kTile * VBV / 16;
 #pragma unroll
-            for (int c = lane; c < CK; c += 64) kd[c] = ks[c];
+            for (int c = lane; c < CK; c += 64) kd[c] = stream_load16(ks + c);
 #pragma unroll
-            for (int c = lane; c < CV; c += 64) vd[c] = vs[c];
+            for (int c = lane; c < CV; c += 64) vd[c] = stream_load16(vs + c);
         }
         __syncthreads();
 
@@ -481,7 +489,8 @@ struct ValueTile {
 
 // Raw buffer view of one cache stream: loads take a per-lane byte offset
 // fixed for the whole split plus a wave-uniform tile offset in an SGPR, so
-// a tile's loads cost no address arithmetic; reads past the stream return 0.
+// a tile's loads cost no address arithmetic.  Only whole tiles inside the
+// stream are requested through it (the SGPR offset is not range-checked).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0), static_cast<int>(bytes),
                                              0x00020000);
@@ -491,6 +500,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const uint8_t* bas
 // once per decode, and streaming reads with nt measured about 7% more bandwidth on
 // MI355X than default-policy reads (6.7 vs 6.1 TB/s median over 570 MB).
 constexpr int kStreamPolicy = 2;
+
+// A resource of zero bytes: loads through it return zeros and read no memory.  The
+// request for "the next tile" after a wavefront's last tile goes through it, so the
+// loads stay unconditional (one path for the compiler's waits) at no HBM cost.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t null_rsrc(const uint8_t* base) { return stream_rsrc(base, 0); }
 
 template <int VB, int NTB, int NB>
 __device__ __forceinline__ void load_keys(KeyTile<NTB, NB>& k, __amdgpu_buffer_rsrc_t r, int norm_off, int word_off,
@@ -573,6 +587,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
     const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
     const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
     const int k_norm = n * VB;                   // key norm of token n
     const int k_word = n * VB + 4 + 16 * g;      // key words 4g..4g+3 of token n
     const int v_norm = n * VB;                   // value norm of token n
@@ -644,7 +659,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     for (; t0 < end; t0 += kStep) {
         const int nv = min(TT, end - t0);
         // the last tile reloads itself instead of reading past the split
-        const int t_next = t0 + kStep < end ? t0 + kStep : t0;
+        const bool more = t0 + kStep < end;
+        const int t_next = more ? t0 + kStep : t0;
+        const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
 
         // ---- scores: column n = token 16 tb + n, k-group g = 32 coordinates per
         // block.  Job J = S * NTB + tb multiplies chunk S (nibbles 4(S&1)..+3 of
@@ -686,7 +703,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             });
         }
         // the keys of this tile are consumed: request the next tile's
-        load_keys<VB>(kt, krs, k_norm, k_word, t_next * VB);
+        load_keys<VB>(kt, krn, k_norm, k_word, t_next * VB);
 
         // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
         // (G is even, so both heads of a lane exist exactly when 2g < G)
@@ -800,7 +817,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
         }
         lds_order();
         // the values of this tile are consumed: request the next tile's
-        load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
+        load_values<VB>(vt, vrn, v_norm, v_word, t_next * VB);
     }
 
     // ---- merge the wavefronts of the workgroup and write the split record
@@ -980,6 +997,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
     const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
     const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
     const int k_norm = n * VB, k_word = n * VB + 4 + 16 * g, v_norm = n * VB, v_word = 4 * g * VB + 4 + 4 * n;
     uint32_t* wa = sm.wa[wi];
 
@@ -1013,15 +1031,19 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         }
     }
 
-    // the first tile, requested unconditionally: a wavefront without tiles reads bytes it never
-    // uses (the buffer range returns zeros past the stream), and the loads stay on one path, so
-    // the waits of the table fill below count only the small reads above
+    // the first tile, requested unconditionally so the loads stay on one path and the waits of
+    // the table fill below count only the small reads above; a wavefront without tiles requests
+    // it through the empty resource (zeros, no memory read)
     int t0 = start + w * TT;
     KeyTile<NTB, 1> kt[VLDS ? 2 : 1];
     ValueTile<NTB, 1> vt;
-    load_keys<VB>(kt[0], krs, k_norm, k_word, t0 * VB);
-    if constexpr (VLDS) stage_values<VB>(vrs, vst0[wi], t0 * VB, lane);
-    else load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
+    {
+        const bool any = t0 < end;
+        const __amdgpu_buffer_rsrc_t kr0 = any ? krs : krs_none, vr0 = any ? vrs : vrs_none;
+        load_keys<VB>(kt[0], kr0, k_norm, k_word, t0 * VB);
+        if constexpr (VLDS) stage_values<VB>(vr0, vst0[wi], t0 * VB, lane);
+        else load_values<VB>(vt, vr0, v_norm, v_word, t0 * VB);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -1080,11 +1102,13 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         constexpr int P = decltype(pc)::value;
         KeyTile<NTB, 1>& kc = kt[VLDS ? P : 0];
         const int nv = min(TT, end - t0);  // <= 0 for the odd tile after the last one
-        const int t_next = t0 + kStep < end ? t0 + kStep : t0;
+        const bool more = t0 + kStep < end;
+        const int t_next = more ? t0 + kStep : t0;
+        const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
         const uint8_t* vcur = P == 0 ? vst0[wi] : vst1[wi];
         if constexpr (VLDS) {
-            stage_values<VB>(vrs, P == 0 ? vst1[wi] : vst0[wi], t_next * VB, lane);
-            load_keys<VB>(kt[1 - P], krs, k_norm, k_word, t_next * VB);
+            stage_values<VB>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VB, lane);
+            load_keys<VB>(kt[1 - P], krn, k_norm, k_word, t_next * VB);
         }
 
         // ---- scores: job J = I * NTB + tb reads bytes 0..3 of key word I of block tb
@@ -1128,7 +1152,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
-        if constexpr (!VLDS) load_keys<VB>(kt[0], krs, k_norm, k_word, t_next * VB);
+        if constexpr (!VLDS) load_keys<VB>(kt[0], krn, k_norm, k_word, t_next * VB);
         if constexpr (VLDS) {  // this tile's value words and norms, from its stage
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
@@ -1231,7 +1255,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             });
         }
         lds_order();
-        if constexpr (!VLDS) load_values<VB>(vt, vrs, v_norm, v_word, t_next * VB);
+        if constexpr (!VLDS) load_values<VB>(vt, vrn, v_norm, v_word, t_next * VB);
     };
     if constexpr (VLDS) {
         // pairs of tiles, so that the parity is static; the second tile of the last pair may be
