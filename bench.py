@@ -142,6 +142,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--hybrid", action="store_true",
                     help="measure the capture-ring mode instead: exact ring + batched flush + hybrid read")
+    ap.add_argument("--sweep", action="store_true",
+                    help="kernel times of the other workloads at full size (c5 bulk prefill, c1/c2/c3/c5 decode), "
+                         "one JSON line each; not the headline line")
     ap.add_argument("--ring-cap", type=int, default=128)
     ap.add_argument("--flush", type=int, default=64)
     args = ap.parse_args()
@@ -161,6 +164,8 @@ def main():
         raise SystemExit("the bench line is the c4 decode workload; other workloads are parity tests")
     if args.hybrid:
         return bench_hybrid(args)
+    if args.sweep:
+        return bench_sweep(args)
     w = synth.C4
     B, Hq, Hkv, d, cap, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.capacity, w.context
     torch.cuda.set_device(0)
@@ -446,6 +451,133 @@ def bench_hybrid(args):
         "cpu_baseline": None,
     }
     print(json.dumps(res), flush=True)
+
+
+SWEEP_NOTE = ("per-kernel times of a workload other than the headline one: decode_partial from events on its "
+              "own dispatch, the other calls as the mean over a replayed HIP graph of repeated calls (so "
+              "including the gap between kernels); algorithmic bytes as in the roofline of the "
+              "headline line; useful flops count the method's arithmetic only (2 G d FMA per token and KV "
+              "head, plus G d for the QJL term of TQ3K keys)")
+
+
+def bench_sweep(args):
+    """The write path at its bulk size (c5 prefill: 131,072 tokens x 4 KV heads at d 256) and the
+    decode of c1, c2, c3 and c5 at full size, each timed on its own; one JSON line per item."""
+    import numpy as np
+    import torch
+
+    import compressed_domain_attention_kv_amd as tq
+    import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    def per_call_ms(fn, reps):
+        """Mean time per call of `reps` calls captured in one HIP graph and replayed, so the
+        host's launch rate does not set the time of microsecond kernels."""
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) / reps
+            best = t if best is None else min(best, t)
+        del g
+        return best
+
+    def emit(item, **kv):
+        print(json.dumps({"sweep": item, "note": SWEEP_NOTE, **kv}), flush=True)
+
+    def codebooks(w):
+        tq3k = w.k_format == synth.TQ3K
+        cbk, S = tq.build_codebook(w.head_dim, w.k_bits, w.k_kind, w.rot_seed_k, w.qjl_seed, want_qjl_matrix=tq3k)
+        cbv, _ = tq.build_codebook(w.head_dim, w.v_bits, w.v_kind, w.rot_seed_v, w.qjl_seed + 1)
+        return cbk, cbv, (torch.from_numpy(S).to(dev) if tq3k else None)
+
+    # ---- write path: c5 bulk prefill in one call (HBM-bound: fp16 rows in, blocks out)
+    w5 = synth.C5
+    T, Hp, d = w5.extra["prefill_tokens"], w5.extra["prefill_kv_heads"], w5.head_dim
+    wp = synth.scaled(w5, batch=1, n_q_heads=Hp, n_kv_heads=Hp, capacity=T, context=T, prefill=T)
+    cbk5, cbv5, _ = codebooks(w5)
+    Lp = tq.Layout(1, Hp, Hp, d, T, w5.k_format, w5.v_format)
+    kb5, vb5 = tq.cache_bytes(Lp)
+    kc5 = torch.empty(kb5, dtype=torch.uint8, device=dev)
+    vc5 = torch.empty(vb5, dtype=torch.uint8, device=dev)
+    t0 = time.time()
+    k_rows = torch.from_numpy(synth.batch_rows(wp, synth.K_TENSOR, 0, 0, T)).to(dev)
+    v_rows = torch.from_numpy(synth.batch_rows(wp, synth.V_TENSOR, 0, 0, T)).to(dev)
+    dst = torch.arange(T, dtype=torch.int32, device=dev)
+    _log(f"sweep: c5 prefill rows generated in {time.time() - t0:.1f}s")
+    ms = per_call_ms(lambda: tq.quantize_append(Lp, cbk5, cbv5, None, k_rows, v_rows, dst, kc5, vc5), 10)
+    nbytes = 2 * T * Hp * d * 2 + kb5 + vb5
+    emit("c5 bulk prefill (write path: norm, rotate, quantize, pack K and V)", kernel="quantize_kv_kernel",
+         workload=f"{T} tokens x {Hp} KV heads, d {d}, PQ4 K and V", us=ms * 1e3, bytes=nbytes,
+         roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    del k_rows, v_rows
+    torch.cuda.synchronize()
+
+    # ---- decode of the other workloads (c5 reads the prefill bytes as [32][2][8192])
+    for w in (synth.C1, synth.C2, synth.C3, synth.C5):
+        B, Hq, Hkv, d, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
+        L = tq.Layout(B, Hq, Hkv, d, w.capacity, w.k_format, w.v_format)
+        if w is synth.C5:
+            cbk, cbv, S = cbk5, cbv5, None
+            kc, vc = kc5, vc5
+        else:
+            cbk, cbv, S = codebooks(w)
+            kbytes, vbytes = tq.cache_bytes(L)
+            kc = torch.zeros(kbytes, dtype=torch.uint8, device=dev)
+            vc = torch.zeros(vbytes, dtype=torch.uint8, device=dev)
+            krows, vrows = gen_rows(w, synth.K_TENSOR, w.prefill), gen_rows(w, synth.V_TENSOR, w.prefill)
+            for b in range(B):
+                dst = torch.arange(b * w.capacity, b * w.capacity + w.prefill, dtype=torch.int32, device=dev)
+                tq.quantize_append(L, cbk, cbv, S, torch.from_numpy(krows[b]).to(dev),
+                                   torch.from_numpy(vrows[b]).to(dev), dst, kc, vc)
+        q = torch.from_numpy(synth.queries(w)).to(dev)
+        q_rot = torch.empty_like(q)
+        q_sk = torch.empty_like(q) if S is not None else None
+        out = torch.empty_like(q)
+        seq = torch.full((B,), N, dtype=torch.int32, device=dev)
+        ws = torch.empty(tq.decode_workspace_bytes(L), dtype=torch.uint8, device=dev)
+        reps = 200 if N * B <= 65536 else 50
+        rot_ms = per_call_ms(lambda: tq.rotate_sketch_query(L, cbk, S, q, q_rot, q_sk), reps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e in ev:  # create the HIP events before handing their handles over
+            e[0].record()
+            e[1].record()
+        for i in range(3):
+            tq.decode_partial(L, cbk, cbv, q_rot, q_sk, kc, vc, seq, ws)
+        torch.cuda.synchronize()
+        for e in ev:
+            tq.decode_partial(L, cbk, cbv, q_rot, q_sk, kc, vc, seq, ws, events=(e[0].cuda_event, e[1].cuda_event))
+        torch.cuda.synchronize()
+        part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+        comb_ms = per_call_ms(lambda: tq.decode_combine(L, cbv, ws, out), reps)
+        alg = B * Hkv * N * (tq.vector_bytes(w.k_format, d) + tq.vector_bytes(w.v_format, d))
+        fma = B * Hkv * N * w.group * d * (3 if w.k_format == synth.TQ3K else 2)
+        gbs = alg / (part_ms * 1e-3) / 1e9
+        emit(f"{w.name} decode", kernel="decode_partial + decode_combine",
+             workload=f"batch {B}, {Hq} query / {Hkv} KV heads, d {d}, context {N}, formats K {w.k_format} V "
+                      f"{w.v_format} (1 PQ4, 2 PQ3, 3 TQ3K, 4 GQ2V)",
+             splits=tq.decode_splits(L), us={"rotate_query": rot_ms * 1e3, "decode_partial": part_ms * 1e3,
+                                             "decode_combine": comb_ms * 1e3},
+             bytes=alg, useful_tflops=2 * fma / (part_ms * 1e-3) / 1e12,
+             roofline={"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": gbs / HBM_PEAK_GBS})
+        del kc, vc
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -67,65 +67,98 @@ constexpr int vec_bytes_c() {
                               : 12 * (D / kGroup);
 }
 
-// The rows of workgroup `block` of one quantize grid.
+// Vectors per lane group handled by one workgroup pass: every one of them has its
+// source row requested before the first is encoded, so a wavefront keeps U rows in
+// flight instead of paying one memory latency per row.
+constexpr int kWriteUnroll = 8;
+
+// Where vector `vec` of a write goes (byte offset of its block) and which source
+// row it reads; inactive vectors (past nvec, bad destination) compute on row 0
+// and store nothing.
 template <int FMT, int D, Src SRC>
-__device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodebook& cb, int block) {
-    constexpr int LPV = D / 8;                  // lanes per vector
-    constexpr int VPB = kWriteThreads / LPV;    // vectors per workgroup
+struct VecTarget {
+    bool active;
+    size_t off;
+    size_t src_row;
+};
+
+template <int FMT, int D, Src SRC>
+__device__ __forceinline__ VecTarget<FMT, D, SRC> vec_target(const WriteArgs& a, int vec) {
     constexpr int VB = vec_bytes_c<FMT, D>();
-    __shared__ float r_sh[FMT == TQ_FMT_TQ3K ? VPB * D : 1];
-
-    const int tid = threadIdx.x;
-    const int l = tid % LPV;
-    const int slot = tid / LPV;
-    const int vec = block * VPB + slot;
-    bool active = vec < a.nvec;
-
-    // destination byte offset of this vector
-    size_t off = 0;
-    size_t src_row = static_cast<size_t>(vec < a.nvec ? vec : 0);  // fp16 source row
+    VecTarget<FMT, D, SRC> t{vec < a.nvec, 0, 0};
     if constexpr (SRC == Src::kRing) {
-        const int t = vec / a.hkv, h = vec % a.hkv;
-        const int bb = (vec < a.nvec ? t : 0) / a.count, i = t % a.count;
+        const int tk = vec / a.hkv, h = vec % a.hkv;
+        const int bb = (t.active ? tk : 0) / a.count, i = tk % a.count;
         const int f = a.first[bb];
         const int pos = f + i;
-        if (!active || f < 0 || pos >= a.capacity) active = false;
-        else off = ((static_cast<size_t>(bb) * a.hkv + h) * a.capacity + pos) * VB;
-        src_row = active ? (static_cast<size_t>(bb) * a.hkv + h) * a.ring_cap + pos % a.ring_cap : 0;
-    } else if (active) {
-        if (a.dst_row) {
-            const int t = vec / a.hkv, h = vec % a.hkv;
-            const int r = a.dst_row[t];
-            if (r < 0 || r >= a.batch * a.capacity) {
-                active = false;
+        if (!t.active || f < 0 || pos >= a.capacity) t.active = false;
+        else t.off = ((static_cast<size_t>(bb) * a.hkv + h) * a.capacity + pos) * VB;
+        t.src_row = t.active ? (static_cast<size_t>(bb) * a.hkv + h) * a.ring_cap + pos % a.ring_cap : 0;
+    } else {
+        t.src_row = t.active ? static_cast<size_t>(vec) : 0;
+        if (t.active) {
+            if (a.dst_row) {
+                const int tk = vec / a.hkv, h = vec % a.hkv;
+                const int r = a.dst_row[tk];
+                if (r < 0 || r >= a.batch * a.capacity) {
+                    t.active = false;
+                } else {
+                    const int b = r / a.capacity, pos = r % a.capacity;
+                    t.off = ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + pos) * VB;
+                }
             } else {
-                const int b = r / a.capacity, pos = r % a.capacity;
-                off = ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + pos) * VB;
+                t.off = static_cast<size_t>(vec) * VB;
             }
-        } else {
-            off = static_cast<size_t>(vec) * VB;
         }
     }
-    const int vsrc = vec < a.nvec ? vec : 0;  // inactive lanes compute on row 0 and store nothing
+    return t;
+}
 
+// The 8 coordinates 8l .. 8l+7 of one source row, as loaded (not yet converted).
+struct RowPiece {
+    uint4 x;        // fp16 rows
+    float4 y0, y1;  // fp32 rotated rows
+    uint32_t n16;   // their stored norm
+};
+
+template <int D, Src SRC>
+__device__ __forceinline__ RowPiece load_piece(const WriteArgs& a, size_t row, int l) {
+    RowPiece p{};
+    if constexpr (SRC != Src::kRotated) {
+        p.x = *reinterpret_cast<const uint4*>(a.x + row * D + 8 * l);
+    } else {
+        const float4* src = reinterpret_cast<const float4*>(a.y + row * D + 8 * l);
+        p.y0 = src[0];
+        p.y1 = src[1];
+        p.n16 = a.norm16[row];
+    }
+    return p;
+}
+
+// Rotation signs of coordinates 8l .. 8l+7 (one byte of the sign words).
+__device__ __forceinline__ uint32_t sign_byte(const DevCodebook& cb, int l) {
+    return (cb.sign_bits[l >> 2] >> (8 * (l & 3))) & 0xFFu;
+}
+
+// Encode one vector from its loaded piece and store its block.
+template <int FMT, int D, Src SRC>
+__device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook& cb, const VecTarget<FMT, D, SRC>& tg,
+                                           const RowPiece& in, uint32_t sgn, int l, int slot, float* r_sh) {
+    constexpr int LPV = D / 8;
+    const bool active = tg.active;
     float v[8];
     uint32_t n16 = 0;
     if constexpr (SRC != Src::kRotated) {
-        const size_t row = SRC == Src::kRing ? src_row : static_cast<size_t>(vsrc);
-        const uint4 raw = *reinterpret_cast<const uint4*>(a.x + row * D + 8 * l);
-        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        const uint32_t w[4] = {in.x.x, in.x.y, in.x.z, in.x.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     } else {
-        const float4* src = reinterpret_cast<const float4*>(a.y + static_cast<size_t>(vsrc) * D + 8 * l);
-        const float4 p0 = src[0], p1 = src[1];
-        v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
-        v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
-        n16 = a.norm16[vsrc];
+        v[0] = in.y0.x; v[1] = in.y0.y; v[2] = in.y0.z; v[3] = in.y0.w;
+        v[4] = in.y1.x; v[5] = in.y1.y; v[6] = in.y1.z; v[7] = in.y1.w;
+        n16 = in.n16;
     }
 
-    uint8_t* dst = a.out + off;
-
+    uint8_t* dst = a.out + tg.off;
     if constexpr (FMT == TQ_FMT_GQ2V) {
         // asymmetric 2-bit group quantization, groups of 32 channels = 4 lanes
         float mn = v[0], mx = v[0];
@@ -156,7 +189,6 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
             if (lg == 0) *reinterpret_cast<uint32_t*>(g) = s16 | (z16 << 16);
             *reinterpret_cast<uint16_t*>(g + 4 + 2 * lg) = static_cast<uint16_t>(packed);
         }
-        return;
     } else {
         constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
         if constexpr (SRC != Src::kRotated) {
@@ -168,7 +200,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
             n16 = float_to_half_bits(fminf(n, kFp16Max));
             const float inv = n > 0.0f ? __fdiv_rn(1.0f, n) : 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * rotation_sign(cb, 8 * l + e);
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * (((sgn >> e) & 1u) ? -1.0f : 1.0f);
             wht8<LPV>(v, l);
 #pragma unroll
             for (int e = 0; e < 8; ++e) v[e] *= kInvSqrtD;
@@ -214,7 +246,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
             float g2 = 0.0f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                r[e] = r[e] * kInvSqrtD * rotation_sign(cb, 8 * l + e);
+                r[e] = r[e] * kInvSqrtD * (((sgn >> e) & 1u) ? -1.0f : 1.0f);
                 g2 += r[e] * r[e];
             }
             g2 = group_sum<LPV>(g2);
@@ -237,6 +269,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
                 }
                 bits |= (acc >= 0.0f ? 1u : 0u) << e;
             }
+            __syncthreads();  // every lane has read the residuals before the next vector writes them
             if (active) {
                 if (l == 0) *reinterpret_cast<uint32_t*>(dst) = n16 | (g16 << 16);
                 *reinterpret_cast<uint16_t*>(dst + 4 + 2 * l) = static_cast<uint16_t>(low);
@@ -244,6 +277,29 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
             }
         }
     }
+}
+
+
+// The vectors of workgroup `block` of one quantize grid: kWriteUnroll passes of
+// kWriteThreads / (d / 8) vectors.
+template <int FMT, int D, Src SRC>
+__device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodebook& cb, int block) {
+    constexpr int LPV = D / 8;                  // lanes per vector
+    constexpr int VPB = kWriteThreads / LPV;    // vectors per pass
+    constexpr int U = kWriteUnroll;
+    __shared__ float r_sh[FMT == TQ_FMT_TQ3K ? VPB * D : 1];
+    const int tid = threadIdx.x;
+    const int l = tid % LPV;
+    const int slot = tid / LPV;
+    const uint32_t sgn = sign_byte(cb, l);
+    VecTarget<FMT, D, SRC> tg[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) tg[u] = vec_target<FMT, D, SRC>(a, (block * U + u) * VPB + slot);
+    RowPiece in[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) in[u] = load_piece<D, SRC>(a, tg[u].src_row, l);
+#pragma unroll
+    for (int u = 0; u < U; ++u) encode_vec<FMT, D, SRC>(a, cb, tg[u], in[u], sgn, l, slot, r_sh);
 }
 
 template <int FMT, int D, Src SRC>
@@ -336,8 +392,8 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
 
 template <int FMT, int D, Src SRC>
 int launch_quantize(const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
-    constexpr int VPB = kWriteThreads / (D / 8);
-    const int grid = (a.nvec + VPB - 1) / VPB;
+    constexpr int VPG = kWriteThreads / (D / 8) * kWriteUnroll;  // vectors per workgroup
+    const int grid = (a.nvec + VPG - 1) / VPG;
     hipLaunchKernelGGL((quantize_kernel<FMT, D, SRC>), dim3(grid), dim3(kWriteThreads), 0, st, a, to_dev(cb));
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
@@ -345,8 +401,8 @@ int launch_quantize(const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
 template <int FMT, int D, Src SRC>
 int launch_quantize_kv(const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk, const tq_codebook& cbv,
                        hipStream_t st) {
-    constexpr int VPB = kWriteThreads / (D / 8);
-    const int kblocks = (ak.nvec + VPB - 1) / VPB;
+    constexpr int VPG = kWriteThreads / (D / 8) * kWriteUnroll;  // vectors per workgroup
+    const int kblocks = (ak.nvec + VPG - 1) / VPG;
     hipLaunchKernelGGL((quantize_kv_kernel<FMT, D, SRC>), dim3(2 * kblocks), dim3(kWriteThreads), 0, st, ak, av,
                        to_dev(cbk), to_dev(cbv), kblocks);
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
