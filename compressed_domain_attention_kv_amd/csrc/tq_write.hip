@@ -17,6 +17,7 @@ namespace tq {
 namespace {
 
 constexpr int kWriteThreads = 256;
+constexpr int kWriteThreadsC = kWriteThreads;
 
 // kFp16Rows: fp16 rows x[nvec][d], destination row from dst_row (append);
 // kRotated: fp32 rotated rows y with given norms, dense output (code test);
@@ -63,6 +64,29 @@ __device__ __forceinline__ uint32_t code_of16(float y, float b3, float b7, float
     const bool m2 = y > f.y;
     const bool m1 = y > (m2 ? f.z : f.x);
     return 4u * q | (m2 ? 2u : 0u) | (m1 ? 1u : 0u);
+}
+
+// Sketch rows of the vectors a workgroup holds in LDS: thread t owns row
+// i = t % d of S and the vectors h, h + NH, ... with h = t / d (NH = 256 / d row
+// groups); acc[k] = sum_j S[i][j] xs[h + NH k][j], summed over j in order four
+// at a time.  Every thread streams its own row of S, so the loads are independent
+// and the vectors are LDS broadcasts.
+template <int D, int NV>
+__device__ __forceinline__ void sketch_rows(const float* __restrict__ S, const float* xs, int tid, float (&acc)[NV]) {
+    constexpr int NH = kWriteThreadsC / D;
+    const int i = tid % D, h = tid / D;
+    const float4* srow = reinterpret_cast<const float4*>(S + static_cast<size_t>(i) * D);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) acc[k] = 0.0f;
+#pragma unroll 8
+    for (int j = 0; j < D / 4; ++j) {
+        const float4 s4 = srow[j];
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const float4 x4 = reinterpret_cast<const float4*>(xs + (h + NH * k) * D)[j];
+            acc[k] += s4.x * x4.x + s4.y * x4.y + s4.z * x4.z + s4.w * x4.w;
+        }
+    }
 }
 
 template <int FMT>
@@ -160,7 +184,8 @@ __device__ __forceinline__ uint32_t sign_byte(const DevCodebook& cb, int l) {
 // Encode one vector from its loaded piece and store its block.
 template <int FMT, int D, Src SRC>
 __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook& cb, const VecTarget<FMT, D, SRC>& tg,
-                                           const RowPiece& in, uint32_t sgn, int l, int slot, float* r_sh) {
+                                           const RowPiece& in, uint32_t sgn, int l, int slot, float* r_sh,
+                                           uint64_t* qjl_sh) {
     constexpr int LPV = D / 8;
     const bool active = tg.active;
     float v[8];
@@ -272,21 +297,20 @@ __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook
 #pragma unroll
             for (int e = 0; e < 8; ++e) rs[8 * l + e] = r[e];
             __syncthreads();
-            uint32_t bits = 0;
+            // b_i = [(S r)_i >= 0]: the sketch rows per thread, the bits of 64 rows of one
+            // vector gathered by a ballot into LDS, where lane l finds its byte (rows 8l..8l+7)
+            constexpr int VPB = kWriteThreads / LPV, NH = kWriteThreads / D, NV = VPB / NH;
+            float acc[NV];
+            sketch_rows<D, NV>(a.S, r_sh, threadIdx.x, acc);
+            const int lane = threadIdx.x & 63, row0 = (threadIdx.x % D) & ~63, h = threadIdx.x / D;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int i = 8 * l + e;
-                const float4* Srow = reinterpret_cast<const float4*>(a.S + static_cast<size_t>(i) * D);
-                const float4* rr = reinterpret_cast<const float4*>(rs);
-                float acc = 0.0f;
-#pragma unroll 8
-                for (int j = 0; j < D / 4; ++j) {
-                    const float4 s4 = Srow[j], r4 = rr[j];
-                    acc += s4.x * r4.x + s4.y * r4.y + s4.z * r4.z + s4.w * r4.w;
-                }
-                bits |= (acc >= 0.0f ? 1u : 0u) << e;
+            for (int k = 0; k < NV; ++k) {
+                const uint64_t m = __builtin_amdgcn_ballot_w64(acc[k] >= 0.0f);
+                if (lane == 0) qjl_sh[(h + NH * k) * (D / 64) + row0 / 64] = m;
             }
-            __syncthreads();  // every lane has read the residuals before the next vector writes them
+            __syncthreads();
+            const uint32_t bits = reinterpret_cast<const uint8_t*>(qjl_sh + slot * (D / 64))[l];
+            __syncthreads();  // residuals and bits are read before the next vector writes them
             if (active) {
                 if (l == 0) *reinterpret_cast<uint32_t*>(dst) = n16 | (g16 << 16);
                 *reinterpret_cast<uint16_t*>(dst + 4 + 2 * l) = static_cast<uint16_t>(low);
@@ -305,6 +329,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
     constexpr int VPB = kWriteThreads / LPV;    // vectors per pass
     constexpr int U = kWriteUnroll;
     __shared__ float r_sh[FMT == TQ_FMT_TQ3K ? VPB * D : 1];
+    __shared__ uint64_t qjl_sh[FMT == TQ_FMT_TQ3K ? VPB * D / 64 : 1];  // sketch bits per vector
     const int tid = threadIdx.x;
     const int l = tid % LPV;
     const int slot = tid / LPV;
@@ -316,7 +341,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
 #pragma unroll
     for (int u = 0; u < U; ++u) in[u] = load_piece<D, SRC>(a, tg[u].src_row, l);
 #pragma unroll
-    for (int u = 0; u < U; ++u) encode_vec<FMT, D, SRC>(a, cb, tg[u], in[u], sgn, l, slot, r_sh);
+    for (int u = 0; u < U; ++u) encode_vec<FMT, D, SRC>(a, cb, tg[u], in[u], sgn, l, slot, r_sh, qjl_sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,7 +521,14 @@ __global__ __launch_bounds__(kWriteThreads) void ring_append_kernel(const uint4*
     else v_ring[dst] = v_new[j];
 }
 
-// q_rot = Pi q = H (s * q) / sqrt(d); for TQ3K keys also q_sketch = S q.
+// q_rot = Pi q = H (s * q) / sqrt(d); for TQ3K keys also q_sketch = S q.  With the
+// sketch the grid has D / RPW workgroups per group of VPB queries along y: workgroup
+// y writes rows y RPW .. y RPW + RPW - 1 of the sketch, one (row, query) dot
+// product per thread (the queries of a row are consecutive threads, so they read
+// the same row of S), and workgroup y = 0 also writes q_rot.
+template <int D>
+constexpr int sketch_rows_per_wg() { return kWriteThreads / (kWriteThreads / (D / 8)); }
+
 template <int D, bool SKETCH>
 __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float* __restrict__ q, float* __restrict__ q_rot,
                                                                   float* __restrict__ q_sk, const float* __restrict__ S,
@@ -504,7 +536,8 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
     constexpr int LPV = D / 8;
     constexpr int VPB = kWriteThreads / LPV;
     constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
-    __shared__ float q_sh[SKETCH ? VPB * D : 1];
+    constexpr int QS = D + 4;  // padded rows: the queries of one row read distinct banks
+    __shared__ float q_sh[SKETCH ? VPB * QS : 1];
     const int tid = threadIdx.x, l = tid % LPV, slot = tid / LPV;
     const int vec = blockIdx.x * VPB + slot;
     const bool active = vec < nvec;
@@ -514,37 +547,30 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
     float v[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
     if constexpr (SKETCH) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q_sh[slot * D + 8 * l + e] = v[e];
+        for (int e = 0; e < 8; ++e) q_sh[slot * QS + 8 * l + e] = v[e];
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] *= rotation_sign(cb, 8 * l + e);
     wht8<LPV>(v, l);
-    if (active) {
+    if (active && blockIdx.y == 0) {
         float4* o = reinterpret_cast<float4*>(q_rot + static_cast<size_t>(vec) * D + 8 * l);
         o[0] = make_float4(v[0] * kInvSqrtD, v[1] * kInvSqrtD, v[2] * kInvSqrtD, v[3] * kInvSqrtD);
         o[1] = make_float4(v[4] * kInvSqrtD, v[5] * kInvSqrtD, v[6] * kInvSqrtD, v[7] * kInvSqrtD);
     }
     if constexpr (SKETCH) {
         __syncthreads();
-        const float4* qq = reinterpret_cast<const float4*>(q_sh + slot * D);
-        float outv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int i = 8 * l + e;
-            const float4* Srow = reinterpret_cast<const float4*>(S + static_cast<size_t>(i) * D);
-            float acc = 0.0f;
+        constexpr int RPW = sketch_rows_per_wg<D>();
+        const int i = blockIdx.y * RPW + tid / VPB, k = tid % VPB;
+        const float4* srow = reinterpret_cast<const float4*>(S + static_cast<size_t>(i) * D);
+        const float4* xq = reinterpret_cast<const float4*>(q_sh + k * QS);
+        float acc = 0.0f;
 #pragma unroll 8
-            for (int j = 0; j < D / 4; ++j) {
-                const float4 s4 = Srow[j], x4 = qq[j];
-                acc += s4.x * x4.x + s4.y * x4.y + s4.z * x4.z + s4.w * x4.w;
-            }
-            outv[e] = acc;
+        for (int j = 0; j < D / 4; ++j) {
+            const float4 s4 = srow[j], x4 = xq[j];
+            acc += s4.x * x4.x + s4.y * x4.y + s4.z * x4.z + s4.w * x4.w;
         }
-        if (active) {
-            float4* o = reinterpret_cast<float4*>(q_sk + static_cast<size_t>(vec) * D + 8 * l);
-            o[0] = make_float4(outv[0], outv[1], outv[2], outv[3]);
-            o[1] = make_float4(outv[4], outv[5], outv[6], outv[7]);
-        }
+        const int vk = blockIdx.x * VPB + k;
+        if (vk < nvec) q_sk[static_cast<size_t>(vk) * D + i] = acc;
     }
 }
 
@@ -761,15 +787,15 @@ int tq_rotate_sketch_query(const tq_layout* L, const tq_codebook* cbk, const flo
     const DevCodebook c = to_dev(*cbk);
     if (d == 128) {
         if (sketch)
-            hipLaunchKernelGGL((rotate_query_kernel<128, true>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
-                               q_sketch, S_dev, nvec, c);
+            hipLaunchKernelGGL((rotate_query_kernel<128, true>), dim3(grid, 128 / sketch_rows_per_wg<128>()),
+                               dim3(kWriteThreads), 0, stream, q, q_rot, q_sketch, S_dev, nvec, c);
         else
             hipLaunchKernelGGL((rotate_query_kernel<128, false>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
                                nullptr, nullptr, nvec, c);
     } else {
         if (sketch)
-            hipLaunchKernelGGL((rotate_query_kernel<256, true>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
-                               q_sketch, S_dev, nvec, c);
+            hipLaunchKernelGGL((rotate_query_kernel<256, true>), dim3(grid, 256 / sketch_rows_per_wg<256>()),
+                               dim3(kWriteThreads), 0, stream, q, q_rot, q_sketch, S_dev, nvec, c);
         else
             hipLaunchKernelGGL((rotate_query_kernel<256, false>), dim3(grid), dim3(kWriteThreads), 0, stream, q, q_rot,
                                nullptr, nullptr, nvec, c);
