@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "tq_internal.h"
 
@@ -65,6 +66,15 @@ __device__ __forceinline__ void wht_wave(float (&v)[DPL], int lane) {
             v[k] = upper ? (p - v[k]) : (v[k] + p);
         }
     }
+}
+
+template <int... I, typename F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
