@@ -1306,13 +1306,15 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 int auto_split_tokens(const tq_layout* L) {
     const long streams = static_cast<long>(L->batch) * L->n_kv_heads;
     const long max_splits = (L->capacity + kSplitQuantum - 1) / kSplitQuantum;
-    // PQ4 at d = 128 and G = 4 or 8 runs four splits per 16-wavefront workgroup, one workgroup
-    // per CU: about 1024 splits fill the chip in a single round.  The other kernels run one split
-    // per 4-wavefront workgroup and do best with two rounds of four workgroups per CU.
+    // Splits per launch, measured per kernel:
+    //   * PQ4 at d = 128, G = 4 or 8 (2:4-sparse kernel): four splits per 16-wavefront workgroup,
+    //     one workgroup per CU, so about 1024 splits fill the chip in a single round;
+    //   * PQ4 at d = 256, G = 4 or 8 (dense bf16 kernel): one split per workgroup, also best in a
+    //     single round of about 256 (c5: 48 us at 256 splits, 72 us at 1024);
+    //   * the generic kernel: about 2048 splits, two rounds of four workgroups per CU.
     const int G = L->n_kv_heads > 0 ? L->n_q_heads / L->n_kv_heads : 0;
-    const bool sparse_path = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && L->head_dim == 128 &&
-                             (G == 4 || G == 8);
-    const long target = sparse_path ? 1024 : 2048;
+    const bool pq4 = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && (G == 4 || G == 8);
+    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 256) : 2048;
     long want = (target + streams - 1) / streams;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
