@@ -145,6 +145,46 @@ def test_append_skips_out_of_range_rows():
         assert (pos in written) == (not np.all(kh[:, pos] == 0xAB))
 
 
+@pytest.mark.parametrize("name", ["c4", "c5", "c2"])
+def test_append_special_vectors(name):
+    """Zero vectors (decode to exactly 0), norms above the fp16 range (saturate),
+    tiny norms, and basis vectors n e_m, whose coordinates all land on the centroid
+    nearest 1/sqrt(d) with the signs of column m of the rotation, against the
+    oracle's encoding of the same rows."""
+    w = REDUCED[name]
+    st = P.Setup(w)
+    d = w.head_dim
+    L = st.layout(batch=1, capacity=64)
+    rng = np.random.default_rng(77)
+    rows = []
+    rows.append(np.zeros(d))
+    rows.append(rng.standard_normal(d) * (70000.0 / np.sqrt(d)) * 1.5)  # norm ~ 1e5 > 65504
+    rows.append(rng.standard_normal(d) * 1e-3)
+    for m in (0, 1, d // 2 + 3, d - 1):
+        e = np.zeros(d)
+        e[m] = 3.0
+        rows.append(e)
+    rows.append(-rows[-1])
+    x = np.stack(rows).astype(np.float16)
+    T = x.shape[0]
+    xh = np.repeat(x[:, None, :], w.n_kv_heads, axis=1)  # [T, Hkv, d]
+    dst = torch.arange(T, dtype=torch.int32, device="cuda")
+    kc = torch.zeros(tq.cache_bytes(L)[0], dtype=torch.uint8, device="cuda")
+    vc = torch.zeros(tq.cache_bytes(L)[1], dtype=torch.uint8, device="cuda")
+    xd = torch.from_numpy(xh).cuda()
+    tq.quantize_append(L, st.cbk, st.cbv, st.S_dev, xd, xd, dst, kc, vc)
+    torch.cuda.synchronize()
+    kh = kc.cpu().numpy().reshape(w.n_kv_heads, 64, st.vbk)
+    vh = vc.cpu().numpy().reshape(w.n_kv_heads, 64, st.vbv)
+    for tensor, cache in ((synth.K_TENSOR, kh), (synth.V_TENSOR, vh)):
+        enc = st.oracle_encode(tensor, x)
+        for h in range(w.n_kv_heads):
+            P.compare_write(st, tensor, cache[h, :T], enc)
+        dq = st.oracle_dequant(tensor, cache[0, :T])
+        assert np.all(dq[0] == 0.0)  # the zero vector
+        assert np.all(np.isfinite(dq))
+
+
 # ---------------------------------------------------------------------------
 # query rotation / sketch
 
