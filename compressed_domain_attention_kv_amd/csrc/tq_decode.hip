@@ -527,6 +527,30 @@ __device__ __forceinline__ void load_values(ValueTile<NTB, NB>& v, __amdgpu_buff
         }
 }
 
+// A wavefront's value tile of BYTES bytes, HBM -> LDS by buffer loads with an LDS
+// destination: whole kilobytes with 16 bytes per lane, the rest (128 or 256 bytes)
+// with 4 bytes per lane; with 128 bytes, lanes 32..63 repeat lanes 0..31 into the
+// 128 bytes after the tile, so nothing outside the tile is fetched.
+template <int BYTES>
+struct StageShape {
+    static constexpr int KB = BYTES / 1024, REST = BYTES % 1024;
+    static_assert(REST == 128 || REST == 256, "tile tails of 128 or 256 bytes");
+    static constexpr int SIZE = KB * 1024 + 256;  // LDS bytes per stage
+};
+
+template <int BYTES>
+__device__ __forceinline__ void stage_tile(__amdgpu_buffer_rsrc_t r, uint8_t* stage, int tile_off, int lane) {
+    using S = StageShape<BYTES>;
+    using lds_ptr = __attribute__((address_space(3))) void*;
+#pragma unroll
+    for (int k = 0; k < S::KB; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * k), 16, 16 * lane, tile_off + 1024 * k, 0,
+                                                 kStreamPolicy);
+    const int tl = S::REST == 256 ? lane : (lane & 31);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * S::KB), 4, 4 * tl, tile_off + 1024 * S::KB, 0,
+                                             kStreamPolicy);
+}
+
 // ---------------------------------------------------------------------------
 // PQ4 keys and values, G = 4 or 8 query heads per KV head, on the bf16 matrix
 // cores (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Every fp32 operand x
@@ -540,10 +564,11 @@ __device__ __forceinline__ void load_values(ValueTile<NTB, NB>& v, __amdgpu_buff
 //   values  D[(h,r)][n] += sum_{t,s} w_r[h][t] * c_s[vcode_t,8n+cb]
 //           with columns the 16 code words n of a 128-coordinate block, one
 //           accumulator per nibble position cb, k = (token, s).
-// Each lane loads exactly the code words it decodes straight from HBM into
-// registers (coalesced 16-byte and 4-byte loads); the next tile's keys are
-// requested as soon as the scores have consumed the current ones, the next
-// values after the value products.  Centroid pairs come from 32-entry LDS
+// Keys go straight from HBM into registers (lane (n, g): code words 4g..4g+3 of
+// token n), two register sets alternating between tiles; values go HBM -> LDS
+// into two stages per wavefront (distinct LDS objects, so the compiler's wait
+// for one stage ignores the other).  The next tile's keys and values are
+// requested at the start of the current tile.  Centroid pairs come from 32-entry LDS
 // tables (lookup = one SDWA mask and one ds_read_b32), the query pairs from
 // LDS (written once per split), and the softmax writes the weight pairs to
 // LDS in the A-operand layout of the value products.
@@ -553,7 +578,10 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     using C = Bf16Cfg<D, G, TT>;
     using SM = SmemBf16<D, G, TT>;
     constexpr int VB = C::VB, NB = C::NB, NTB = C::NTB, ROWS = C::ROWS;
+    constexpr int STAGE = StageShape<TT * VB>::SIZE;
     __shared__ __align__(16) SM sm;
+    __shared__ __align__(16) uint8_t vst0[kWaves][STAGE];
+    __shared__ __align__(16) uint8_t vst1[kWaves][STAGE];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -582,18 +610,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
     const int k_norm = n * VB;                   // key norm of token n
     const int k_word = n * VB + 4 + 16 * g;      // key words 4g..4g+3 of token n
-    const int v_norm = n * VB;                   // value norm of token n
-    const int v_word = 4 * g * VB + 4 + 4 * n;   // value word n of token 4g
     uint32_t* wa = sm.u.op.wa[w];
 
-    // the first tile of this wavefront in flight before anything else (tiles
-    // lie inside the cache: t0 + TT <= capacity because TT divides 64)
+    // the first tile of this wavefront in flight before anything else (tiles lie inside the
+    // cache: t0 + TT <= capacity because TT divides 64); a wavefront without tiles requests it
+    // through the empty resource, so the loads stay on one path
     int t0 = start + w * TT;
-    KeyTile<NTB, NB> kt;
+    KeyTile<NTB, NB> kt[2];
     ValueTile<NTB, NB> vt;
-    if (t0 < end) {
-        load_keys<VB>(kt, krs, k_norm, k_word, t0 * VB);
-        load_values<VB>(vt, vrs, v_norm, v_word, t0 * VB);
+    {
+        const bool any = t0 < end;
+        load_keys<VB>(kt[0], any ? krs : krs_none, k_norm, k_word, t0 * VB);
+        stage_tile<TT * VB>(any ? vrs : vrs_none, vst0[w], t0 * VB, lane);
     }
 
     if (tid < 32) {
@@ -648,12 +676,18 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const int wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
     constexpr int kStep = kWaves * TT;
 
-    for (; t0 < end; t0 += kStep) {
-        const int nv = min(TT, end - t0);
-        // the last tile reloads itself instead of reading past the split
+    // One tile at t0; P = tile parity selects the key register set and the value stage.
+    auto tile = [&](auto pc, const int t0) {
+        constexpr int P = decltype(pc)::value;
+        KeyTile<NTB, NB>& kc = kt[P];
+        const int nv = min(TT, end - t0);  // <= 0 for the odd tile after the last one
+        // past the last tile the requests go through the empty resource
         const bool more = t0 + kStep < end;
         const int t_next = more ? t0 + kStep : t0;
         const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
+        const uint8_t* vcur = P == 0 ? vst0[w] : vst1[w];
+        stage_tile<TT * VB>(vrn, P == 0 ? vst1[w] : vst0[w], t_next * VB, lane);
+        load_keys<VB>(kt[1 - P], krn, k_norm, k_word, t_next * VB);
 
         // ---- scores: column n = token 16 tb + n, k-group g = 32 coordinates per
         // block.  Job J = S * NTB + tb multiplies chunk S (nibbles 4(S&1)..+3 of
@@ -669,7 +703,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk) nk[tb][blk] = half_bits_to_float(kt.norm[tb][blk]);
+            for (int blk = 0; blk < NB; ++blk) nk[tb][blk] = half_bits_to_float(kc.norm[tb][blk]);
         {
             // QB query chunks in flight: chunk S is loaded at job S*NTB and last
             // read by the product of job S*NTB + NTB-1, kLookahead jobs later
@@ -681,7 +715,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
                 if constexpr (J < NJ) {
                     constexpr int S = J / NTB, TB = J % NTB, BLK = S / 8, CC = S % 8;
                     if constexpr (TB == 0) qk[S % QB] = sm.u.op.qa[S][lane];
-                    const uint32_t x = kt.w[TB][BLK][CC >> 1];
+                    const uint32_t x = kc.w[TB][BLK][CC >> 1];
                     decode_half<CC & 1>(x << 2, x >> 1, klo, khi, ring[J % R]);
                 }
                 if constexpr (J >= kLookahead) {
@@ -694,8 +728,17 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
                 __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
             });
         }
-        // the keys of this tile are consumed: request the next tile's
-        load_keys<VB>(kt, krn, k_norm, k_word, t_next * VB);
+        // this tile's value words and norms, from its stage
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) {
+                vt.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(vcur + (16 * tb + n) * VB + 68 * blk);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    vt.w[tb][blk][u] =
+                        *reinterpret_cast<const uint32_t*>(vcur + (16 * tb + 4 * g + u) * VB + 68 * blk + 4 + 4 * n);
+            }
 
         // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
         // (G is even, so both heads of a lane exist exactly when 2g < G)
@@ -808,9 +851,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             });
         }
         lds_order();
-        // the values of this tile are consumed: request the next tile's
-        load_values<VB>(vt, vrn, v_norm, v_word, t_next * VB);
+    };
+    // pairs of tiles, so that the parity is static; the second tile of the last pair may be
+    // empty (its weights are all zero, and the running maximum is finite by then)
+    for (; t0 < end; t0 += 2 * kStep) {
+        tile(std::integral_constant<int, 0>{}, t0);
+        tile(std::integral_constant<int, 1>{}, t0 + kStep);
     }
+    // the last requests (tiles past the end) land before the LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     // ---- merge the wavefronts of the workgroup and write the split record
 #pragma unroll
@@ -940,23 +989,6 @@ struct SmemSp {
     alignas(16) uint32_t wa[kPairWaves][C::WA];
 };
 
-// Value tiles through LDS (G = 4 with one table): a wavefront's 32-token value
-// tile is 2176 bytes; it is moved HBM -> LDS by three buffer loads with LDS
-// destination: two of 16 bytes per lane, and one of 4 bytes per lane in which
-// lanes 32..63 repeat the last 128 bytes (into stage bytes 2176..2303, never
-// read) so that no byte outside the tile is fetched.
-constexpr int kVStage = 2 * 1024 + 256;
-
-template <int VB>
-__device__ __forceinline__ void stage_values(__amdgpu_buffer_rsrc_t r, uint8_t* stage, int tile_off, int lane) {
-    using lds_ptr = __attribute__((address_space(3))) void*;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage), 16, 16 * lane, tile_off, 0, kStreamPolicy);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024), 16, 16 * lane, tile_off + 1024, 0,
-                                             kStreamPolicy);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 2048), 4, 4 * (lane & 31), tile_off + 2048, 0,
-                                             kStreamPolicy);
-}
-
 template <int G, bool VTAB>
 __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_partial_sparse_kernel(
     DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
@@ -966,12 +998,12 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     constexpr int D = C::D, VB = C::VB, NTB = C::NTB, RB = C::RB, TT = C::TT;
     // values through LDS where the two stages fit next to the table (G = 4, one table)
     constexpr bool VLDS = G == 4 && !VTAB;
-    static_assert(!VLDS || TT * VB <= 2 * 1024 + 128, "a value tile in the three stage loads");
+    constexpr int STAGE = StageShape<TT * VB>::SIZE;
     __shared__ __align__(16) SmemSp<G, VTAB> sm;
     // two stages in distinct LDS objects: the compiler's wait for one stage's loads then
     // ignores the other stage's
-    __shared__ __align__(16) uint8_t vst0[VLDS ? kPairWaves : 1][VLDS ? kVStage : 16];
-    __shared__ __align__(16) uint8_t vst1[VLDS ? kPairWaves : 1][VLDS ? kVStage : 16];
+    __shared__ __align__(16) uint8_t vst0[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
+    __shared__ __align__(16) uint8_t vst1[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
 
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1033,7 +1065,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         const bool any = t0 < end;
         const __amdgpu_buffer_rsrc_t kr0 = any ? krs : krs_none, vr0 = any ? vrs : vrs_none;
         load_keys<VB>(kt[0], kr0, k_norm, k_word, t0 * VB);
-        if constexpr (VLDS) stage_values<VB>(vr0, vst0[wi], t0 * VB, lane);
+        if constexpr (VLDS) stage_tile<TT * VB>(vr0, vst0[wi], t0 * VB, lane);
         else load_values<VB>(vt, vr0, v_norm, v_word, t0 * VB);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -1099,7 +1131,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
         const uint8_t* vcur = P == 0 ? vst0[wi] : vst1[wi];
         if constexpr (VLDS) {
-            stage_values<VB>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VB, lane);
+            stage_tile<TT * VB>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VB, lane);
             load_keys<VB>(kt[1 - P], krn, k_norm, k_word, t_next * VB);
         }
 
@@ -1309,12 +1341,12 @@ int auto_split_tokens(const tq_layout* L) {
     // Splits per launch, measured per kernel:
     //   * PQ4 at d = 128, G = 4 or 8 (2:4-sparse kernel): four splits per 16-wavefront workgroup,
     //     one workgroup per CU, so about 1024 splits fill the chip in a single round;
-    //   * PQ4 at d = 256, G = 4 or 8 (dense bf16 kernel): one split per workgroup, also best in a
-    //     single round of about 256 (c5: 48 us at 256 splits, 72 us at 1024);
+    //   * PQ4 at d = 256, G = 4 or 8 (dense bf16 kernel): one split per 4-wavefront workgroup,
+    //     best at two workgroups per CU (c5: 44 us at 512 splits, 47 at 256, 62 at 2048);
     //   * the generic kernel: about 2048 splits, two rounds of four workgroups per CU.
     const int G = L->n_kv_heads > 0 ? L->n_q_heads / L->n_kv_heads : 0;
     const bool pq4 = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && (G == 4 || G == 8);
-    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 256) : 2048;
+    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 512) : 2048;
     long want = (target + streams - 1) / streams;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
