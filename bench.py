@@ -462,7 +462,8 @@ SWEEP_NOTE = ("per-kernel times of a workload other than the headline one: decod
 
 def bench_sweep(args):
     """The write path at its bulk size (c5 prefill: 131,072 tokens x 4 KV heads at d 256) and the
-    decode of c1, c2, c3 and c5 at full size, each timed on its own; one JSON line per item."""
+    decode of c1, c2, c3 and c5 at full size (and c2's shapes with PQ4 values), each timed on its
+    own; one JSON line per item."""
     import numpy as np
     import torch
 
@@ -529,7 +530,9 @@ def bench_sweep(args):
     torch.cuda.synchronize()
 
     # ---- decode of the other workloads (c5 reads the prefill bytes as [32][2][8192])
-    for w in (synth.C1, synth.C2, synth.C3, synth.C5):
+    # the asymmetric pair of the survey's next steps: turbo3-style keys with 4-bit values, at c2's shapes
+    asym = synth.scaled(synth.C2, name="c2 with PQ3 keys and PQ4 values", v_format=synth.PQ4, v_bits=4)
+    for w in (synth.C1, synth.C2, asym, synth.C3, synth.C5):
         B, Hq, Hkv, d, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
         L = tq.Layout(B, Hq, Hkv, d, w.capacity, w.k_format, w.v_format)
         if w is synth.C5:
