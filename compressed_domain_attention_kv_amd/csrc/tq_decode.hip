@@ -399,6 +399,18 @@ __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// An LDS word or byte offset that the optimizer keeps whole.  The LDS lowering gives
+// an access an alias scope only when its address lies a few steps below the LDS
+// variable; an access built from more steps goes unscoped, and the compiler then
+// makes it wait for every buffer-to-LDS load still in flight (this tile's value
+// stage included).  Addresses written as array + lds_offset(o) (+ a constant) stay
+// shallow.  ON = false passes o through (kernels without buffer-to-LDS loads).
+template <bool ON = true>
+__device__ __forceinline__ uint32_t lds_offset(uint32_t o) {
+    if constexpr (ON) asm("" : "+v"(o));
+    return o;
+}
+
 // Online-softmax rescale threshold (log2 units): the running reference m is
 // moved to the maximum only when some score exceeds m + kRescaleSlack, so
 // weights 2^(s - m) stay below 2^kRescaleSlack and a tile without a new
@@ -672,8 +684,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const char* vlo = reinterpret_cast<const char*>(sm.vlo);
     const char* vhi = reinterpret_cast<const char*>(sm.vhi);
     // value-product A operand of this lane: row n (zero row when n >= ROWS), tokens 4g..4g+3
-    const uint32_t* wa_rd = n < ROWS ? wa + n * 16 + 4 * g : wa + C::WA - 16 + 4 * g;
-    const int wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
+    const uint32_t rd_lane = n < ROWS ? n * 16 + 4 * g : C::WA - 16 + 4 * g;
+    const uint32_t wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
+    const uint32_t w_lane = 4 * g * 16 + n;              // this lane's weight word in block 0
+    // this lane's value norm and words in a stage (token n; tokens 4g.., word n)
+    const uint32_t v_norm_lane = lds_offset(n * VB), v_word_lane = lds_offset(4 * g * VB + 4 + 4 * n);
     constexpr int kStep = kWaves * TT;
 
     // One tile at t0; P = tile parity selects the key register set and the value stage.
@@ -733,11 +748,11 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) {
-                vt.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(vcur + (16 * tb + n) * VB + 68 * blk);
+                vt.norm[tb][blk] = *reinterpret_cast<const uint16_t*>(vcur + v_norm_lane + 16 * tb * VB + 68 * blk);
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
                     vt.w[tb][blk][u] =
-                        *reinterpret_cast<const uint32_t*>(vcur + (16 * tb + 4 * g + u) * VB + 68 * blk + 4 + 4 * n);
+                        *reinterpret_cast<const uint32_t*>(vcur + v_word_lane + (16 * tb + u) * VB + 68 * blk);
             }
 
         // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
@@ -809,7 +824,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
                         const float wt = pw[tb][e][blk];
                         const uint32_t bits = __float_as_uint(wt);
                         const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                        uint32_t* dst = wa + ((blk * NTB + tb) * ROWS + 4 * g + 2 * e) * 16 + n;
+                        uint32_t* dst = wa + lds_offset(w_lane + ((blk * NTB + tb) * ROWS + 2 * e) * 16);
                         dst[0] = dup_hi16(bits);                 // row (h, hi)
                         dst[16] = dup_hi16(__float_as_uint(lo));  // row (h, lo)
                     }
@@ -826,7 +841,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int blk = 0; blk < NB; ++blk)
-                    av[tb][blk] = *reinterpret_cast<const u32x4*>(wa_rd + (blk * NTB + tb) * wa_step);
+                    av[tb][blk] = *reinterpret_cast<const u32x4*>(wa + lds_offset(rd_lane + (blk * NTB + tb) * wa_step));
             constexpr int NJ = NTB * NB * 8, R = kLookahead + 1;
             uint32_t ring[R][4];
             static_for<NJ + kLookahead>([&](auto jc) {
@@ -1113,8 +1128,8 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int i = 0; i < 4; ++i) addr[i] = (lane & 31) * 8u;  // bits 8..15 take the code byte
     // weights: token n is written to k-group sp_group(n / 4, n % 4) of [tb][head][r]; the value
     // A operand of lane (row n, group g) is the four groups 4g .. 4g+3 of its (head, r)
-    const int w_slot = sp_group(n >> 2, n & 3);
-    const uint32_t* wa_rd = wa + ((n >> 2) * 2 + ((n >> 1) & 1)) * 16 + 4 * g;
+    const uint32_t w_lane = g * 32 + sp_group(n >> 2, n & 3);
+    const uint32_t rd_lane = ((n >> 2) * 2 + ((n >> 1) & 1)) * 16 + 4 * g;
     constexpr int kStep = kWaves * TT;
     constexpr int LA = kSpLookahead, R = LA + 1;
 
@@ -1237,7 +1252,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 const float wt = p * nvn;
                 const uint32_t bits = __float_as_uint(wt);
                 const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                uint32_t* dst = wa + (tb * G + 4 * rb + g) * 32 + w_slot;
+                uint32_t* dst = wa + lds_offset<VLDS>(w_lane + (tb * G + 4 * rb) * 32);
                 dst[0] = dup_hi16(bits);
                 dst[16] = dup_hi16(__float_as_uint(lo));
             }
@@ -1251,7 +1266,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    av[tb][rb] = *reinterpret_cast<const u32x4*>(wa_rd + (tb * G + 4 * rb) * 32);
+                    av[tb][rb] = *reinterpret_cast<const u32x4*>(wa + lds_offset<VLDS>(rd_lane + (tb * G + 4 * rb) * 32));
             constexpr int NJ = 4 * NTB;
             u32x8 ring[R];
             static_for<NJ + LA>([&](auto jc) {
