@@ -463,7 +463,7 @@ SWEEP_NOTE = ("per-kernel times of a workload other than the headline one: decod
 def bench_sweep(args):
     """The write path at its bulk size (c5 prefill: 131,072 tokens x 4 KV heads at d 256) and the
     decode of c1, c2, c3 and c5 at full size (and c2's shapes with PQ4 values), each timed on its
-    own; one JSON line per item."""
+    own, plus sparse V against the plain decode at c3 and c5; one JSON line per item."""
     import numpy as np
     import torch
 
@@ -579,6 +579,22 @@ def bench_sweep(args):
              bytes=alg, useful_tflops=2 * fma / (part_ms * 1e-3) / 1e12,
              roofline={"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                        "frac": gbs / HBM_PEAK_GBS})
+        if w is synth.C3 or w is synth.C5:
+            # sparse V against the plain call on the same cache, with queries four times as sharp
+            # (logit spread about 8): most tokens then sit far below their wavefront's running
+            # maximum, the case the threshold is for
+            qs = q * 4.0
+            qs_rot = torch.empty_like(qs)
+            qs_sk = torch.empty_like(qs) if S is not None else None
+            tq.rotate_sketch_query(L, cbk, S, qs, qs_rot, qs_sk)
+            tau = 1e-3
+            plain_ms = per_call_ms(lambda: tq.decode_partial(L, cbk, cbv, qs_rot, qs_sk, kc, vc, seq, ws), reps)
+            sv_ms = per_call_ms(lambda: tq.decode_partial_sparse_v(L, cbk, cbv, qs_rot, qs_sk, kc, vc, seq, ws, tau),
+                                reps)
+            emit(f"{w.name} decode, sparse V", kernel="decode_partial vs decode_partial_sparse_v",
+                 workload=f"as the {w.name} decode line, queries scaled by 4", threshold=tau,
+                 us={"decode_partial": plain_ms * 1e3, "decode_partial_sparse_v": sv_ms * 1e3},
+                 speedup=plain_ms / sv_ms)
         del kc, vc
         torch.cuda.synchronize()
 

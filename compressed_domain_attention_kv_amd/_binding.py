@@ -109,6 +109,8 @@ lib.tq_decode_partial.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P,
 lib.tq_decode_partial_timed.restype = _I
 lib.tq_decode_partial_timed.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P, _P, _P]
 lib.tq_decode_combine.restype = _I
+lib.tq_decode_partial_sparse_v.restype = _I
+lib.tq_decode_partial_sparse_v.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, ctypes.c_float, _P, _SZ, _P]
 lib.tq_decode_combine.argtypes = [_PL, _PC, _I, _P, _SZ, _P, _P]
 lib.tq_ring_bytes.restype = _SZ
 lib.tq_ring_bytes.argtypes = [_PL, _I]
@@ -224,6 +226,15 @@ def decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, ws,
         start, stop = events
         _check(lib.tq_decode_partial_timed(*args, ctypes.c_void_p(start), ctypes.c_void_p(stop)),
                "tq_decode_partial_timed")
+
+
+def decode_partial_sparse_v(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, ws, v_threshold,
+                            scores=None, split_tokens=0, stream=None):
+    _check(lib.tq_decode_partial_sparse_v(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), _ptr(q_rot),
+                                          _ptr(q_sketch), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                          _ptr(scores), split_tokens, float(v_threshold), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(stream)),
+           "tq_decode_partial_sparse_v")
 
 
 def decode_combine(L, cbv, ws, out, split_tokens=0, stream=None):

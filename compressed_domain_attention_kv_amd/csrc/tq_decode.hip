@@ -49,6 +49,10 @@ struct DecodeArgs {
     int capacity;
     int splits;
     int split_len;
+    // Sparse V: a token whose weight against the running maximum, e^(s - m), is below
+    // v_skip adds nothing to the value sum (its weight still enters the denominator), and
+    // value work is skipped where no weight survives.  0 keeps every value.
+    float v_skip;
 };
 
 // byte k of a register-resident little-endian byte run (k known at compile time after unrolling)
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
                 m_run[g] = mn;
 #pragma unroll
                 for (int k = 0; k < DPL; ++k) acc[g][k] *= alpha;
-                pw[lane * G + g] = p;
+                pw[lane * G + g] = p >= a.v_skip ? p : 0.0f;
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -265,8 +269,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
             for (int i = 0; i < nv; ++i) {
                 const uint8_t* vb = vt + i * VBV;
                 float wgt[G];
+                bool keep = false;
 #pragma unroll
-                for (int g = 0; g < G; ++g) wgt[g] = pw[i * G + g];
+                for (int g = 0; g < G; ++g) {
+                    wgt[g] = pw[i * G + g];
+                    keep = keep || wgt[g] != 0.0f;
+                }
+                if (!keep) continue;  // the same for every lane: no value to decode
                 float val[DPL];
                 if constexpr (VF == TQ_FMT_PQ4) {
                     constexpr int LPB = 128 / DPL;  // lanes per 128-block
@@ -684,6 +693,9 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const char* vlo = reinterpret_cast<const char*>(sm.vlo);
     const char* vhi = reinterpret_cast<const char*>(sm.vhi);
     // value-product A operand of this lane: row n (zero row when n >= ROWS), tokens 4g..4g+3
+    // with sparse V the reference follows the maximum exactly, so weights against it are as
+    // small as they can be and more values drop
+    const float slack = a.v_skip > 0.0f ? 0.0f : kRescaleSlack;
     const uint32_t rd_lane = n < ROWS ? n * 16 + 4 * g : C::WA - 16 + 4 * g;
     const uint32_t wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
     const uint32_t w_lane = 4 * g * 16 + n;              // this lane's weight word in block 0
@@ -781,7 +793,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
                         a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 2 * g + e) * a.capacity + t0 + 16 * tb + n] =
                             tv[tb][e] * kLn2;
         }
-        if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + kRescaleSlack || mx[1] > m_run[1] + kRescaleSlack) != 0) {
+        if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + slack || mx[1] > m_run[1] + slack) != 0) {
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const float mn = fmaxf(m_run[e], row16_max(mx[e]));
@@ -798,6 +810,7 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             }
         }
         float pw[NTB][2][NB];
+        bool keep = false;
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             const bool tok = 16 * tb + n < nv;
@@ -810,10 +823,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
                 for (int e = 0; e < 2; ++e) {
                     const float p = __builtin_amdgcn_exp2f(tv[tb][e] - m_run[e]);  // 0 for invalid tokens and rows
                     if (blk == 0) l_run[e] += p;
-                    pw[tb][e][blk] = p * nvn;
+                    pw[tb][e][blk] = (p >= a.v_skip ? p : 0.0f) * nvn;
+                    keep = keep || pw[tb][e][blk] != 0.0f;
                 }
             }
         }
+        // the value products of the tile only where some weight is left (uniform)
+        if (__builtin_amdgcn_ballot_w64(keep) == 0) return;
         if (live) {
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
@@ -1128,6 +1144,10 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int i = 0; i < 4; ++i) addr[i] = (lane & 31) * 8u;  // bits 8..15 take the code byte
     // weights: token n is written to k-group sp_group(n / 4, n % 4) of [tb][head][r]; the value
     // A operand of lane (row n, group g) is the four groups 4g .. 4g+3 of its (head, r)
+    // with sparse V the reference follows the maximum exactly, so weights against it are as
+    // small as they can be and more values drop (not in the kernels that hold the values in
+    // registers: the register costs them a spill)
+    const float slack = VLDS && a.v_skip > 0.0f ? 0.0f : kRescaleSlack;
     const uint32_t w_lane = g * 32 + sp_group(n >> 2, n & 3);
     const uint32_t rd_lane = ((n >> 2) * 2 + ((n >> 1) & 1)) * 16 + 4 * g;
     constexpr int kStep = kWaves * TT;
@@ -1229,7 +1249,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         }
         bool grow = false;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) grow = grow || mx[rb] > m_run[rb] + kRescaleSlack;
+        for (int rb = 0; rb < RB; ++rb) grow = grow || mx[rb] > m_run[rb] + slack;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -1241,6 +1261,8 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 m_run[rb] = mn;
             }
         }
+        float wts[NTB][RB];
+        bool keep = false;
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             // rows past the sequence end hold whatever the cache held: weight exactly 0
@@ -1249,51 +1271,64 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int rb = 0; rb < RB; ++rb) {
                 const float p = __builtin_amdgcn_exp2f(tv[tb][rb] - m_run[rb]);
                 l_run[rb] += p;
-                const float wt = p * nvn;
-                const uint32_t bits = __float_as_uint(wt);
-                const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                uint32_t* dst = wa + lds_offset<VLDS>(w_lane + (tb * G + 4 * rb) * 32);
-                dst[0] = dup_hi16(bits);
-                dst[16] = dup_hi16(__float_as_uint(lo));
+                wts[tb][rb] = (p >= a.v_skip ? p : 0.0f) * nvn;
+                keep = keep || wts[tb][rb] != 0.0f;
             }
         }
-        lds_order();
-
-        // ---- values: job J = tb * 4 + Q reads byte Q of code word n of tokens 4g .. 4g+3
-        {
-            u32x4 av[NTB][RB];
+        // the value products of the tile only where some weight is left (uniform); the
+        // kernels that load values into registers keep one path (the branch costs them
+        // registers)
+        if (!VLDS || __builtin_amdgcn_ballot_w64(keep) != 0) {
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
+            for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    av[tb][rb] = *reinterpret_cast<const u32x4*>(wa + lds_offset<VLDS>(rd_lane + (tb * G + 4 * rb) * 32));
-            constexpr int NJ = 4 * NTB;
-            u32x8 ring[R];
-            static_for<NJ + LA>([&](auto jc) {
-                constexpr int J = decltype(jc)::value;
-                if constexpr (J < NJ) {
-                    constexpr int TB = J / 4, Q = J % 4;
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB][0][u]);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(vtab + addr[u]);
-                        ring[J % R][2 * u] = v.x;
-                        ring[J % R][2 * u + 1] = v.y;
-                    }
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float wt = wts[tb][rb];
+                    const uint32_t bits = __float_as_uint(wt);
+                    const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
+                    uint32_t* dst = wa + lds_offset<VLDS>(w_lane + (tb * G + 4 * rb) * 32);
+                    dst[0] = dup_hi16(bits);
+                    dst[16] = dup_hi16(__float_as_uint(lo));
                 }
-                if constexpr (J >= LA) {
-                    constexpr int M = J - LA, TB = M / 4, Q = M % 4;
-                    const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
+            }
+            lds_order();
+
+            // ---- values: job J = tb * 4 + Q reads byte Q of code word n of tokens 4g .. 4g+3
+            {
+                u32x4 av[NTB][RB];
+#pragma unroll
+                for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
-                        acc[rb][Q] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av[TB][rb]), bop,
-                                                                              acc[rb][Q], sp_idx, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            });
+                        av[tb][rb] = *reinterpret_cast<const u32x4*>(wa + lds_offset<VLDS>(rd_lane + (tb * G + 4 * rb) * 32));
+                constexpr int NJ = 4 * NTB;
+                u32x8 ring[R];
+                static_for<NJ + LA>([&](auto jc) {
+                    constexpr int J = decltype(jc)::value;
+                    if constexpr (J < NJ) {
+                        constexpr int TB = J / 4, Q = J % 4;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB][0][u]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) {
+                            const uint2 v = *reinterpret_cast<const uint2*>(vtab + addr[u]);
+                            ring[J % R][2 * u] = v.x;
+                            ring[J % R][2 * u + 1] = v.y;
+                        }
+                    }
+                    if constexpr (J >= LA) {
+                        constexpr int M = J - LA, TB = M / 4, Q = M % 4;
+                        const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb)
+                            acc[rb][Q] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av[TB][rb]), bop,
+                                                                                  acc[rb][Q], sp_idx, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            }
+            lds_order();
         }
-        lds_order();
         if constexpr (!VLDS) load_values<VB>(vt, vrn, v_norm, v_word, t_next * VB);
     };
     if constexpr (VLDS) {
@@ -1509,7 +1544,8 @@ namespace {
 // Split records of the compressed cache.
 int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
                    const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream) {
+                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream,
+                   float v_skip = 0.0f) {
     int st = check_decode(L, cbk, cbv);
     if (st != TQ_OK) return st;
     int len = 0;
@@ -1520,6 +1556,7 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(ws, 16) || !aligned(q_rot, 4) ||
         !aligned(seq_lens, 4) || (scores && !aligned(scores, 4)) || (q_sketch && !aligned(q_sketch, 4)))
         return TQ_ERR_INVALID;
+    if (!(v_skip >= 0.0f && v_skip <= 1.0f)) return TQ_ERR_INVALID;  // NaN fails too
     if (ws_bytes < workspace_bytes(L, split_tokens)) return TQ_ERR_WORKSPACE;
     DecodeArgs a{};
     a.q_rot = q_rot;
@@ -1536,6 +1573,7 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
     a.capacity = L->capacity;
     a.splits = splits;
     a.split_len = len;
+    a.v_skip = v_skip;
     const int kf = L->k_format, vf = L->v_format;
     if (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ4, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ3>(a, L, *cbk, *cbv, stream);
@@ -1564,6 +1602,14 @@ int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq
     if (!start || !stop) return TQ_ERR_INVALID;
     return tq::decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
                               ws_bytes, tq::Launch{stream, start, stop});
+}
+
+int tq_decode_partial_sparse_v(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                               const float* q_sketch, const void* k_cache, const void* v_cache,
+                               const int32_t* seq_lens, float* scores, int split_tokens, float v_threshold, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    return tq::decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
+                              ws_bytes, tq::Launch{stream, nullptr, nullptr}, v_threshold);
 }
 
 int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_tokens, const void* ws, size_t ws_bytes,

@@ -261,6 +261,28 @@ int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq
                             int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop);
 
+/* Sparse V.  [P1] "turbo4 post-mortem", section 9 (current state) lists a
+ * sparse-V mode as active alongside the 4-bit format; the page gives no rule
+ * or threshold.  Reading taken here: the value of a token is skipped when its
+ * weight against the running maximum is negligible.  Exactly: with m the
+ * running reference maximum of the wavefront that processes token t (never
+ * above the split's true maximum), the token adds its weight e^(s_t - m) to
+ * the denominator always, and its value times that weight to the accumulator
+ * only when e^(s_t - m) >= v_threshold; a tile of tokens none of whose values
+ * survive skips its value decode and products.  Since m is at most the row
+ * maximum M, a skipped token has softmax weight p_t < v_threshold, so every
+ * output coordinate j moves by at most sum_{t: p_t < v_threshold} p_t |v_tj|;
+ * tokens with p_t >= v_threshold are always kept.  Which tokens below the
+ * threshold are skipped depends on the order the kernel visits them.
+ * Arguments, layout and errors as tq_decode_partial; v_threshold in [0, 1]
+ * (else TQ_ERR_INVALID, NaN included).  v_threshold = 0 gives the results of
+ * tq_decode_partial bit for bit.  The records feed tq_decode_combine.     */
+int tq_decode_partial_sparse_v(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
+                               const float* q_rot, const float* q_sketch, const void* k_cache,
+                               const void* v_cache, const int32_t* seq_lens, float* scores,
+                               int split_tokens, float v_threshold, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
 /* Second half: merge the split records (m = max m_p, l = sum l_p 2^(m_p-m),
  * acc = sum acc_p 2^(m_p - m)), normalize o = acc / l (o = 0 when l = 0) and
  * rotate back with the V codebook's signs for PQ4/PQ3 values.              */

@@ -14,6 +14,13 @@ Grouped-query attention: query head g reads KV head g // (Hq / Hkv).
 ``hybrid_attention`` is the same softmax over the compressed history and the
 exact tokens of the capture ring taken together.
 
+Sparse V ("turbo4 post-mortem", section 9, lists a sparse-V mode without a rule
+or threshold; the reading here: a token's value is left out when its weight is
+negligible).  ``sparse_v_output`` is the softmax with every token in the
+denominator but only a chosen set of tokens in the value sum;
+``sparse_v_interval`` bounds, per output coordinate, every result that keeps
+at least the tokens whose softmax weight reaches the threshold.
+
 Besides the plain path, two helpers restate the identities the fast path
 relies on, so that tests can pin them:
 
@@ -128,3 +135,40 @@ def combine_records(recs):
     L = sum(wi * r[1] for wi, r in zip(w, recs))
     acc = sum(wi * r[2] for wi, r in zip(w, recs))
     return acc / L
+
+
+def sparse_v_output(q, khat, vhat, keep):
+    """Softmax attention of one query in which every token's weight enters the
+    denominator but only tokens with keep[t] add their value:
+    o = sum_{t kept} p_t vhat_t with p = softmax(q khat^T / sqrt(d))."""
+    q = np.asarray(q, dtype=np.float64)
+    if khat.shape[0] == 0:
+        return np.zeros(vhat.shape[1])
+    s = khat @ q / np.sqrt(q.shape[-1])
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    return (p * np.asarray(keep, dtype=np.float64)) @ vhat
+
+
+def sparse_v_interval(q, khat, vhat, tau, margin=0.0):
+    """Per-coordinate range [lo, hi] of sparse_v_output over every keep set that
+    contains each token with p_t >= tau (1 + margin), the others optional.
+
+    A token left out by the threshold rule has weight e^(s_t - m) < tau against
+    a running maximum m that never exceeds the true maximum M, so its softmax
+    weight p_t <= e^(s_t - M) < tau: such sets cover every visiting order.
+    margin > 0 also lets tokens just above tau drop, for a decision taken in
+    finite precision.  Coordinate j: lo = sure_j + sum_opt min(0, p_t v_tj),
+    hi = sure_j + sum_opt max(0, p_t v_tj)."""
+    q = np.asarray(q, dtype=np.float64)
+    if khat.shape[0] == 0:
+        z = np.zeros(vhat.shape[1])
+        return z, z.copy()
+    s = khat @ q / np.sqrt(q.shape[-1])
+    p = np.exp(s - s.max())
+    p /= p.sum()
+    sure = p >= tau * (1.0 + margin)
+    contrib = p[:, None] * np.asarray(vhat, dtype=np.float64)
+    base = contrib[sure].sum(axis=0)
+    opt = contrib[~sure]
+    return base + np.minimum(opt, 0.0).sum(axis=0), base + np.maximum(opt, 0.0).sum(axis=0)

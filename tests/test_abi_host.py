@@ -135,6 +135,12 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert tq.lib.tq_decode_partial_timed(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
                                           need - 1, None, fake, fake) == -3
     assert tq.lib.tq_quantize_rotated(9, r(cb), None, fake, fake, 1, fake, None) == -2
+    # the sparse-V variant checks its arguments like the plain call, and the threshold range
+    sv = tq.lib.tq_decode_partial_sparse_v
+    assert sv(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, 0.0, fake, need - 1, None) == -3
+    assert sv(r(L), r(cb), r(cb), fake, None, misaligned, fake, fake, None, 0, 0.0, fake, need, None) == -1
+    for bad in (-1e-3, 1.0001, float("nan"), float("inf")):
+        assert sv(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, bad, fake, need, None) == -1
     assert tq.strerror(-3).startswith("workspace")
 
 

@@ -153,3 +153,73 @@ def test_tq3k_key_inner_product_unbiased_over_qjl_matrices():
     mse_only = float(np.float16(n)) * rotation.unrotate(
         t.centroids.astype(np.float64)[F.encode_tq3k(x, t, s, S).idx], s)[0] @ q
     assert abs(mse_only - target) > 3 * vals.std() / np.sqrt(len(vals))
+
+
+# ---------------------------------------------------------------------------
+# sparse V
+
+
+def _tiny(n, d, seed, peak=0.0):
+    rng = np.random.default_rng(seed)
+    k = rng.normal(size=(n, d))
+    v = rng.normal(size=(n, d))
+    q = rng.normal(size=d) + peak * k[0]
+    return q, k, v
+
+
+def test_sparse_v_output_keep_all_and_keep_none():
+    q, k, v = _tiny(9, 8, 1)
+    o, _ = A.softmax_attention(q, k, v)
+    assert np.allclose(A.sparse_v_output(q, k, v, np.ones(9, bool)), o, rtol=0, atol=1e-15)
+    assert np.all(A.sparse_v_output(q, k, v, np.zeros(9, bool)) == 0.0)
+
+
+def test_sparse_v_output_is_softmax_weighted_partial_sum():
+    """Against scipy's softmax: the kept tokens' p_t v_t summed, by a loop."""
+    q, k, v = _tiny(7, 4, 2)
+    keep = np.array([1, 0, 1, 1, 0, 0, 1], bool)
+    p = softmax(k @ q / 2.0)  # sqrt(4)
+    want = np.zeros(4)
+    for t in range(7):
+        if keep[t]:
+            want += p[t] * v[t]
+    assert np.allclose(A.sparse_v_output(q, k, v, keep), want, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("seed,tau,peak", [(3, 0.05, 0.0), (4, 0.1, 1.0), (5, 0.02, 2.0), (6, 0.2, 3.0)])
+def test_sparse_v_interval_is_attained_by_brute_force(seed, tau, peak):
+    """Every keep set that holds the tokens with p >= tau: its output lies in
+    [lo, hi], and per coordinate some such set reaches lo and another hi."""
+    n, d = 10, 6
+    q, k, v = _tiny(n, d, seed, peak)
+    lo, hi = A.sparse_v_interval(q, k, v, tau)
+    p = softmax(k @ q / math.sqrt(d))
+    must = p >= tau
+    opt = np.flatnonzero(~must)
+    assert 0 < len(opt) < n
+    outs = []
+    for mask in range(1 << len(opt)):
+        keep = must.copy()
+        for i, t in enumerate(opt):
+            if mask >> i & 1:
+                keep[t] = True
+        outs.append(A.sparse_v_output(q, k, v, keep))
+    outs = np.array(outs)
+    assert np.all(outs >= lo - 1e-14) and np.all(outs <= hi + 1e-14)
+    assert np.allclose(outs.min(axis=0), lo, atol=1e-14) and np.allclose(outs.max(axis=0), hi, atol=1e-14)
+
+
+def test_sparse_v_interval_threshold_zero_is_exact_attention():
+    q, k, v = _tiny(12, 5, 7)
+    o, _ = A.softmax_attention(q, k, v)
+    lo, hi = A.sparse_v_interval(q, k, v, 0.0)
+    assert np.allclose(lo, o, atol=1e-15) and np.allclose(hi, o, atol=1e-15)
+
+
+def test_sparse_v_interval_margin_widens_only():
+    q, k, v = _tiny(10, 6, 8, 1.5)
+    lo0, hi0 = A.sparse_v_interval(q, k, v, 0.05)
+    lo1, hi1 = A.sparse_v_interval(q, k, v, 0.05, margin=10.0)
+    assert np.all(lo1 <= lo0 + 1e-15) and np.all(hi1 >= hi0 - 1e-15)
+    o, _ = A.softmax_attention(q, k, v)
+    assert np.all(lo0 <= o + 1e-14) and np.all(o <= hi0 + 1e-14)
