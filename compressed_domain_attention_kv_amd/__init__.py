@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     decode_combine,
     decode_hybrid_workspace_bytes,
     decode_partial,
+    decode_partial_from_query,
     decode_partial_sparse_v,
     decode_splits,
     decode_workspace_bytes,

@@ -53,6 +53,8 @@ struct DecodeArgs {
     // v_skip adds nothing to the value sum (its weight still enters the denominator), and
     // value work is skipped where no weight survives.  0 keeps every value.
     float v_skip;
+    // the unrotated query [B][Hq][D], when the kernel rotates it itself (q_rot unused)
+    const float* q_raw;
 };
 
 // byte k of a register-resident little-endian byte run (k known at compile time after unrolling)
@@ -1035,6 +1037,8 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     // ignores the other stage's
     __shared__ __align__(16) uint8_t vst0[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
     __shared__ __align__(16) uint8_t vst1[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
+    // the rotated query heads of the group, when the kernel rotates the query itself
+    __shared__ __align__(16) float qrot_sh[G][D];
 
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1075,9 +1079,25 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int k = 0; k < 8; ++k) cv_hi[k] = cbv.centroids[hi_base + 2 * k];
     }
+    // an unrotated query (values through LDS only): wavefronts wi < G / 4 rotate it below,
+    // four heads each, with the arithmetic of the query rotation kernel (16 lanes per head,
+    // 8 coordinates per lane: signs, Walsh-Hadamard butterflies, 1/sqrt(d)), so the rotated
+    // values are the same bits.  The query and its sign word are read here, before the tiles.
+    const bool raw = VLDS && a.q_raw != nullptr;  // uniform
+    const int rh = 4 * wi + (lane >> 4), rl = lane & 15;
+    float rv[8];
+    uint32_t rsign = 0;
+    if (raw && wi < G / 4) {
+        const float4* src =
+            reinterpret_cast<const float4*>(a.q_raw + (static_cast<size_t>(b) * a.hq + hq0 + rh) * D + 8 * rl);
+        const float4 p0 = src[0], p1 = src[1];
+        rv[0] = p0.x; rv[1] = p0.y; rv[2] = p0.z; rv[3] = p0.w;
+        rv[4] = p1.x; rv[5] = p1.y; rv[6] = p1.z; rv[7] = p1.w;
+        rsign = cbk.sign_bits[rl >> 2] >> (8 * (rl & 3));  // bits of coordinates 8 rl .. 8 rl + 7
+    }
     float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int qrb = wi / 4, qI = wi % 4, qhh = 4 * qrb + (n >> 2), qr = (n >> 1) & 1, qp = n & 1;
-    if (wi < 4 * RB) {
+    if (!raw && wi < 4 * RB) {
         const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + qhh) * D;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1105,6 +1125,23 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     for (int k = 0; k < 8; ++k) {
         sm.u.op.table[tid + 1024 * k] = make_uint2(bf16_split(ck_lo), bf16_split(ck_hi[k]));
         if constexpr (VTAB) sm.u.op.vtable[tid + 1024 * k] = make_uint2(bf16_split(cv_lo), bf16_split(cv_hi[k]));
+    }
+    if (raw) {
+        if (wi < G / 4) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rv[e] *= ((rsign >> e) & 1u) ? -1.0f : 1.0f;
+            wht8<16>(rv, rl);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qrot_sh[rh][8 * rl + e] = rv[e] * 0.08838834764831845f;  // 1/sqrt(128)
+        }
+        __syncthreads();
+        if (wi < 4 * RB) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int gd = 4 * g + q;
+                qv[q] = qrot_sh[qhh][2 * (16 * sp_lane_group(gd) + 4 * qI + sp_quad(gd)) + qp];
+            }
+        }
     }
     if (wi < 4 * RB) {
         const float qscale = kLog2e / sqrtf(static_cast<float>(D));
@@ -1454,6 +1491,14 @@ bool same_centroids(const tq_codebook& x, const tq_codebook& y) {
     return true;
 }
 
+// The kernel that rotates an unrotated query in its prologue: PQ4 keys and values at d 128,
+// four query heads per KV head, one centroid table (the values staged through LDS).
+bool rotates_in_kernel(const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv) {
+    return L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && L->head_dim == 128 &&
+           L->n_q_heads == 4 * L->n_kv_heads && static_cast<size_t>(L->capacity) * 68 <= 0x7FFFFFFFu &&
+           same_centroids(cbk, cbv);
+}
+
 template <int D, int G>
 int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                         const Launch& l) {
@@ -1541,11 +1586,10 @@ size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens) {
 namespace tq {
 namespace {
 
-// Split records of the compressed cache.
-int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
-                   const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
-                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream,
-                   float v_skip = 0.0f) {
+// Checks every argument of a partial call and fills its kernel arguments; nothing is launched.
+int partial_args(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                 const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                 float* scores, int split_tokens, void* ws, size_t ws_bytes, float v_skip, DecodeArgs* a) {
     int st = check_decode(L, cbk, cbv);
     if (st != TQ_OK) return st;
     int len = 0;
@@ -1558,30 +1602,45 @@ int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
         return TQ_ERR_INVALID;
     if (!(v_skip >= 0.0f && v_skip <= 1.0f)) return TQ_ERR_INVALID;  // NaN fails too
     if (ws_bytes < workspace_bytes(L, split_tokens)) return TQ_ERR_WORKSPACE;
-    DecodeArgs a{};
-    a.q_rot = q_rot;
-    a.q_sk = q_sketch;
-    a.k_cache = static_cast<const uint8_t*>(k_cache);
-    a.v_cache = static_cast<const uint8_t*>(v_cache);
-    a.seq_lens = seq_lens;
-    a.scores = scores;
+    *a = DecodeArgs{};
+    a->q_rot = q_rot;
+    a->q_sk = q_sketch;
+    a->k_cache = static_cast<const uint8_t*>(k_cache);
+    a->v_cache = static_cast<const uint8_t*>(v_cache);
+    a->seq_lens = seq_lens;
+    a->scores = scores;
     const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
-    a.ml = static_cast<float2*>(ws);
-    a.acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
-    a.hq = L->n_q_heads;
-    a.hkv = L->n_kv_heads;
-    a.capacity = L->capacity;
-    a.splits = splits;
-    a.split_len = len;
-    a.v_skip = v_skip;
+    a->ml = static_cast<float2*>(ws);
+    a->acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
+    a->hq = L->n_q_heads;
+    a->hkv = L->n_kv_heads;
+    a->capacity = L->capacity;
+    a->splits = splits;
+    a->split_len = len;
+    a->v_skip = v_skip;
+    return TQ_OK;
+}
+
+int dispatch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+                     const Launch& stream) {
     const int kf = L->k_format, vf = L->v_format;
-    if (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ4, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
-    if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ3>(a, L, *cbk, *cbv, stream);
-    if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ4>(a, L, *cbk, *cbv, stream);
-    if (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V) return dispatch_dim<TQ_FMT_TQ3K, TQ_FMT_GQ2V>(a, L, *cbk, *cbv, stream);
+    if (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ4, TQ_FMT_PQ4>(a, L, cbk, cbv, stream);
+    if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ3>(a, L, cbk, cbv, stream);
+    if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ4>(a, L, cbk, cbv, stream);
+    if (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V) return dispatch_dim<TQ_FMT_TQ3K, TQ_FMT_GQ2V>(a, L, cbk, cbv, stream);
     return TQ_ERR_UNSUPPORTED;
 }
 
+// Split records of the compressed cache.
+int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
+                   const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
+                   float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream,
+                   float v_skip = 0.0f) {
+    DecodeArgs a;
+    const int st = partial_args(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
+                                ws_bytes, v_skip, &a);
+    return st != TQ_OK ? st : dispatch_partial(a, L, *cbk, *cbv, stream);
+}
 
 }  // namespace
 }  // namespace tq
@@ -1602,6 +1661,27 @@ int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq
     if (!start || !stop) return TQ_ERR_INVALID;
     return tq::decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
                               ws_bytes, tq::Launch{stream, start, stop});
+}
+
+int tq_decode_partial_from_query(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q,
+                                 float* q_rot_scratch, const void* k_cache, const void* v_cache,
+                                 const int32_t* seq_lens, float* scores, int split_tokens, void* ws, size_t ws_bytes,
+                                 hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    using namespace tq;
+    if (!L || L->k_format == TQ_FMT_TQ3K) return L ? TQ_ERR_UNSUPPORTED : TQ_ERR_INVALID;  // TQ3K needs the sketch
+    if (!q || !aligned(q, 16) || !aligned(q_rot_scratch, 16) || (start == nullptr) != (stop == nullptr))
+        return TQ_ERR_INVALID;
+    DecodeArgs a;
+    const int st = partial_args(L, cbk, cbv, q_rot_scratch, nullptr, k_cache, v_cache, seq_lens, scores,
+                                split_tokens, ws, ws_bytes, 0.0f, &a);
+    if (st != TQ_OK) return st;
+    const Launch l{stream, start, stop};
+    if (rotates_in_kernel(L, *cbk, *cbv)) {
+        a.q_raw = q;  // rotated in the kernel's prologue; the scratch stays untouched
+        return dispatch_partial(a, L, *cbk, *cbv, l);
+    }
+    const int rs = tq_rotate_sketch_query(L, cbk, nullptr, q, q_rot_scratch, nullptr, stream);
+    return rs != TQ_OK ? rs : dispatch_partial(a, L, *cbk, *cbv, l);
 }
 
 int tq_decode_partial_sparse_v(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,

@@ -261,6 +261,30 @@ int tq_decode_partial_timed(const tq_layout* L, const tq_codebook* cbk, const tq
                             int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream,
                             hipEvent_t start, hipEvent_t stop);
 
+/* The partial from the unrotated query: the query rotation of
+ * tq_rotate_sketch_query ([P2] trick 1: <q, Pi^T y> = <Pi q, y>, rotate once
+ * per query) followed by tq_decode_partial, in one call.  Where the kernel
+ * can (PQ4 keys and values at d 128, four query heads per KV head, one
+ * centroid table for K and V) it rotates the query in its own prologue, with
+ * the same arithmetic, so the records equal those of the two calls bit for
+ * bit and one launch is saved; otherwise the rotation runs as its own launch
+ * into q_rot_scratch first.
+ *   q              device fp32 [B][Hq][d], unrotated, 16-byte aligned
+ *   q_rot_scratch  device fp32 [B][Hq][d], caller-owned, 16-byte aligned;
+ *                  holds the rotated query after the call when the rotation
+ *                  ran as its own launch, untouched otherwise
+ *   start, stop    optional events attached to the partial kernel's own
+ *                  dispatch (both or neither), as tq_decode_partial_timed
+ * Other arguments as tq_decode_partial.  Errors: those of tq_decode_partial;
+ * TQ_ERR_UNSUPPORTED for TQ3K keys (their scores need the query sketch: use
+ * tq_rotate_sketch_query and tq_decode_partial); TQ_ERR_INVALID for a null
+ * or misaligned q or scratch, or one event without the other.             */
+int tq_decode_partial_from_query(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
+                                 const float* q, float* q_rot_scratch, const void* k_cache,
+                                 const void* v_cache, const int32_t* seq_lens, float* scores,
+                                 int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream,
+                                 hipEvent_t start, hipEvent_t stop);
+
 /* Sparse V.  [P1] "turbo4 post-mortem", section 9 (current state) lists a
  * sparse-V mode as active alongside the 4-bit format; the page gives no rule
  * or threshold.  Reading taken here: the value of a token is skipped when its

@@ -135,6 +135,15 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert tq.lib.tq_decode_partial_timed(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake,
                                           need - 1, None, fake, fake) == -3
     assert tq.lib.tq_quantize_rotated(9, r(cb), None, fake, fake, 1, fake, None) == -2
+    # the partial from the unrotated query: its own arguments first, then those of the partial
+    fq = tq.lib.tq_decode_partial_from_query
+    assert fq(r(L), r(cb), r(cb), None, fake, fake, fake, fake, None, 0, fake, need, None, None, None) == -1
+    assert fq(r(L), r(cb), r(cb), misaligned, fake, fake, fake, fake, None, 0, fake, need, None, None, None) == -1
+    assert fq(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, fake, need, None, None, None) == -1
+    assert fq(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, None, 0, fake, need, None, fake, None) == -1
+    assert fq(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, None, 0, fake, need - 1, None, None, None) == -3
+    Lt = tq.Layout(1, 4, 2, 128, 128, tq.FMT_TQ3K, tq.FMT_GQ2V)
+    assert fq(r(Lt), r(cb), r(cb), fake, fake, fake, fake, fake, None, 0, fake, need, None, None, None) == -2
     # the sparse-V variant checks its arguments like the plain call, and the threshold range
     sv = tq.lib.tq_decode_partial_sparse_v
     assert sv(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, 0.0, fake, need - 1, None) == -3
