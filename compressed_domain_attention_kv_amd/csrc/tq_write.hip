@@ -359,8 +359,11 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
 // from 4 to 16 and 1 to 8 measured within 5% of each other.
 template <int D>
 constexpr int pq4_lanes() { return D / 16; }
+// passes per workgroup: four for bulk writes; one when the launch is small (an append of
+// a token per stream), so each wavefront's chain of VALU work is a quarter as long
 template <int D>
 constexpr int pq4_unroll() { return 4; }
+constexpr int kPq4SmallVectors = 8192;  // at most this many vectors: one pass per workgroup
 constexpr int kDppQuadRev = 0x1B;  // quad_perm [3,2,1,0]
 
 // DPP move with bound_ctrl set (every pattern used here stays inside its row, so it
@@ -379,7 +382,7 @@ __device__ __forceinline__ float lane_xor(float x) {
     else return dpp_f<kDppHalfMirror>(dpp_f<kDppMirror>(x));                       // 15 - (l ^ 7) = l ^ 8
 }
 
-template <int D, Src SRC>
+template <int D, Src SRC, int U>
 __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs ak, WriteArgs av, DevCodebook cbk,
                                                                      DevCodebook cbv, int kblocks) {
     static_assert(SRC != Src::kRotated, "fp16 sources");
@@ -387,7 +390,6 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
     constexpr int CPL = D / LANES;                // coordinates per lane
     constexpr int NPC = CPL / 8;                  // 16-byte pieces of fp16 input per lane
     constexpr int VPP = kWriteThreads / LANES;    // vectors per pass
-    constexpr int U = pq4_unroll<D>();
     constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
     // copies chosen by a uniform condition (a reference chosen at run time would put the
     // kernel arguments in scratch memory)
@@ -578,11 +580,18 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
 template <int D, Src SRC>
 int launch_pq4(const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk, const tq_codebook& cbv,
                hipStream_t st) {
-    constexpr int VPG = kWriteThreads / pq4_lanes<D>() * pq4_unroll<D>();  // vectors per workgroup
-    const int kblocks = (ak.nvec + VPG - 1) / VPG, vblocks = (av.nvec + VPG - 1) / VPG;
-    if (kblocks + vblocks == 0) return TQ_OK;
-    hipLaunchKernelGGL((quantize_pq4_kernel<D, SRC>), dim3(kblocks + vblocks), dim3(kWriteThreads), 0, st, ak, av,
-                       to_dev(cbk), to_dev(cbv), kblocks);
+    constexpr int VPP = kWriteThreads / pq4_lanes<D>();  // vectors per pass
+    if (ak.nvec + av.nvec == 0) return TQ_OK;
+    if (static_cast<long>(ak.nvec) + av.nvec <= kPq4SmallVectors) {
+        const int kblocks = (ak.nvec + VPP - 1) / VPP, vblocks = (av.nvec + VPP - 1) / VPP;
+        hipLaunchKernelGGL((quantize_pq4_kernel<D, SRC, 1>), dim3(kblocks + vblocks), dim3(kWriteThreads), 0, st, ak,
+                           av, to_dev(cbk), to_dev(cbv), kblocks);
+    } else {
+        constexpr int VPG = VPP * pq4_unroll<D>();  // vectors per workgroup
+        const int kblocks = (ak.nvec + VPG - 1) / VPG, vblocks = (av.nvec + VPG - 1) / VPG;
+        hipLaunchKernelGGL((quantize_pq4_kernel<D, SRC, pq4_unroll<D>()>), dim3(kblocks + vblocks),
+                           dim3(kWriteThreads), 0, st, ak, av, to_dev(cbk), to_dev(cbv), kblocks);
+    }
     return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

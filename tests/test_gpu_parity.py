@@ -340,3 +340,30 @@ def test_c1_end_to_end():
     else:  # a flipped code moves one coordinate by one centroid step
         ref, _ = P.oracle_decode(st, q, kdq, vdq, [512])
         assert P.rel_err_rows(out[0, 0], ref[0, 0]) < 1e-2
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_small_and_bulk_pq4_appends_write_the_same_bytes(d):
+    """The PQ4 write kernel takes one pass per workgroup for small launches (an append of a
+    token per stream) and four for bulk writes; the bytes are the same either way."""
+    base = REDUCED["c4"] if d == 128 else REDUCED["c5"]
+    w = synth.scaled(base, batch=1, n_q_heads=8, n_kv_heads=8, capacity=1152, context=1100)
+    st = P.Setup(w)
+    L = st.layout()
+    T = w.context
+    assert 2 * T * w.n_kv_heads > 8192  # one bulk launch
+    k_rows = torch.from_numpy(synth.batch_rows(w, synth.K_TENSOR, 0, 0, T)).cuda()
+    v_rows = torch.from_numpy(synth.batch_rows(w, synth.V_TENSOR, 0, 0, T)).cuda()
+    dst = torch.arange(T, dtype=torch.int32, device="cuda")
+    kcb, vcb = tq.cache_bytes(L)
+    caches = []
+    for chunk in (T, 97):  # 97 tokens x 8 heads x 2 tensors: small launches
+        kc = torch.full((kcb,), 0xEE, dtype=torch.uint8, device="cuda")
+        vc = torch.full((vcb,), 0xEE, dtype=torch.uint8, device="cuda")
+        for t0 in range(0, T, chunk):
+            t1 = min(T, t0 + chunk)
+            tq.quantize_append(L, st.cbk, st.cbv, None, k_rows[t0:t1].contiguous(), v_rows[t0:t1].contiguous(),
+                               dst[t0:t1].contiguous(), kc, vc)
+        torch.cuda.synchronize()
+        caches.append((kc.cpu().numpy(), vc.cpu().numpy()))
+    assert np.array_equal(caches[0][0], caches[1][0]) and np.array_equal(caches[0][1], caches[1][1])
