@@ -40,7 +40,7 @@ HBM_PEAK_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "decode_partial_pq4_c4_counters.txt")
 # the sources the decode_partial kernels are compiled from
 DECODE_SRCS = [os.path.join(ROOT, "compressed_domain_attention_kv_amd", "csrc", f)
-               for f in ("tq_decode.hip", "tq_device.h", "tq_internal.h")]
+               for f in ("tq_decode.hip", "tq_device.h", "tq_internal.h", "tq_pq4.h")]
 
 
 def _log(msg):
@@ -204,15 +204,15 @@ def main():
     k_new = torch.from_numpy(kn).to(dev)  # [steps, B, Hkv, d]: token t = sequence b
     v_new = torch.from_numpy(vn).to(dev)
     qs = torch.from_numpy(np.stack([synth.queries(w, step=s) for s in range(total)])).to(dev)
-    dst_row = torch.tensor([b * cap + N - 1 for b in range(B)], dtype=torch.int32, device=dev)
+    new_pos = torch.full((B,), N - 1, dtype=torch.int32, device=dev)  # the appended token of each sequence
     seq_lens = torch.full((B,), N, dtype=torch.int32, device=dev)
     q_rot = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)  # scratch; the c4 kernel rotates in place
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     ws = torch.empty(tq.decode_workspace_bytes(L, args.split_tokens), dtype=torch.uint8, device=dev)
     splits = tq.decode_splits(L, args.split_tokens)
 
-    # decode_partial (the roofline kernel) runs through tq_decode_partial_from_query in every step:
-    # it rotates the query in its prologue (no separate rotation launch), and the
+    # decode_partial (the roofline kernel) runs through tq_decode_step in every step: it appends
+    # the step's token and rotates the query in its prologue (no separate launches), and the
     # runtime records its two events on the kernel's own dispatch, so their interval is the kernel
     # alone and adds no packet to the stream.  Recorded events are packets that delay the next
     # kernel by a few microseconds, so only the last warm-up steps carry them, around the other
@@ -229,11 +229,8 @@ def main():
         e = ev[s]
         if marks == 5:
             e[0].record()
-        tq.quantize_append(L, cbk, cbv, None, k_new[s], v_new[s], dst_row, kc, vc)
-        if marks == 5:
-            e[1].record()
-        tq.decode_partial_from_query(L, cbk, cbv, qs[s], q_rot, kc, vc, seq_lens, ws, split_tokens=args.split_tokens,
-                                     events=(e[2].cuda_event, e[3].cuda_event))
+        tq.decode_step(L, cbk, cbv, k_new[s], v_new[s], new_pos, qs[s], q_rot, kc, vc, seq_lens, ws,
+                       split_tokens=args.split_tokens, events=(e[2].cuda_event, e[3].cuda_event))
         tq.decode_combine(L, cbv, ws, out, split_tokens=args.split_tokens)
         if marks == 5:
             e[4].record()
@@ -255,8 +252,7 @@ def main():
     probe_steps = range(args.warmup - n_probe, args.warmup)
     timed_steps = range(args.warmup, total)
     partial_ms = mean_ms(2, 3, timed_steps)
-    append_ms, gap_ms, combine_ms = (mean_ms(0, 1, probe_steps), mean_ms(1, 2, probe_steps),
-                                     mean_ms(3, 4, probe_steps))
+    gap_ms, combine_ms = mean_ms(0, 2, probe_steps), mean_ms(3, 4, probe_steps)
     ms_step = t_total / args.steps * 1e3
     alg_bytes = B * Hkv * N * (tq.vector_bytes(tq.FMT_PQ4, d) * 2)
     achieved = alg_bytes / (partial_ms * 1e-3) / 1e9
@@ -296,13 +292,13 @@ def main():
             "splits": splits,
             "cache_copies": args.copies,
         },
-        "step_breakdown_ms": {"append": append_ms, "to_partial_start": gap_ms, "decode_partial": partial_ms,
+        "step_breakdown_ms": {"to_partial_start": gap_ms, "decode_partial": partial_ms,
                               "decode_combine": combine_ms},
-        "step_breakdown_note": (f"decode_partial (the query rotation included, in its prologue): HIP events on "
-                                f"the kernel's own dispatch in each of the {args.steps} timed steps "
-                                f"(tq_decode_partial_from_query); append, to_partial_start (end of the append "
-                                f"to the start of decode_partial) and decode_combine: the last {n_probe} "
-                                "warm-up steps, with events between kernels"),
+        "step_breakdown_note": (f"decode_partial (the token append and the query rotation included, in its "
+                                f"prologue): HIP events on the kernel's own dispatch in each of the {args.steps} "
+                                f"timed steps (tq_decode_step); to_partial_start (a recorded event to the start "
+                                f"of decode_partial) and decode_combine: the last {n_probe} warm-up steps, with "
+                                "events between kernels"),
         "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
         "roofline": {
             "kernel": "decode_partial_sparse_kernel<4, false>",

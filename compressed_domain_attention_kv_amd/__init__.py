@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     decode_partial,
     decode_partial_from_query,
     decode_partial_sparse_v,
+    decode_step,
     decode_splits,
     decode_workspace_bytes,
     lib,

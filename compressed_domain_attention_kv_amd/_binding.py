@@ -111,6 +111,8 @@ lib.tq_decode_partial_timed.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _
 lib.tq_decode_combine.restype = _I
 lib.tq_decode_partial_from_query.restype = _I
 lib.tq_decode_partial_from_query.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P, _P, _P]
+lib.tq_decode_step.restype = _I
+lib.tq_decode_step.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P, _P, _P]
 lib.tq_decode_partial_sparse_v.restype = _I
 lib.tq_decode_partial_sparse_v.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, ctypes.c_float, _P, _SZ, _P]
 lib.tq_decode_combine.argtypes = [_PL, _PC, _I, _P, _SZ, _P, _P]
@@ -239,6 +241,16 @@ def decode_partial_from_query(L, cbk, cbv, q, q_rot_scratch, k_cache, v_cache, s
                                             _ptr(scores), split_tokens, _ptr(ws), ws.numel() * ws.element_size(),
                                             _stream(stream), ctypes.c_void_p(start), ctypes.c_void_p(stop)),
            "tq_decode_partial_from_query")
+
+
+def decode_step(L, cbk, cbv, k_new, v_new, new_pos, q, q_rot_scratch, k_cache, v_cache, seq_lens, ws, scores=None,
+                split_tokens=0, stream=None, events=None):
+    """events: optional (start, stop) raw hipEvent_t handles for the partial kernel's dispatch."""
+    start, stop = events if events is not None else (None, None)
+    _check(lib.tq_decode_step(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), _ptr(k_new), _ptr(v_new),
+                              _ptr(new_pos), _ptr(q), _ptr(q_rot_scratch), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(seq_lens), _ptr(scores), split_tokens, _ptr(ws), ws.numel() * ws.element_size(),
+                              _stream(stream), ctypes.c_void_p(start), ctypes.c_void_p(stop)), "tq_decode_step")
 
 
 def decode_partial_sparse_v(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, ws, v_threshold,

@@ -21,6 +21,7 @@
 #include <utility>
 
 #include "tq_device.h"
+#include "tq_pq4.h"
 
 namespace tq {
 namespace {
@@ -55,6 +56,13 @@ struct DecodeArgs {
     float v_skip;
     // the unrotated query [B][Hq][D], when the kernel rotates it itself (q_rot unused)
     const float* q_raw;
+    // the step's new token, when the kernel appends it itself: fp16 rows [B][Hkv][D] of K
+    // and V, written at position new_pos[b] of each stream (skipped when outside the cache)
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    const int32_t* new_pos;
+    uint8_t* k_wr;
+    uint8_t* v_wr;
 };
 
 // byte k of a register-resident little-endian byte run (k known at compile time after unrolling)
@@ -1039,6 +1047,8 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     __shared__ __align__(16) uint8_t vst1[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
     // the rotated query heads of the group, when the kernel rotates the query itself
     __shared__ __align__(16) float qrot_sh[G][D];
+    // key and value boundaries of the encoder, when the kernel appends the step's token
+    __shared__ __align__(16) float app_sb[2][4][4];
 
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1095,6 +1105,56 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         rv[4] = p1.x; rv[5] = p1.y; rv[6] = p1.z; rv[7] = p1.w;
         rsign = cbk.sign_bits[rl >> 2] >> (8 * (rl & 3));  // bits of coordinates 8 rl .. 8 rl + 7
     }
+    // the step's new token (values through LDS only): the workgroup whose splits hold position
+    // new_pos[b] of this stream encodes its key and value rows with the write kernel's
+    // arithmetic (wavefront 1: lanes 0..7 the key, 8..15 the value) and writes them into the
+    // caches before any wavefront requests the tile holding them: ahead of the first tiles
+    // when the position lies in one, else before the barrier that precedes every other tile.
+    bool app = false, app_first = false;
+    int apos = 0;
+    if (VLDS && a.new_pos != nullptr) {
+        apos = a.new_pos[b];
+        if (apos >= 0 && apos < a.capacity) {
+            const int sp = min(apos / a.split_len, a.splits - 1);
+            app = sp / kPairSub == static_cast<int>(blockIdx.x);
+            app_first = app && apos - sp * a.split_len < kWaves * TT;
+        }
+    }
+    const bool app_lane = app && wi == 1 && lane < 16, app_v = lane >= 8;
+    const int al = lane & 7;
+    uint4 araw[2];
+    if (app_lane) {
+        const uint16_t* src = (app_v ? a.v_new : a.k_new) + (static_cast<size_t>(b) * a.hkv + h) * D + 16 * al;
+        araw[0] = reinterpret_cast<const uint4*>(src)[0];
+        araw[1] = reinterpret_cast<const uint4*>(src)[1];
+    }
+    auto append_token = [&]() __attribute__((always_inline)) {
+        if (wi != 1) return;
+        if (lane < 32)  // boundaries b0 .. b14 and +inf of the key (lanes 0..15) and value tables
+            app_sb[lane >> 4][(lane & 15) >> 2][lane & 3] =
+                (lane & 15) < 15 ? (lane < 16 ? cbk.bounds[lane & 15] : cbv.bounds[lane & 15]) : INFINITY;
+        lds_order();
+        if (lane < 16) {
+            // the 16 signs of coordinates 16 al .. 16 al + 15 by 64-bit shifts (no indexing)
+            const uint64_t s01 = (static_cast<uint64_t>(app_v ? cbv.sign_bits[1] : cbk.sign_bits[1]) << 32) |
+                                 (app_v ? cbv.sign_bits[0] : cbk.sign_bits[0]);
+            const uint64_t s23 = (static_cast<uint64_t>(app_v ? cbv.sign_bits[3] : cbk.sign_bits[3]) << 32) |
+                                 (app_v ? cbv.sign_bits[2] : cbk.sign_bits[2]);
+            uint32_t smask[8];
+            pq4_sign_masks<16>(static_cast<uint32_t>((al < 4 ? s01 : s23) >> (16 * (al & 3))) & 0xFFFFu, smask);
+            const float b3 = app_v ? cbv.bounds[3] : cbk.bounds[3], b7 = app_v ? cbv.bounds[7] : cbk.bounds[7],
+                        b11 = app_v ? cbv.bounds[11] : cbk.bounds[11];
+            uint32_t n16, words[2];
+            pq4_encode<128, 8>(araw, smask, b3, b7, b11, reinterpret_cast<const float4*>(app_sb[app_v ? 1 : 0]), al,
+                               n16, words);
+            uint8_t* out = (app_v ? a.v_wr : a.k_wr) + ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + apos) * VB;
+            pq4_store<128, 8>(out, al, n16, words);
+        }
+    };
+    if (app_first) {
+        append_token();
+        __syncthreads();  // the rows are in memory before any tile request
+    }
     float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int qrb = wi / 4, qI = wi % 4, qhh = 4 * qrb + (n >> 2), qr = (n >> 1) & 1, qp = n & 1;
     if (!raw && wi < 4 * RB) {
@@ -1126,6 +1186,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         sm.u.op.table[tid + 1024 * k] = make_uint2(bf16_split(ck_lo), bf16_split(ck_hi[k]));
         if constexpr (VTAB) sm.u.op.vtable[tid + 1024 * k] = make_uint2(bf16_split(cv_lo), bf16_split(cv_hi[k]));
     }
+    if (app && !app_first) append_token();  // its tile is requested after the barrier below
     if (raw) {
         if (wi < G / 4) {
 #pragma unroll
@@ -1682,6 +1743,37 @@ int tq_decode_partial_from_query(const tq_layout* L, const tq_codebook* cbk, con
     }
     const int rs = tq_rotate_sketch_query(L, cbk, nullptr, q, q_rot_scratch, nullptr, stream);
     return rs != TQ_OK ? rs : dispatch_partial(a, L, *cbk, *cbv, l);
+}
+
+int tq_decode_step(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const void* k_new,
+                   const void* v_new, const int32_t* new_pos, const float* q, float* q_rot_scratch, void* k_cache,
+                   void* v_cache, const int32_t* seq_lens, float* scores, int split_tokens, void* ws, size_t ws_bytes,
+                   hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+    using namespace tq;
+    if (!L || L->k_format == TQ_FMT_TQ3K) return L ? TQ_ERR_UNSUPPORTED : TQ_ERR_INVALID;  // TQ3K needs S
+    if (!q || !aligned(q, 16) || !aligned(q_rot_scratch, 16) || (start == nullptr) != (stop == nullptr))
+        return TQ_ERR_INVALID;
+    if (!k_new || !v_new || !new_pos || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(new_pos, 4))
+        return TQ_ERR_INVALID;
+    DecodeArgs a;
+    int st = partial_args(L, cbk, cbv, q_rot_scratch, nullptr, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
+                          ws_bytes, 0.0f, &a);
+    if (st != TQ_OK) return st;
+    const Launch l{stream, start, stop};
+    if (rotates_in_kernel(L, *cbk, *cbv)) {  // one launch: append, rotation and partial
+        a.q_raw = q;
+        a.k_new = static_cast<const uint16_t*>(k_new);
+        a.v_new = static_cast<const uint16_t*>(v_new);
+        a.new_pos = new_pos;
+        a.k_wr = static_cast<uint8_t*>(k_cache);
+        a.v_wr = static_cast<uint8_t*>(v_cache);
+        return dispatch_partial(a, L, *cbk, *cbv, l);
+    }
+    // the new rows as a ring of one slot per stream, flushed at new_pos; then the rotation
+    st = tq_ring_flush(L, cbk, cbv, nullptr, 1, k_new, v_new, new_pos, 1, k_cache, v_cache, stream);
+    if (st != TQ_OK) return st;
+    st = tq_rotate_sketch_query(L, cbk, nullptr, q, q_rot_scratch, nullptr, stream);
+    return st != TQ_OK ? st : dispatch_partial(a, L, *cbk, *cbv, l);
 }
 
 int tq_decode_partial_sparse_v(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,

@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
+#include "tq_pq4.h"
 
 
 namespace tq {
@@ -48,22 +49,6 @@ __device__ __forceinline__ uint32_t code_of(float y, const DevCodebook& cb) {
 #pragma unroll
     for (int k = 0; k < NLEV - 1; ++k) c += (y > cb.bounds[k]) ? 1u : 0u;
     return c;
-}
-
-// The same count for 16 sorted boundaries by binary search: four comparisons,
-// each against the boundary the earlier ones select (b[7]; b[c + 3]; b[c + 1];
-// b[c]), so strict comparisons in fp32 give exactly #{k : b[k] < y}.  The first
-// two come from registers; the quad b[c .. c+3] holding the last two candidates
-// is one LDS read (a select among four or eight register values is turned into a
-// lookup table in scratch memory by the compiler).
-__device__ __forceinline__ uint32_t code_of16(float y, float b3, float b7, float b11, const float4* sb4) {
-    const bool m8 = y > b7;
-    const bool m4 = y > (m8 ? b11 : b3);
-    const uint32_t q = (m8 ? 2u : 0u) | (m4 ? 1u : 0u);
-    const float4 f = sb4[q];
-    const bool m2 = y > f.y;
-    const bool m1 = y > (m2 ? f.z : f.x);
-    return 4u * q | (m2 ? 2u : 0u) | (m1 ? 1u : 0u);
 }
 
 // Sketch rows of the vectors a workgroup holds in LDS: thread t owns row
@@ -364,24 +349,6 @@ constexpr int pq4_lanes() { return D / 16; }
 template <int D>
 constexpr int pq4_unroll() { return 4; }
 constexpr int kPq4SmallVectors = 8192;  // at most this many vectors: one pass per workgroup
-constexpr int kDppQuadRev = 0x1B;  // quad_perm [3,2,1,0]
-
-// DPP move with bound_ctrl set (every pattern used here stays inside its row, so it
-// changes nothing), which lets the compiler fold the move into the VALU op using it
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
-}
-
-// value of lane l ^ M (M = 1, 2, 4, 8) inside each row of 16 lanes, by DPP moves
-template <int M>
-__device__ __forceinline__ float lane_xor(float x) {
-    if constexpr (M == 1) return dpp_f<kDppXor1>(x);
-    else if constexpr (M == 2) return dpp_f<kDppXor2>(x);
-    else if constexpr (M == 4) return dpp_f<kDppQuadRev>(dpp_f<kDppHalfMirror>(x));  // 7 - (l ^ 3) = l ^ 4
-    else return dpp_f<kDppHalfMirror>(dpp_f<kDppMirror>(x));                       // 15 - (l ^ 7) = l ^ 8
-}
-
 template <int D, Src SRC, int U>
 __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs ak, WriteArgs av, DevCodebook cbk,
                                                                      DevCodebook cbv, int kblocks) {
@@ -390,7 +357,6 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
     constexpr int CPL = D / LANES;                // coordinates per lane
     constexpr int NPC = CPL / 8;                  // 16-byte pieces of fp16 input per lane
     constexpr int VPP = kWriteThreads / LANES;    // vectors per pass
-    constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
     // copies chosen by a uniform condition (a reference chosen at run time would put the
     // kernel arguments in scratch memory)
     const bool is_k = static_cast<int>(blockIdx.x) < kblocks;
@@ -399,16 +365,11 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
     const int block = is_k ? blockIdx.x : blockIdx.x - kblocks;
     const int tid = threadIdx.x, l = tid % LANES, slot = tid / LANES;
 
-    // rotation signs of this lane's coordinates CPL l .. CPL l + CPL - 1 (selected, not indexed)
-    uint32_t sw = cb.sign_bits[0];
-#pragma unroll
-    for (int i = 1; i < D / 32; ++i)
-        if ((CPL * l) >> 5 == i) sw = cb.sign_bits[i];
-    const uint32_t sgn = CPL == 32 ? sw : (sw >> ((CPL * l) & 31)) & 0xFFFFu;
-    // the signs as XOR masks of the fp16 input words (bit 15 / 31 per coordinate)
     uint32_t smask[CPL / 2];
+    uint32_t sws[D / 32];  // the sign words as values (a reference to the selected codebook would go to scratch)
 #pragma unroll
-    for (int i = 0; i < CPL / 2; ++i) smask[i] = (((sgn >> (2 * i)) & 1u) << 15) | (((sgn >> (2 * i + 1)) & 1u) << 31);
+    for (int i = 0; i < D / 32; ++i) sws[i] = cb.sign_bits[i];
+    pq4_sign_masks<CPL>(pq4_lane_signs<D, LANES>([&](int i) { return sws[i]; }, l), smask);
     __shared__ float4 sb4[4];  // boundaries b0 .. b14 (and +inf)
     if (tid < 16)  // indexed in the arguments, not in a copy
         reinterpret_cast<float*>(sb4)[tid] = tid < 15 ? (is_k ? cbk.bounds[tid] : cbv.bounds[tid]) : INFINITY;
@@ -427,63 +388,9 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        // s * x: the signs flip the fp16 sign bits before conversion
-        float v[CPL];
-#pragma unroll
-        for (int c = 0; c < NPC; ++c) {
-            const uint32_t w[4] = {raw[u][c].x ^ smask[4 * c], raw[u][c].y ^ smask[4 * c + 1],
-                                   raw[u][c].z ^ smask[4 * c + 2], raw[u][c].w ^ smask[4 * c + 3]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[8 * c + e] = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-        }
-        // norm: this lane's squares, then the lanes of the vector
-        float ss = 0.0f;
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) ss += v[e] * v[e];
-        static_for<__builtin_ctz(LANES)>([&](auto mc) { ss += lane_xor<(1 << decltype(mc)::value)>(ss); });
-        const float n = sqrtf(ss);
-        const uint32_t n16 = float_to_half_bits(fminf(n, kFp16Max));
-        const float scale = (n > 0.0f ? __fdiv_rn(1.0f, n) : 0.0f) * kInvSqrtD;  // 1 / (n sqrt(d))
-#pragma unroll
-        for (int e = 0; e < CPL; ++e) v[e] *= scale;
-        // y = H (s * u) / sqrt(d): stages over index bits 0 .. log2(d) - 1 in order
-#pragma unroll
-        for (int st = 1; st < CPL; st <<= 1)
-#pragma unroll
-            for (int e = 0; e < CPL; ++e)
-                if ((e & st) == 0) {
-                    const float x = v[e], y = v[e + st];
-                    v[e] = x + y;
-                    v[e + st] = x - y;
-                }
-        static_for<__builtin_ctz(LANES)>([&](auto mc) {
-            constexpr int M = 1 << decltype(mc)::value;
-            const bool upper = (l & M) != 0;
-#pragma unroll
-            for (int e = 0; e < CPL; ++e) {
-                const float p = lane_xor<M>(v[e]);
-                v[e] = upper ? (p - v[e]) : (v[e] + p);
-            }
-        });
-        uint32_t words[CPL / 8];
-#pragma unroll
-        for (int wq = 0; wq < CPL / 8; ++wq) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) word |= code_of16(v[8 * wq + e], b3, b7, b11, sb4) << (4 * e);
-            words[wq] = word;
-        }
-        if (tg[u].active) {
-            // coordinates CPL l .. : block (CPL l) / 128, code bytes from (CPL l % 128) / 2
-            uint8_t* bp = a.out + tg[u].off + 68 * ((CPL * l) / 128);
-            const int cofs = 4 + ((CPL * l) % 128) / 2;
-            if ((CPL * l) % 128 == 0) *reinterpret_cast<uint32_t*>(bp) = n16;
-            if constexpr (CPL == 16) {
-                *reinterpret_cast<uint2*>(bp + cofs) = make_uint2(words[0], words[1]);
-            } else {
-                *reinterpret_cast<uint4*>(bp + cofs) = make_uint4(words[0], words[1], words[2], words[3]);
-            }
-        }
+        uint32_t n16, words[CPL / 8];
+        pq4_encode<D, LANES>(raw[u], smask, b3, b7, b11, sb4, l, n16, words);
+        if (tg[u].active) pq4_store<D, LANES>(a.out + tg[u].off, l, n16, words);
     }
 }
 

@@ -285,6 +285,25 @@ int tq_decode_partial_from_query(const tq_layout* L, const tq_codebook* cbk, con
                                  int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream,
                                  hipEvent_t start, hipEvent_t stop);
 
+/* One decode step: append one new token per (sequence, KV head), then the
+ * partial from the unrotated query, as tq_ring_flush of a one-slot ring (the
+ * write path of [P2]: quantize on the way in, [P1] section 5 format)
+ * followed by tq_decode_partial_from_query.  Where the kernel rotates the
+ * query itself (the layouts named there) it also encodes and writes the new
+ * rows, with the write kernel's arithmetic, so the cache bytes and the
+ * records equal those of the separate calls bit for bit, in one launch.
+ *   k_new, v_new  device fp16 [B][Hkv][d], 16-byte aligned
+ *   new_pos       device int32 [B]: position of sequence b's new token;
+ *                 < 0, or >= capacity, skips the sequence.  seq_lens must
+ *                 count the new token when it is to be attended.
+ * Other arguments as tq_decode_partial_from_query (k_cache and v_cache are
+ * written).  Errors: those of tq_decode_partial_from_query, TQ_ERR_INVALID
+ * for null or misaligned new rows or positions.                           */
+int tq_decode_step(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const void* k_new,
+                   const void* v_new, const int32_t* new_pos, const float* q, float* q_rot_scratch,
+                   void* k_cache, void* v_cache, const int32_t* seq_lens, float* scores, int split_tokens,
+                   void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+
 /* Sparse V.  [P1] "turbo4 post-mortem", section 9 (current state) lists a
  * sparse-V mode as active alongside the 4-bit format; the page gives no rule
  * or threshold.  Reading taken here: the value of a token is skipped when its

@@ -144,6 +144,19 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert fq(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, None, 0, fake, need - 1, None, None, None) == -3
     Lt = tq.Layout(1, 4, 2, 128, 128, tq.FMT_TQ3K, tq.FMT_GQ2V)
     assert fq(r(Lt), r(cb), r(cb), fake, fake, fake, fake, fake, None, 0, fake, need, None, None, None) == -2
+    # one decode step: the new rows and positions, then the arguments of the partial from the query
+    ds = tq.lib.tq_decode_step
+    assert ds(r(L), r(cb), r(cb), None, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need, None, None,
+              None) == -1
+    odd = ctypes.c_void_p((1 << 20) + 2)  # not 4-byte aligned
+    assert ds(r(L), r(cb), r(cb), fake, fake, odd, fake, fake, fake, fake, fake, None, 0, fake, need, None,
+              None, None) == -1
+    assert ds(r(L), r(cb), r(cb), fake, misaligned, fake, fake, fake, fake, fake, fake, None, 0, fake, need, None,
+              None, None) == -1
+    assert ds(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need - 1, None,
+              None, None) == -3
+    assert ds(r(Lt), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need, None, None,
+              None) == -2
     # the sparse-V variant checks its arguments like the plain call, and the threshold range
     sv = tq.lib.tq_decode_partial_sparse_v
     assert sv(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, 0.0, fake, need - 1, None) == -3

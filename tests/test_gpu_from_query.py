@@ -108,3 +108,53 @@ def test_from_query_edge_lengths():
         assert np.array_equal(ws0, ws1)
         assert np.all(out[0] == 0.0)
         P.check_read(st, q, kdq, vdq, lens, out, None, w.capacity)
+
+
+STEP_CASES = {
+    # rotated and appended in the kernel; sequence 2's new token lies in a wavefront's first tile
+    "c4": (synth.scaled(synth.C4, batch=5, n_q_heads=8, n_kv_heads=2, context=1300, capacity=1344),
+           [1300, 1203, 70, 1025, 640], [1299, 1202, 69, -1, 1344]),
+    "c5": (synth.scaled(synth.C5, batch=3, n_q_heads=16, n_kv_heads=2, context=700, capacity=704),
+           [700, 603, 33], [699, 602, 32]),
+    "c2": (synth.scaled(synth.C2, batch=2, n_q_heads=8, n_kv_heads=2, context=777, capacity=832),
+           [777, 680], [776, 679]),
+}
+
+
+@pytest.mark.parametrize("name", list(STEP_CASES))
+def test_decode_step_equals_flush_then_partial(name):
+    """tq_decode_step writes the same cache bytes and split records as a one-slot ring
+    flush followed by the partial from the query (sequences with a negative position or
+    one past the capacity are skipped)."""
+    w, lens, pos = STEP_CASES[name]
+    st = P.Setup(w)
+    L = st.layout()
+    kc0, vc0, _, _ = _cache(st, w, L, [max(0, n - 1) for n in lens])
+    k_new = torch.from_numpy(np.stack([synth.batch_rows(w, synth.K_TENSOR, b, 5000, 1)[0]
+                                       for b in range(w.batch)])).cuda()
+    v_new = torch.from_numpy(np.stack([synth.batch_rows(w, synth.V_TENSOR, b, 5000, 1)[0]
+                                       for b in range(w.batch)])).cuda()
+    new_pos = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    sl = torch.tensor(np.asarray(lens, np.int32), device="cuda")
+    qd = torch.from_numpy(np.ascontiguousarray(synth.queries(w), np.float32)).cuda()
+    _say(f"decode step {name} lens={lens} pos={pos}")
+    for split in (0, 256):
+        nbytes = tq.decode_workspace_bytes(L, split)
+        kc1, vc1, kc2, vc2 = kc0.clone(), vc0.clone(), kc0.clone(), vc0.clone()
+        ws1 = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        ws2 = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        s1, s2 = torch.empty_like(qd), torch.empty_like(qd)
+        tq.decode_step(L, st.cbk, st.cbv, k_new, v_new, new_pos, qd, s1, kc1, vc1, sl, ws1, split_tokens=split)
+        tq.ring_flush(L, st.cbk, st.cbv, None, 1, k_new, v_new, new_pos, 1, kc2, vc2)
+        tq.decode_partial_from_query(L, st.cbk, st.cbv, qd, s2, kc2, vc2, sl, ws2, split_tokens=split)
+        torch.cuda.synchronize()
+        assert torch.equal(kc1, kc2) and torch.equal(vc1, vc2), f"{name} split {split}: cache bytes differ"
+        assert torch.equal(ws1, ws2), f"{name} split {split}: records differ"
+        # the appended rows landed where asked, and nowhere else changed
+        changed = (kc1 != kc0).view(w.batch, w.n_kv_heads, w.capacity, -1).any(-1).cpu().numpy()
+        for b in range(w.batch):
+            want = np.zeros(w.capacity, bool)
+            if 0 <= pos[b] < w.capacity:
+                want[pos[b]] = True
+            for h in range(w.n_kv_heads):
+                assert np.all(changed[b, h] <= want), f"{name} b={b} h={h}: bytes changed elsewhere"
