@@ -150,8 +150,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the decode path runs on a single MI355X and this build has no "
-              "multi-GPU path (sharding is described in DESIGN.md); rerun with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the decode path runs on a single MI355X and the library has no "
+              "multi-GPU path; rerun with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -527,7 +527,7 @@ def bench_sweep(args):
     torch.cuda.synchronize()
 
     # ---- decode of the other workloads (c5 reads the prefill bytes as [32][2][8192])
-    # the asymmetric pair of the survey's next steps: turbo3-style keys with 4-bit values, at c2's shapes
+    # the asymmetric pair: turbo3-style keys with 4-bit values, at c2's shapes
     asym = synth.scaled(synth.C2, name="c2 with PQ3 keys and PQ4 values", v_format=synth.PQ4, v_bits=4)
     for w in (synth.C1, synth.C2, asym, synth.C3, synth.C5):
         B, Hq, Hkv, d, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
