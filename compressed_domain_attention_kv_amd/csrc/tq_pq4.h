@@ -46,20 +46,8 @@ __device__ __forceinline__ uint32_t code_of16(float y, float b3, float b7, float
     return 4u * q | (m2 ? 2u : 0u) | (m1 ? 1u : 0u);
 }
 
-// The rotation signs of lane l's coordinates CPL l .. CPL l + CPL - 1 (CPL = D / LANES),
-// bit e for coordinate CPL l + e.  word(i) returns sign word i; the word is selected,
-// not indexed, so a codebook stays in the kernel arguments.
-template <int D, int LANES, typename W>
-__device__ __forceinline__ uint32_t pq4_lane_signs(W word, int l) {
-    constexpr int CPL = D / LANES;
-    uint32_t sw = word(0);
-#pragma unroll
-    for (int i = 1; i < D / 32; ++i)
-        if ((CPL * l) >> 5 == i) sw = word(i);
-    return CPL == 32 ? sw : (sw >> ((CPL * l) & 31)) & 0xFFFFu;
-}
-
-// The signs as XOR masks of the lane's fp16 input words (bit 15 / 31 per coordinate).
+// The rotation signs of a lane's CPL coordinates (bit e for its coordinate e) as XOR masks
+// of its fp16 input words (bit 15 / 31 per coordinate).
 template <int CPL>
 __device__ __forceinline__ void pq4_sign_masks(uint32_t sgn, uint32_t (&smask)[CPL / 2]) {
 #pragma unroll

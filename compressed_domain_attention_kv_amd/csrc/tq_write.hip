@@ -366,10 +366,13 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
     const int tid = threadIdx.x, l = tid % LANES, slot = tid / LANES;
 
     uint32_t smask[CPL / 2];
-    uint32_t sws[D / 32];  // the sign words as values (a reference to the selected codebook would go to scratch)
+    // rotation signs of this lane's coordinates CPL l .. CPL l + CPL - 1 (selected, not indexed:
+    // an indexed array of the words would be placed in LDS or scratch)
+    uint32_t sw = cb.sign_bits[0];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) sws[i] = cb.sign_bits[i];
-    pq4_sign_masks<CPL>(pq4_lane_signs<D, LANES>([&](int i) { return sws[i]; }, l), smask);
+    for (int i = 1; i < D / 32; ++i)
+        if ((CPL * l) >> 5 == i) sw = cb.sign_bits[i];
+    pq4_sign_masks<CPL>(CPL == 32 ? sw : (sw >> ((CPL * l) & 31)) & 0xFFFFu, smask);
     __shared__ float4 sb4[4];  // boundaries b0 .. b14 (and +inf)
     if (tid < 16)  // indexed in the arguments, not in a copy
         reinterpret_cast<float*>(sb4)[tid] = tid < 15 ? (is_k ? cbk.bounds[tid] : cbv.bounds[tid]) : INFINITY;
