@@ -171,3 +171,69 @@ def test_c5_bulk_prefill_then_decode():
             ref, logits = P.oatt.softmax_attention(q[b, g], kdq[(b, h)], vdq[(b, h)])
             assert P.rel_err_rows(scores[b, g], logits) <= P.SCORE_TOL
             assert P.rel_err_rows(out[b, g], ref) <= P.OUT_TOL
+
+
+def _last_row(e):
+    """The oracle encoding of the last row alone."""
+    import dataclasses
+    return dataclasses.replace(e, blocks=e.blocks[-1:], norm=e.norm[-1:], y=e.y[-1:], idx=e.idx[-1:])
+
+
+def test_c4_full_size_fused_step():
+    """The benchmark's launch: tq_decode_step at c4's full size (the kernel appends token
+    65,535 of every stream and rotates the query in its prologue), then the combine.  The
+    prefix of the sampled streams holds the oracle's bytes; the appended rows the kernel
+    wrote are checked against the oracle's encoding, and the outputs against the oracle's
+    attention over its own encoding of every row."""
+    w = synth.C4
+    st = P.Setup(w)
+    L = st.layout()
+    d, n0 = w.head_dim, w.prefill
+    kb_, vb_ = tq.cache_bytes(L)
+    kc = torch.empty(kb_, dtype=torch.uint8, device="cuda")
+    vc = torch.empty(vb_, dtype=torch.uint8, device="cuda")
+    _say(f"{w.name} fused step: generating and encoding {w.batch}x{w.n_kv_heads}x{n0} rows")
+    krows = _gen_rows(w, synth.K_TENSOR, n0)
+    vrows = _gen_rows(w, synth.V_TENSOR, n0)
+    for b in range(w.batch):
+        dst = torch.arange(b * w.capacity, b * w.capacity + n0, dtype=torch.int32, device="cuda")
+        tq.quantize_append(L, st.cbk, st.cbv, None, torch.from_numpy(krows[b]).cuda(),
+                           torch.from_numpy(vrows[b]).cuda(), dst, kc, vc)
+    step = 1
+    kn = np.stack([np.stack([synth.appended(w, synth.K_TENSOR, b, h, step) for h in range(w.n_kv_heads)])
+                   for b in range(w.batch)])
+    vn = np.stack([np.stack([synth.appended(w, synth.V_TENSOR, b, h, step) for h in range(w.n_kv_heads)])
+                   for b in range(w.batch)])
+    torch.cuda.synchronize()
+    kview, vview = _cache_view(kc, L, st.vbk), _cache_view(vc, L, st.vbv)
+    sample = [(0, 0), (5, 7), (2, 3)]
+    enc = {}
+    for (b, h) in sample:
+        ek = st.oracle_encode(synth.K_TENSOR, np.concatenate([krows[b][:, h], kn[b, h][None]]))
+        ev = st.oracle_encode(synth.V_TENSOR, np.concatenate([vrows[b][:, h], vn[b, h][None]]))
+        kview[b, h, :n0].copy_(torch.from_numpy(ek.blocks[:n0]))
+        vview[b, h, :n0].copy_(torch.from_numpy(ev.blocks[:n0]))
+        enc[(b, h)] = (ek, ev)
+    q = synth.queries(w, step=step)
+    qd = torch.from_numpy(q).cuda()
+    out = torch.full((w.batch, w.n_q_heads, d), float("nan"), device="cuda")
+    ws = torch.empty(tq.decode_workspace_bytes(L), dtype=torch.uint8, device="cuda")
+    tq.decode_step(L, st.cbk, st.cbv, torch.from_numpy(kn).cuda(), torch.from_numpy(vn).cuda(),
+                   torch.full((w.batch,), n0, dtype=torch.int32, device="cuda"), qd, torch.empty_like(qd), kc, vc,
+                   torch.full((w.batch,), n0 + 1, dtype=torch.int32, device="cuda"), ws)
+    tq.decode_combine(L, st.cbv, ws, out)
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+    worst = 0.0
+    for (b, h), (ek, ev) in enc.items():
+        sk = P.compare_write(st, synth.K_TENSOR, kview[b, h, n0:n0 + 1].cpu().numpy(), _last_row(ek))
+        sv = P.compare_write(st, synth.V_TENSOR, vview[b, h, n0:n0 + 1].cpu().numpy(), _last_row(ev))
+        _say(f"  stream {(b, h)} appended row: K {sk} V {sv}")
+        kd, vd = st.oracle_dequant(synth.K_TENSOR, ek.blocks), st.oracle_dequant(synth.V_TENSOR, ev.blocks)
+        for g in range(h * w.group, (h + 1) * w.group):
+            ref, _ = P.oatt.softmax_attention(q[b, g], kd, vd)
+            e = float(P.rel_err_rows(out[b, g], ref))
+            worst = max(worst, e)
+            assert e <= P.OUT_TOL, (b, g, e)
+    _say(f"  sampled streams: worst output err {worst:.2e}")
