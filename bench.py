@@ -10,16 +10,23 @@ split-K decode attention over the compressed bytes.  Inputs are the seeded
 synthetic rows of ``synth`` (Gaussian, 1% of channels scaled by 8), already
 resident in HBM when timing starts.
 
-One step = append (K and V) + query rotation + decode partial + combine.
-Two cache copies (1.14 GB together) alternate between steps so that the
-256 MB Infinity Cache cannot hold the bytes a step reads.  The default 200
-warm-up steps (about 35 ms of decode) let the GPU clock settle before the
-200 timed steps; a 10-step warm-up measures the kernel about 10% slower.
+One step = append (K and V) + query rotation + decode partial, in one launch
+of the decode kernel (tq_decode_step), then the combine of the split records.
+Two launches measured faster than the one-launch step that merges the splits
+in each stream's last workgroup (``--one-launch``).  Two cache copies (1.14 GB
+together) alternate between steps so that the 256 MB Infinity Cache cannot
+hold the bytes a step reads.  The default 200 warm-up steps (about 20 ms of
+decode) let the GPU clock settle before the 200 timed steps; a 10-step
+warm-up measures the kernel about 10% slower.
 
 Output: one JSON line.  ``value`` is compressed-KV tokens attended per second
-(batch * context / step time).  ``roofline`` reports the dominant kernel,
-decode_partial: algorithmic K+V bytes per launch over its mean duration
-measured with HIP events on the launch stream, against the 8 TB/s HBM peak.
+(batch * context / host-clock step time).  ``roofline`` reports the dominant
+kernel, decode_partial: algorithmic K+V bytes per launch over its mean
+duration, measured with HIP events that the runtime attaches to the kernel's
+own dispatch on every 8th timed step (events on every step add about 4 us to
+each step they are on).  ``decode_attention_gbs`` divides the same bytes by
+the whole host-clock step (append, rotation, partial, combine and the gaps
+between launches).
 ``cpu_baseline`` times the float64 CPU oracle on a bounded sample of the same
 step.  ``--copy-calibration`` additionally runs a plain 1 GiB elementwise
 copy, the reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE.
@@ -145,6 +152,8 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="kernel times of the other workloads at full size (c5 bulk prefill, c1/c2/c3/c5 decode), "
                          "one JSON line each; not the headline line")
+    ap.add_argument("--one-launch", action="store_true",
+                    help="time the one-launch step (the decode kernel merges the splits; no combine launch)")
     ap.add_argument("--ring-cap", type=int, default=128)
     ap.add_argument("--flush", type=int, default=64)
     args = ap.parse_args()
@@ -208,54 +217,46 @@ def main():
     seq_lens = torch.full((B,), N, dtype=torch.int32, device=dev)
     q_rot = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)  # scratch; the c4 kernel rotates in place
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
-    ws = torch.empty(tq.decode_workspace_bytes(L, args.split_tokens), dtype=torch.uint8, device=dev)
+    ws = tq.decode_workspace(L, args.split_tokens)
     splits = tq.decode_splits(L, args.split_tokens)
 
-    # decode_partial (the roofline kernel) runs through tq_decode_step in every step: it appends
-    # the step's token and rotates the query in its prologue (no separate launches), and the
-    # runtime records its two events on the kernel's own dispatch, so their interval is the kernel
-    # alone and adds no packet to the stream.  Recorded events are packets that delay the next
-    # kernel by a few microseconds, so only the last warm-up steps carry them, around the other
-    # kernels, for the per-kernel breakdown of the step.
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
+    # The decode kernel (tq_decode_step) appends the step's token and rotates the query in its
+    # prologue; the combine follows (or, with --one-launch, the kernel merges the splits itself).
+    # On every EVERY-th timed step the runtime records two events on the decode kernel's own
+    # dispatch, so their interval is that kernel alone.
+    EVERY = 8
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(total)]
     for e in ev:  # create the HIP events now (torch creates them on first record)
-        e[2].record()
-        e[3].record()
+        e[0].record()
+        e[1].record()
     torch.cuda.synchronize()
-    n_probe = min(args.warmup, 50)
 
-    def step(s, marks):
+    def step(s):
         kc, vc = caches[s % args.copies]
-        e = ev[s]
-        if marks == 5:
-            e[0].record()
-        tq.decode_step(L, cbk, cbv, k_new[s], v_new[s], new_pos, qs[s], q_rot, kc, vc, seq_lens, ws,
-                       split_tokens=args.split_tokens, events=(e[2].cuda_event, e[3].cuda_event))
-        tq.decode_combine(L, cbv, ws, out, split_tokens=args.split_tokens)
-        if marks == 5:
-            e[4].record()
+        evs = (ev[s][0].cuda_event, ev[s][1].cuda_event) if s % EVERY == 0 else None
+        if args.one_launch:
+            tq.decode_step(L, cbk, cbv, k_new[s], v_new[s], new_pos, qs[s], q_rot, kc, vc, seq_lens, ws, out=out,
+                           split_tokens=args.split_tokens, events=evs)
+        else:
+            tq.decode_step(L, cbk, cbv, k_new[s], v_new[s], new_pos, qs[s], q_rot, kc, vc, seq_lens, ws,
+                           split_tokens=args.split_tokens, events=evs)
+            tq.decode_combine(L, cbv, ws, out, split_tokens=args.split_tokens)
 
     for s in range(args.warmup):
-        step(s, 5 if s >= args.warmup - n_probe else 2)
+        step(s)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.warmup, total):
-        step(s, 2)
+        step(s)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
 
-    def mean_ms(i, j, steps):
-        if len(steps) == 0:
-            return None
-        return float(np.mean([ev[s][i].elapsed_time(ev[s][j]) for s in steps]))
-
-    probe_steps = range(args.warmup - n_probe, args.warmup)
-    timed_steps = range(args.warmup, total)
-    partial_ms = mean_ms(2, 3, timed_steps)
-    gap_ms, combine_ms = mean_ms(0, 2, probe_steps), mean_ms(3, 4, probe_steps)
+    timed_steps = [s for s in range(args.warmup, total) if s % EVERY == 0]
+    kern = np.array([ev[s][0].elapsed_time(ev[s][1]) for s in timed_steps])
+    kernel_ms = float(np.mean(kern))
     ms_step = t_total / args.steps * 1e3
     alg_bytes = B * Hkv * N * (tq.vector_bytes(tq.FMT_PQ4, d) * 2)
-    achieved = alg_bytes / (partial_ms * 1e-3) / 1e9
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
@@ -292,16 +293,17 @@ def main():
             "splits": splits,
             "cache_copies": args.copies,
         },
-        "step_breakdown_ms": {"to_partial_start": gap_ms, "decode_partial": partial_ms,
-                              "decode_combine": combine_ms},
-        "step_breakdown_note": (f"decode_partial (the token append and the query rotation included, in its "
-                                f"prologue): HIP events on the kernel's own dispatch in each of the {args.steps} "
-                                f"timed steps (tq_decode_step); to_partial_start (a recorded event to the start "
-                                f"of decode_partial) and decode_combine: the last {n_probe} warm-up steps, with "
-                                "events between kernels"),
-        "decode_attention_gbs": alg_bytes / ((partial_ms + combine_ms) * 1e-3) / 1e9,
+        "step_breakdown_ms": {"decode_kernel": kernel_ms, "decode_kernel_median": float(np.median(kern)),
+                              "rest_of_step": ms_step - kernel_ms},
+        "step_breakdown_note": (f"decode_kernel: token append and query rotation in its prologue, then the "
+                                f"partial{' and the merge of the splits' if args.one_launch else ''}; HIP events on "
+                                f"the kernel's own dispatch on {len(timed_steps)} of the {args.steps} timed steps "
+                                f"(every {EVERY}th); rest_of_step: host-clock step time minus that kernel "
+                                f"({'launch gaps' if args.one_launch else 'the combine and the launch gaps'})"),
+        "decode_attention_gbs": alg_bytes / (ms_step * 1e-3) / 1e9,
+        "decode_attention_gbs_note": "algorithmic K+V bytes over the whole host-clock step",
         "roofline": {
-            "kernel": "decode_partial_sparse_kernel<4, false>",
+            "kernel": "decode_partial_sparse_kernel<4, false>" + (" (with the merge)" if args.one_launch else ""),
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -31,7 +31,9 @@ from ._binding import (  # noqa: F401
     decode_partial_sparse_v,
     decode_step,
     decode_splits,
+    decode_workspace,
     decode_workspace_bytes,
+    decode_workspace_init,
     lib,
     library_path,
     quantize_append,

@@ -313,15 +313,26 @@ void launch_combine(const CombineArgs& a, int rows, int rmax, const DevCodebook&
     else hipLaunchKernelGGL((decode_combine_kernel<D, ROT, 256>), grid, block, 0, st, a, ck, cv);
 }
 
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, size_t n) {
+    const size_t i = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 }  // namespace
+
+int clear_words(uint32_t* p, size_t n, hipStream_t stream) {
+    if (n == 0) return TQ_OK;
+    hipLaunchKernelGGL(clear_words_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
 
 int combine(const tq_layout* L, const tq_codebook* cbk, const tq_codebook& cbv, int splits, const void* ws, float* out,
             hipStream_t stream, const RingView* ring) {
     static_assert(kRingCapMax <= 256, "combine kernels are built for up to 256 ring tokens");
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
+    const WsLayout wl = ws_layout(*L, splits);
     CombineArgs a{};
     a.ml = static_cast<const float2*>(ws);
-    a.acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + recs * sizeof(float2));
+    a.acc = reinterpret_cast<const float*>(static_cast<const char*>(ws) + wl.acc);
     a.out = out;
     a.splits = splits;
     a.hq = L->n_q_heads;

@@ -63,6 +63,11 @@ struct DecodeArgs {
     const int32_t* new_pos;
     uint8_t* k_wr;
     uint8_t* v_wr;
+    // when out is set, the workgroup that finishes a stream last merges the stream's split
+    // records into the attention output (fp32 [B][Hq][D]); arrivals[b * hkv + h] counts the
+    // stream's finished workgroups and is zero before and after the launch
+    float* out;
+    uint32_t* arrivals;
 };
 
 // byte k of a register-resident little-endian byte run (k known at compile time after unrolling)
@@ -468,6 +473,161 @@ __device__ __forceinline__ float row16_max(float x) {
     x = fmaxf(x, dpp<kDppHalfMirror>(x));
     x = fmaxf(x, dpp<kDppMirror>(x));
     return x;
+}
+
+// ---------------------------------------------------------------------------
+// Merge of a stream's split records inside the decode launch ([P2] trick 3: the
+// (m, l, acc) state of the splits is combined once, and acc / l taken once, at the
+// end).  Each XCD has an L2 of its own, so the records are written with device-scope
+// stores (write-through past the L2) and read back with device-scope loads; a
+// workgroup waits for its own stores to complete, then counts itself in
+// arrivals[b * hkv + h] with a device-scope atomic.  The workgroup that arrives last
+// (it has seen every other increment, each issued after that workgroup's stores had
+// completed) merges the G rows of the stream with the arithmetic of the combine
+// kernel, normalizes, rotates back once (rotated value formats) and writes the
+// output; it then sets the counter back to zero for the next launch.  No workgroup
+// waits for another, and no L2 is written back or invalidated.
+
+__device__ __forceinline__ void store_dev(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_dev(float2* p, float2 v) {
+    const uint64_t bits = (static_cast<uint64_t>(__float_as_uint(v.y)) << 32) | __float_as_uint(v.x);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_dev(const float2* p) {
+    const uint64_t bits =
+        __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float2*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_float2(__uint_as_float(static_cast<uint32_t>(bits)), __uint_as_float(static_cast<uint32_t>(bits >> 32)));
+}
+
+// Workgroup-wide; true in the workgroup that finished stream (b, h) last.  flag_sh is
+// one LDS word.  Every record store of the workgroup precedes the call.
+__device__ __forceinline__ bool stream_arrive(const DecodeArgs& a, int b, int h, uint32_t* flag_sh) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wavefront's record stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.arrivals + (static_cast<size_t>(b) * a.hkv + h), 1u,
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag_sh = prev + 1 == gridDim.x ? 1u : 0u;
+    }
+    __syncthreads();
+    return *flag_sh != 0;
+}
+
+// The last workgroup's merge of rows hq0 .. hq0 + G - 1 with NT threads: NT / G
+// threads per row, each owning four coordinates of one of its row's split groups and
+// merging that group's records with a running maximum of its own, in batches of four
+// records whose loads are all issued first; then the groups merge through LDS, and
+// wavefront r rotates row r back and normalizes it.  With 256 threads per row this
+// is exactly the combine kernel's order of operations.  lds: 4 NT + (2 NGS + D + 1) G
+// floats.
+template <int D, int G, int NT>
+__device__ __forceinline__ void stream_merge(const DecodeArgs& a, const DevCodebook& cbv, bool rotated, int b, int hq0,
+                                             float* lds) {
+    constexpr int TPR = NT / G, C = D / 4, NGS = TPR / C, DPL = D / 64, SPT = 4;
+    static_assert(NT % G == 0 && TPR % C == 0 && NGS >= 1, "whole split groups per row");
+    static_assert(NT / 64 >= G, "a wavefront per row for the rotation back");
+    constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
+    float4* part = reinterpret_cast<float4*>(lds);
+    float* pm = lds + 4 * NT;
+    float* pl = pm + G * NGS;
+    float* fin = pl + G * NGS;
+    float* finl = fin + G * D;
+    const int tid = threadIdx.x, r = tid / TPR, u = tid % TPR, grp = u / C, c = u % C;
+    const size_t row = static_cast<size_t>(b) * a.hq + hq0 + r;
+    const float2* mr = a.ml + row * a.splits;
+    const float4* ar = reinterpret_cast<const float4*>(a.acc) + row * a.splits * C + c;
+    float Mt = -INFINITY, Lt = 0.0f;
+    float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s0 = grp; s0 < a.splits; s0 += SPT * NGS) {
+        float2 rc[SPT];
+        float4 v[SPT];
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const int s = min(s0 + k * NGS, a.splits - 1);
+            rc[k] = load_dev(mr + s);
+            const float* x = reinterpret_cast<const float*>(ar + static_cast<size_t>(s) * C);
+            v[k] = make_float4(load_dev(x), load_dev(x + 1), load_dev(x + 2), load_dev(x + 3));
+        }
+        float mb = Mt;
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            if (s0 + k * NGS >= a.splits) rc[k].x = -INFINITY;  // the reread past the last split weighs nothing
+            mb = fmaxf(mb, rc[k].x);
+        }
+        const bool none = mb == -INFINITY;
+        const float so = none ? 1.0f : exp2f(Mt - mb);
+        Lt *= so;
+        o.x *= so; o.y *= so; o.z *= so; o.w *= so;
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+            const float f = rc[k].x == -INFINITY ? 0.0f : exp2f(rc[k].x - mb);
+            Lt = fmaf(rc[k].y, f, Lt);
+            o.x = fmaf(v[k].x, f, o.x); o.y = fmaf(v[k].y, f, o.y);
+            o.z = fmaf(v[k].z, f, o.z); o.w = fmaf(v[k].w, f, o.w);
+        }
+        Mt = mb;
+    }
+    part[tid] = o;
+    if (c == 0) {
+        pm[r * NGS + grp] = Mt;
+        pl[r * NGS + grp] = Lt;
+    }
+    __syncthreads();
+    if (tid < G * C) {
+        const int rr = tid / C, cc = tid % C;
+        float M = pm[rr * NGS];
+#pragma unroll
+        for (int g = 1; g < NGS; ++g) M = fmaxf(M, pm[rr * NGS + g]);
+        float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        float L = 0.0f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int g = 0; g < NGS; ++g) {
+                const float f = exp2f(pm[rr * NGS + g] - M);
+                const float4 x = part[rr * TPR + g * C + cc];
+                t.x = fmaf(x.x, f, t.x); t.y = fmaf(x.y, f, t.y);
+                t.z = fmaf(x.z, f, t.z); t.w = fmaf(x.w, f, t.w);
+                L = fmaf(pl[rr * NGS + g], f, L);
+            }
+        }
+        *reinterpret_cast<float4*>(fin + rr * D + 4 * cc) = t;
+        if (cc == 0) finl[rr] = L;
+    }
+    __syncthreads();
+    const int wv = tid >> 6, lane = tid & 63;
+    if (wv < G) {
+        float v[DPL];
+#pragma unroll
+        for (int k = 0; k < DPL; ++k) v[k] = fin[wv * D + DPL * lane + k];
+        if (rotated) {  // o <- Pi^T o = diag(s) H o / sqrt(d)
+            wht_wave<DPL>(v, lane);
+#pragma unroll
+            for (int k = 0; k < DPL; ++k) v[k] *= kInvSqrtD * rotation_sign(cbv, DPL * lane + k);
+        }
+        const float L = finl[wv];
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+#pragma unroll
+        for (int k = 0; k < DPL; ++k)
+            a.out[(static_cast<size_t>(b) * a.hq + hq0 + wv) * D + DPL * lane + k] = v[k] * inv;
+    }
+}
+
+// The end of a decode workgroup: when the launch merges, arrive, and merge the stream
+// if this workgroup is its last.  Uniform over the workgroup.
+template <int D, int G, int NT>
+__device__ __forceinline__ void stream_finish(const DecodeArgs& a, const DevCodebook& cbv, bool rotated, int b, int h,
+                                              float* lds, uint32_t* flag_sh) {
+    if (a.out == nullptr) return;
+    if (!stream_arrive(a, b, h, flag_sh)) return;
+    stream_merge<D, G, NT>(a, cbv, rotated, b, h * G, lds);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(a.arrivals + (static_cast<size_t>(b) * a.hkv + h), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int D, int G, int TT>
@@ -1049,6 +1209,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     __shared__ __align__(16) float qrot_sh[G][D];
     // key and value boundaries of the encoder, when the kernel appends the step's token
     __shared__ __align__(16) float app_sb[2][4][4];
+    __shared__ uint32_t tail_flag;  // this workgroup finished its stream last
 
     const int h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1477,10 +1638,16 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 A = fmaf(r[2 + j], f, A);
             }
             const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-            a.acc[rec * D + j] = A;
-            if (j == 0) a.ml[rec] = make_float2(M, L);
+            store_dev(a.acc + rec * D + j, A);  // device scope: another XCD may merge them
+            if (j == 0) store_dev(a.ml + rec, make_float2(M, L));
         }
     }
+    // the merge reuses the table and reduction area (the barrier in stream_arrive orders it
+    // after the reads of red above)
+    constexpr int NT = kPairWaves * 64;
+    static_assert(sizeof(sm.u) >= sizeof(float) * (4 * NT + (2 * (NT / G / (D / 4)) + D + 1) * G),
+                  "merge buffers fit the reused area");
+    stream_finish<D, G, NT>(a, cbv, true, b, h, reinterpret_cast<float*>(&sm.u), &tail_flag);
 }
 
 int auto_split_tokens(const tq_layout* L) {
@@ -1560,6 +1727,15 @@ bool rotates_in_kernel(const tq_layout* L, const tq_codebook& cbk, const tq_code
            same_centroids(cbk, cbv);
 }
 
+// The kernels that merge a stream's records themselves when given an output: the
+// 2:4-sparse PQ4 kernel (d 128, G = 4, or G = 8 with one table).  Mirrors dispatch_group.
+bool merges_in_kernel(const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv) {
+    if (L->k_format != TQ_FMT_PQ4 || L->v_format != TQ_FMT_PQ4 || L->head_dim != 128) return false;
+    if (static_cast<size_t>(L->capacity) * 68 > 0x7FFFFFFFu) return false;
+    const int G = L->n_q_heads / L->n_kv_heads;
+    return G == 4 || (G == 8 && same_centroids(cbk, cbv));
+}
+
 template <int D, int G>
 int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                         const Launch& l) {
@@ -1619,8 +1795,7 @@ size_t workspace_bytes(const tq_layout* L, int split_tokens) {
     int len = 0;
     const int splits = resolve_splits(L, split_tokens, &len);
     if (splits <= 0) return 0;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
-    return recs * sizeof(float2) + recs * L->head_dim * sizeof(float);
+    return ws_layout(*L, splits).total;
 }
 
 }  // namespace
@@ -1640,6 +1815,19 @@ size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens) {
 
 size_t tq_decode_hybrid_workspace_bytes(const tq_layout* L, int split_tokens) {
     return tq::workspace_bytes(L, split_tokens);  // the ring is merged in the combine: no record of its own
+}
+
+int tq_decode_workspace_init(const tq_layout* L, int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream) {
+    using namespace tq;
+    const int st = check_layout(L);
+    if (st != TQ_OK) return st;
+    int len = 0;
+    const int splits = resolve_splits(L, split_tokens, &len);
+    if (splits <= 0 || !ws || !aligned(ws, 16)) return TQ_ERR_INVALID;
+    const WsLayout wl = ws_layout(*L, splits);
+    if (ws_bytes < wl.total) return TQ_ERR_WORKSPACE;
+    return clear_words(reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.cnt),
+                       static_cast<size_t>(L->batch) * L->n_kv_heads, stream);
 }
 
 }  // extern "C"
@@ -1670,9 +1858,10 @@ int partial_args(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* 
     a->v_cache = static_cast<const uint8_t*>(v_cache);
     a->seq_lens = seq_lens;
     a->scores = scores;
-    const size_t recs = static_cast<size_t>(L->batch) * L->n_q_heads * splits;
+    const WsLayout wl = ws_layout(*L, splits);
     a->ml = static_cast<float2*>(ws);
-    a->acc = reinterpret_cast<float*>(static_cast<char*>(ws) + recs * sizeof(float2));
+    a->acc = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.acc);
+    a->arrivals = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + wl.cnt);
     a->hq = L->n_q_heads;
     a->hkv = L->n_kv_heads;
     a->capacity = L->capacity;
@@ -1692,15 +1881,28 @@ int dispatch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook&
     return TQ_ERR_UNSUPPORTED;
 }
 
-// Split records of the compressed cache.
+// One partial launch, and the output when `out` is set: merged by the partial kernel's
+// last workgroup per stream where it can (one launch), else by the combine kernel after it.
+int run_partial(DecodeArgs a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv, const Launch& l,
+                float* out) {
+    if (out && merges_in_kernel(L, cbk, cbv)) {
+        a.out = out;
+        return dispatch_partial(a, L, cbk, cbv, l);
+    }
+    const int st = dispatch_partial(a, L, cbk, cbv, l);
+    if (st != TQ_OK || !out) return st;
+    return combine(L, nullptr, cbv, a.splits, a.ml, out, l.st);
+}
+
+// Split records of the compressed cache (and the output when `out` is set).
 int decode_partial(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
                    const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                    float* scores, int split_tokens, void* ws, size_t ws_bytes, const Launch& stream,
-                   float v_skip = 0.0f) {
+                   float v_skip = 0.0f, float* out = nullptr) {
     DecodeArgs a;
     const int st = partial_args(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
                                 ws_bytes, v_skip, &a);
-    return st != TQ_OK ? st : dispatch_partial(a, L, *cbk, *cbv, stream);
+    return st != TQ_OK ? st : run_partial(a, L, *cbk, *cbv, stream, out);
 }
 
 }  // namespace
@@ -1747,12 +1949,13 @@ int tq_decode_partial_from_query(const tq_layout* L, const tq_codebook* cbk, con
 
 int tq_decode_step(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const void* k_new,
                    const void* v_new, const int32_t* new_pos, const float* q, float* q_rot_scratch, void* k_cache,
-                   void* v_cache, const int32_t* seq_lens, float* scores, int split_tokens, void* ws, size_t ws_bytes,
-                   hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
+                   void* v_cache, const int32_t* seq_lens, float* out, float* scores, int split_tokens, void* ws,
+                   size_t ws_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
     using namespace tq;
     if (!L || L->k_format == TQ_FMT_TQ3K) return L ? TQ_ERR_UNSUPPORTED : TQ_ERR_INVALID;  // TQ3K needs S
     if (!q || !aligned(q, 16) || !aligned(q_rot_scratch, 16) || (start == nullptr) != (stop == nullptr))
         return TQ_ERR_INVALID;
+    if (out && !aligned(out, 4)) return TQ_ERR_INVALID;
     if (!k_new || !v_new || !new_pos || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(new_pos, 4))
         return TQ_ERR_INVALID;
     DecodeArgs a;
@@ -1767,13 +1970,13 @@ int tq_decode_step(const tq_layout* L, const tq_codebook* cbk, const tq_codebook
         a.new_pos = new_pos;
         a.k_wr = static_cast<uint8_t*>(k_cache);
         a.v_wr = static_cast<uint8_t*>(v_cache);
-        return dispatch_partial(a, L, *cbk, *cbv, l);
+        return run_partial(a, L, *cbk, *cbv, l, out);
     }
     // the new rows as a ring of one slot per stream, flushed at new_pos; then the rotation
     st = tq_ring_flush(L, cbk, cbv, nullptr, 1, k_new, v_new, new_pos, 1, k_cache, v_cache, stream);
     if (st != TQ_OK) return st;
     st = tq_rotate_sketch_query(L, cbk, nullptr, q, q_rot_scratch, nullptr, stream);
-    return st != TQ_OK ? st : dispatch_partial(a, L, *cbk, *cbv, l);
+    return st != TQ_OK ? st : run_partial(a, L, *cbk, *cbv, l, out);
 }
 
 int tq_decode_partial_sparse_v(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
@@ -1800,7 +2003,10 @@ int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_toke
 int tq_decode_attention(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const float* q_rot,
                         const float* q_sketch, const void* k_cache, const void* v_cache, const int32_t* seq_lens,
                         float* out, float* scores, int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream) {
-    if (!out) return TQ_ERR_INVALID;
+    if (!out || !tq::aligned(out, 4)) return TQ_ERR_INVALID;
+    // two launches: at the c4 shape (one round of workgroups) a separate combine costs less
+    // than the in-launch merge's tail, whose record stores, arrival and record loads are three
+    // memory round trips after the last workgroup of a stream (100.7 against 102.4 us a step)
     int st = tq_decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, scores, split_tokens, ws,
                                ws_bytes, stream);
     if (st != TQ_OK) return st;

@@ -33,6 +33,29 @@ inline DevCodebook to_dev(const tq_codebook& cb) {
     return d;
 }
 
+// Byte layout of a decode workspace with `splits` records per (b, query head) row:
+//   [0, acc)      float2 ml[B][Hq][splits]          (m, l) of every split record
+//   [acc, cnt)    float  acc[B][Hq][splits][d]      unnormalized value sums
+//   [cnt, total)  uint32 arrivals[B][Hkv]           workgroups of a stream done so far
+// Each region starts on a 256-byte boundary.  The arrival counters serve the decodes
+// that merge the records in the same launch: the last workgroup of a stream to arrive
+// merges it and sets its counter back to zero, so the counters are zero between calls
+// once they have been cleared after allocation.
+struct WsLayout {
+    size_t acc, cnt, total;
+};
+
+constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WsLayout ws_layout(const tq_layout& L, int splits) {
+    const size_t recs = static_cast<size_t>(L.batch) * L.n_q_heads * splits;
+    WsLayout w{};
+    w.acc = round_up(recs * 8, 256);
+    w.cnt = w.acc + round_up(recs * static_cast<size_t>(L.head_dim) * 4, 256);
+    w.total = w.cnt + round_up(static_cast<size_t>(L.batch) * L.n_kv_heads * 4, 256);
+    return w;
+}
+
 // The capture ring a hybrid read attends over besides the compressed records.
 struct RingView {
     const float* q_rot;
@@ -47,6 +70,9 @@ struct RingView {
 // and the capture ring when one is given; normalize, rotate back (tq_combine.hip).
 int combine(const tq_layout* L, const tq_codebook* cbk, const tq_codebook& cbv, int splits, const void* ws,
             float* out, hipStream_t stream, const RingView* ring = nullptr);
+
+// Zero n words of device memory with a fill kernel (graph-capturable, unlike a memset node).
+int clear_words(uint32_t* p, size_t n, hipStream_t stream);
 
 size_t vector_bytes(int format, int d);
 bool is_rotated(int format);

@@ -110,18 +110,18 @@ __device__ __forceinline__ void pq4_encode(const uint4 (&raw)[D / LANES / 8], co
 
 // Lane l's part of the row's 68-byte blocks at out: coordinates CPL l .. lie in block
 // (CPL l) / 128, their codes from byte 4 + (CPL l % 128) / 2; the lane that starts a
-// block also writes its [fp16 norm][2 zero bytes].
+// block also writes its [fp16 norm][2 zero bytes].  A row starts at a multiple of 68
+// bytes, so only 4-byte alignment is known: the code words are stored as dwords (the
+// compiler joins them into one wide store, which the hardware allows at that alignment).
 template <int D, int LANES>
 __device__ __forceinline__ void pq4_store(uint8_t* out, int l, uint32_t n16, const uint32_t (&words)[D / LANES / 8]) {
     constexpr int CPL = D / LANES;
     uint8_t* bp = out + 68 * ((CPL * l) / 128);
     const int cofs = 4 + ((CPL * l) % 128) / 2;
     if ((CPL * l) % 128 == 0) *reinterpret_cast<uint32_t*>(bp) = n16;
-    if constexpr (CPL == 16) {
-        *reinterpret_cast<uint2*>(bp + cofs) = make_uint2(words[0], words[1]);
-    } else {
-        *reinterpret_cast<uint4*>(bp + cofs) = make_uint4(words[0], words[1], words[2], words[3]);
-    }
+    uint32_t* cw = reinterpret_cast<uint32_t*>(bp + cofs);
+#pragma unroll
+    for (int i = 0; i < CPL / 8; ++i) cw[i] = words[i];
 }
 
 }  // namespace tq

@@ -208,9 +208,29 @@ int tq_rotate_sketch_query(const tq_layout* L, const tq_codebook* cbk, const flo
 /* Number of context splits and workspace bytes of a decode call.
  *   split_tokens  tokens per split, a multiple of 256, or 0 for the
  *                 library's choice (enough splits to fill the GPU)
+ * Workspace layout (each region starts at a multiple of 256 bytes):
+ *   float2 ml[B][Hq][splits]  (m, l) of every split record
+ *   float  acc[B][Hq][splits][d]
+ *   uint32 arrivals[B][Hkv]   per-stream arrival counters of the one-launch
+ *                             decode (tq_decode_step with an output), which
+ *                             merges the records in the launch that writes
+ *                             them ([P2] trick 3: the split states are
+ *                             combined once at the end); they must be zero
+ *                             when such a decode starts, and every such
+ *                             decode leaves them zero.
+ *                             tq_decode_workspace_init clears them once
+ *                             after allocation (a zero-filled allocation
+ *                             does too).
  * Returns 0 on invalid input.                                             */
 int tq_decode_splits(const tq_layout* L, int split_tokens);
 size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens);
+
+/* Clear the arrival counters of a workspace (a fill kernel on `stream`, so
+ * the call may be captured in a graph).  Needed once after allocation before
+ * tq_decode_step with an output; the records need no initialization.  Errors: TQ_ERR_INVALID (layout, split length, null or
+ * misaligned ws), TQ_ERR_WORKSPACE (ws_bytes too small), TQ_ERR_HIP.     */
+int tq_decode_workspace_init(const tq_layout* L, int split_tokens, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* Fused decode attention over the compressed caches, one query token per
  * sequence: for query head g of sequence b, with h = g / (Hq/Hkv) and
@@ -230,7 +250,8 @@ size_t tq_decode_workspace_bytes(const tq_layout* L, int split_tokens);
  *               written for i < N (the score-only path of [P2] tricks 1-2)
  *   split_tokens  as for tq_decode_splits
  *   ws, ws_bytes  device workspace of at least tq_decode_workspace_bytes
- * Equivalent to tq_decode_partial followed by tq_decode_combine.
+ * Equivalent to tq_decode_partial followed by tq_decode_combine (two
+ * launches; tq_decode_step with an output merges in one launch instead).
  * Errors: TQ_ERR_INVALID, TQ_ERR_UNSUPPORTED, TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 int tq_decode_attention(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
                         const float* q_rot, const float* q_sketch, const void* k_cache,
@@ -288,21 +309,36 @@ int tq_decode_partial_from_query(const tq_layout* L, const tq_codebook* cbk, con
 /* One decode step: append one new token per (sequence, KV head), then the
  * partial from the unrotated query, as tq_ring_flush of a one-slot ring (the
  * write path of [P2]: quantize on the way in, [P1] section 5 format)
- * followed by tq_decode_partial_from_query.  Where the kernel rotates the
- * query itself (the layouts named there) it also encodes and writes the new
- * rows, with the write kernel's arithmetic, so the cache bytes and the
- * records equal those of the separate calls bit for bit, in one launch.
+ * followed by tq_decode_partial_from_query, and with `out` the merge of
+ * tq_decode_combine.  Where the kernel rotates the query itself (the layouts
+ * named there) it also encodes and writes the new rows, with the write
+ * kernel's arithmetic, so the cache bytes and the records equal those of the
+ * separate calls bit for bit, in one launch.  With `out`, the PQ4 kernels at
+ * d 128 (four query heads per KV head, or eight with one centroid table)
+ * merge each (b, kv-head) stream's split records in the workgroup that
+ * finishes the stream last, with the combine's arithmetic (the output equals
+ * the combine's bit for bit at four heads per KV head), so the whole step is
+ * one launch; other layouts run the combine after the partial.  One launch
+ * saves the second launch but adds a tail of three memory round trips after
+ * a stream's last workgroup (record stores, arrival, record loads); at
+ * batch 8, 32/8 heads, 65,536 tokens the two launches of the separate calls
+ * measured 1.7 us less per step.  Calls sharing a workspace must not overlap.
  *   k_new, v_new  device fp16 [B][Hkv][d], 16-byte aligned
  *   new_pos       device int32 [B]: position of sequence b's new token;
  *                 < 0, or >= capacity, skips the sequence.  seq_lens must
  *                 count the new token when it is to be attended.
+ *   out           nullable device fp32 [B][Hq][d]: the attention output;
+ *                 then the workspace's arrival counters must be zero
+ *                 (tq_decode_workspace_init).  Null: records only.
  * Other arguments as tq_decode_partial_from_query (k_cache and v_cache are
- * written).  Errors: those of tq_decode_partial_from_query, TQ_ERR_INVALID
- * for null or misaligned new rows or positions.                           */
+ * written); the events bracket the partial kernel (which holds the merge in
+ * the one-launch case).  Errors: those of tq_decode_partial_from_query,
+ * TQ_ERR_INVALID for null or misaligned new rows, positions or output.    */
 int tq_decode_step(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv, const void* k_new,
                    const void* v_new, const int32_t* new_pos, const float* q, float* q_rot_scratch,
-                   void* k_cache, void* v_cache, const int32_t* seq_lens, float* scores, int split_tokens,
-                   void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start, hipEvent_t stop);
+                   void* k_cache, void* v_cache, const int32_t* seq_lens, float* out, float* scores,
+                   int split_tokens, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t start,
+                   hipEvent_t stop);
 
 /* Sparse V.  [P1] "turbo4 post-mortem", section 9 (current state) lists a
  * sparse-V mode as active alongside the 4-bit format; the page gives no rule

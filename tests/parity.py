@@ -202,7 +202,7 @@ def gpu_decode(setup, L, q, k_cache, v_cache, seq_lens, split_tokens=0, want_sco
     q_sk = torch.empty_like(qd) if w.k_format == synth.TQ3K else None
     tq.rotate_sketch_query(L, setup.cbk, setup.S_dev, qd, q_rot, q_sk)
     out = torch.full((L.batch, L.n_q_heads, d), float("nan"), device="cuda")
-    ws = torch.empty(tq.decode_workspace_bytes(L, split_tokens), dtype=torch.uint8, device="cuda")
+    ws = tq.decode_workspace(L, split_tokens)
     scores = torch.full((L.batch, L.n_q_heads, L.capacity), float("nan"), device="cuda") if want_scores else None
     sl = torch.tensor(np.asarray(seq_lens, np.int32), device="cuda")
     tq.decode_attention(L, setup.cbk, setup.cbv, q_rot, q_sk, k_cache, v_cache, sl, out, ws, scores=scores,

@@ -97,7 +97,12 @@ def test_splits_and_workspace_arithmetic():
     assert s >= 1 and 8 * 8 * s >= 1024  # PQ4, d 128, G 4: four splits per workgroup, one per CU
     other = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ3, tq.FMT_PQ3)
     assert 8 * 8 * tq.decode_splits(other) >= 2048  # one split per workgroup elsewhere
-    assert tq.decode_workspace_bytes(L) == 8 * 32 * s * (8 + 4 * 128)
+    # (m, l) records, value sums and one arrival counter per stream, each region 256-byte aligned
+    recs = 8 * 32 * s
+    up = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert tq.decode_workspace_bytes(L) == up(8 * recs) + up(4 * 128 * recs) + up(4 * 8 * 8)
+    odd = tq.Layout(1, 5, 1, 128, 256, tq.FMT_PQ4, tq.FMT_PQ4)  # 5 records: the value sums still start aligned
+    assert tq.decode_workspace_bytes(odd, 256) == 256 + up(5 * 512) + 256
     assert tq.decode_splits(L, 1024) == 64
     assert tq.decode_splits(L, 1000) == 0  # not a multiple of 256
     small = tq.Layout(1, 1, 1, 128, 512, tq.FMT_PQ4, tq.FMT_PQ4)
@@ -146,23 +151,32 @@ def test_device_calls_reject_bad_arguments_before_any_launch():
     assert fq(r(Lt), r(cb), r(cb), fake, fake, fake, fake, fake, None, 0, fake, need, None, None, None) == -2
     # one decode step: the new rows and positions, then the arguments of the partial from the query
     ds = tq.lib.tq_decode_step
-    assert ds(r(L), r(cb), r(cb), None, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need, None, None,
-              None) == -1
+    assert ds(r(L), r(cb), r(cb), None, fake, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need, None,
+              None, None) == -1
     odd = ctypes.c_void_p((1 << 20) + 2)  # not 4-byte aligned
-    assert ds(r(L), r(cb), r(cb), fake, fake, odd, fake, fake, fake, fake, fake, None, 0, fake, need, None,
+    assert ds(r(L), r(cb), r(cb), fake, fake, odd, fake, fake, fake, fake, fake, None, None, 0, fake, need, None,
               None, None) == -1
-    assert ds(r(L), r(cb), r(cb), fake, misaligned, fake, fake, fake, fake, fake, fake, None, 0, fake, need, None,
-              None, None) == -1
-    assert ds(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need - 1, None,
-              None, None) == -3
-    assert ds(r(Lt), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need, None, None,
-              None) == -2
+    assert ds(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, odd, None, 0, fake, need, None,
+              None, None) == -1  # a misaligned output
+    assert ds(r(L), r(cb), r(cb), fake, misaligned, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need,
+              None, None, None) == -1
+    assert ds(r(L), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, fake, None, 0, fake, need - 1,
+              None, None, None) == -3
+    assert ds(r(Lt), r(cb), r(cb), fake, fake, fake, fake, fake, fake, fake, fake, None, None, 0, fake, need, None,
+              None, None) == -2
     # the sparse-V variant checks its arguments like the plain call, and the threshold range
     sv = tq.lib.tq_decode_partial_sparse_v
     assert sv(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, 0.0, fake, need - 1, None) == -3
     assert sv(r(L), r(cb), r(cb), fake, None, misaligned, fake, fake, None, 0, 0.0, fake, need, None) == -1
     for bad in (-1e-3, 1.0001, float("nan"), float("inf")):
         assert sv(r(L), r(cb), r(cb), fake, None, fake, fake, fake, None, 0, bad, fake, need, None) == -1
+    # clearing a workspace's arrival counters: layout, split length, pointer and size first
+    wi = tq.lib.tq_decode_workspace_init
+    assert wi(r(L), 0, None, need, None) == -1
+    assert wi(r(L), 0, misaligned, need, None) == -1
+    assert wi(r(L), 100, fake, need, None) == -1
+    assert wi(r(L), 0, fake, need - 1, None) == -3
+    assert wi(r(Lg), 0, fake, need - 1, None) == -3  # the layout itself is valid; G is checked by the decodes
     assert tq.strerror(-3).startswith("workspace")
 
 
@@ -191,3 +205,24 @@ def test_ring_capacity_limit_matches_the_header():
     text = open(HEADER).read()
     m = re.search(r"#define TQ_RING_CAP_MAX (\d+)", text)
     assert m and int(m.group(1)) == tq.RING_CAP_MAX
+
+
+def test_binding_refuses_bad_tensors_before_the_library():
+    """The binding checks what the C ABI cannot see (device, dtype, layout, size); on the
+    CPU every device argument is refused as not being a GPU tensor."""
+    import torch
+    L = tq.Layout(1, 4, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4)
+    cb, _ = tq.build_codebook(128, 4, 0, 1, 2)
+    cpu = torch.zeros(1 << 16, dtype=torch.uint8)
+    q = torch.zeros(1, 4, 128)
+    with pytest.raises(tq.TQError, match="k_cache must be a GPU tensor") as e:
+        tq.decode_attention(L, cb, cb, q, None, cpu, cpu, torch.zeros(1, dtype=torch.int32), q, cpu)
+    assert e.value.status == -1
+    with pytest.raises(tq.TQError, match="must be a torch tensor"):
+        tq.decode_combine(L, cb, bytearray(1 << 16), q)
+    with pytest.raises(tq.TQError, match="ws is required"):
+        tq.decode_workspace_init(L, None)
+    with pytest.raises(tq.TQError, match="dst_row must be a 1-D int32 tensor"):
+        tq.quantize_append(L, cb, cb, None, None, None, [0, 1], cpu, cpu)
+    with pytest.raises(tq.TQError, match="invalid layout or ring_cap"):
+        tq.ring_append(L, 0, None, None, None, cpu, cpu)

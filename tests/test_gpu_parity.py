@@ -315,8 +315,10 @@ def test_single_key_returns_its_value_on_gpu():
 
 def test_c1_end_to_end():
     """Workload c1 at its full size: append through the HIP encoder, decode,
-    compare with the oracle's encode + attention (index flips, if any, are
-    counted by the write-side check and tolerated by the looser bound)."""
+    compare with the oracle.  The GPU's bytes are first checked against the
+    oracle's encoding of the same rows (codes may differ only on a decision
+    boundary, counted); the oracle then decodes the GPU's own bytes, so the
+    read side holds the output tolerance whatever ties the encoder met."""
     w = synth.C1
     st = P.Setup(w)
     L = st.layout()
@@ -330,16 +332,15 @@ def test_c1_end_to_end():
     out, scores, _, _ = P.gpu_decode(st, L, q, kc, vc, [512])
     ek = st.oracle_encode(synth.K_TENSOR, k[:, 0])
     ev = st.oracle_encode(synth.V_TENSOR, v[:, 0])
-    sk = P.compare_write(st, synth.K_TENSOR, kc.cpu().numpy().reshape(512, 68), ek)
-    sv = P.compare_write(st, synth.V_TENSOR, vc.cpu().numpy().reshape(512, 68), ev)
+    gk, gv = kc.cpu().numpy().reshape(512, 68), vc.cpu().numpy().reshape(512, 68)
+    sk = P.compare_write(st, synth.K_TENSOR, gk, ek)
+    sv = P.compare_write(st, synth.V_TENSOR, gv, ev)
     _say(f"c1 write: {sk} {sv}")
-    kdq = [[st.oracle_dequant(synth.K_TENSOR, ek.blocks)]]
-    vdq = [[st.oracle_dequant(synth.V_TENSOR, ev.blocks)]]
-    if sk["bytes_equal"] and sv["bytes_equal"]:
-        P.check_read(st, q, kdq, vdq, [512], out, scores, 512)
-    else:  # a flipped code moves one coordinate by one centroid step
-        ref, _ = P.oracle_decode(st, q, kdq, vdq, [512])
-        assert P.rel_err_rows(out[0, 0], ref[0, 0]) < 1e-2
+    kdq = [[st.oracle_dequant(synth.K_TENSOR, gk)]]  # validated above: the oracle decodes the GPU's bytes
+    vdq = [[st.oracle_dequant(synth.V_TENSOR, gv)]]
+    ws, wo = P.check_read(st, q, kdq, vdq, [512], out, scores, 512)
+    _say(f"c1 read: worst score err {ws:.2e}, output err {wo:.2e}; code flips K {sk['code_flips']} "
+         f"V {sv['code_flips']}")
 
 
 @pytest.mark.parametrize("d", [128, 256])

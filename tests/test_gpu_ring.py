@@ -236,16 +236,24 @@ def test_ring_lifecycle_append_flush_read():
                                        torch.tensor(n, dtype=torch.int32, device="cuda"), out, ws)
             torch.cuda.synchronize()
             o = out.cpu().numpy()
+            gk = kc.view(B, H, w.capacity, st.vbk).cpu().numpy()
+            gv = vc.view(B, H, w.capacity, st.vbv).cpu().numpy()
+            flips = 0
             for b in range(B):
-                for g in range(w.n_q_heads):
-                    h = g // w.group
+                for h in range(H):
+                    # the GPU encoder wrote the compressed rows (prefill and flushes): checked
+                    # against the oracle's encoding of the same fp16 rows, then decoded by the
+                    # oracle from the GPU's own bytes, so the read bound holds unchanged
                     ek = st.oracle_encode(synth.K_TENSOR, _rows(w, synth.K_TENSOR, b, h, 0, comp[b]))
                     ev = st.oracle_encode(synth.V_TENSOR, _rows(w, synth.V_TENSOR, b, h, 0, comp[b]))
-                    ref, _ = P.oatt.hybrid_attention(
-                        q[b, g], st.oracle_dequant(synth.K_TENSOR, ek.blocks), st.oracle_dequant(synth.V_TENSOR, ev.blocks),
-                        _rows(w, synth.K_TENSOR, b, h, comp[b], n[b]).astype(np.float64),
-                        _rows(w, synth.V_TENSOR, b, h, comp[b], n[b]).astype(np.float64))
-                    # the GPU encoder wrote the compressed rows: rare boundary flips move a code,
-                    # so the bound is the end-to-end one of the append tests (5x the read bound)
-                    assert P.rel_err_rows(o[b, g], ref) <= 5 * P.OUT_TOL, (step, b, g)
-            _say(f"  step {step}: comp={comp} ring={n} ok")
+                    sk = P.compare_write(st, synth.K_TENSOR, gk[b, h, :comp[b]], ek)
+                    sv = P.compare_write(st, synth.V_TENSOR, gv[b, h, :comp[b]], ev)
+                    flips += sk["code_flips"] + sv["code_flips"]
+                    kd = st.oracle_dequant(synth.K_TENSOR, gk[b, h, :comp[b]])
+                    vd = st.oracle_dequant(synth.V_TENSOR, gv[b, h, :comp[b]])
+                    for g in range(h * w.group, (h + 1) * w.group):
+                        ref, _ = P.oatt.hybrid_attention(
+                            q[b, g], kd, vd, _rows(w, synth.K_TENSOR, b, h, comp[b], n[b]).astype(np.float64),
+                            _rows(w, synth.V_TENSOR, b, h, comp[b], n[b]).astype(np.float64))
+                        assert P.rel_err_rows(o[b, g], ref) <= P.OUT_TOL, (step, b, g)
+            _say(f"  step {step}: comp={comp} ring={n} ok (boundary code flips {flips})")
