@@ -19,10 +19,12 @@ from ._binding import (  # noqa: F401
     Codebook,
     Layout,
     RING_CAP_MAX,
+    STATIC_SCRATCH_BYTES,
     TQError,
     build_codebook,
     cache_bytes,
     decode_attention,
+    decode_attention_static,
     decode_attention_hybrid,
     decode_combine,
     decode_hybrid_workspace_bytes,

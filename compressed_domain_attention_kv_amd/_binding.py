@@ -113,6 +113,8 @@ lib.tq_decode_workspace_init.restype = _I
 lib.tq_decode_workspace_init.argtypes = [_PL, _I, _P, _SZ, _P]
 lib.tq_decode_attention.restype = _I
 lib.tq_decode_attention.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]
+lib.tq_decode_attention_static.restype = _I
+lib.tq_decode_attention_static.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P]
 lib.tq_decode_partial.restype = _I
 lib.tq_decode_partial.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _P, _I, _P, _SZ, _P]
 lib.tq_decode_partial_timed.restype = _I
@@ -137,6 +139,7 @@ lib.tq_decode_attention_hybrid.restype = _I
 lib.tq_decode_attention_hybrid.argtypes = [_PL, _PC, _PC, _P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _P, _SZ, _P]
 
 RING_CAP_MAX = 256
+STATIC_SCRATCH_BYTES = 8 << 20
 
 
 class TQError(RuntimeError):
@@ -322,6 +325,15 @@ def decode_attention(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, o
     _check(lib.tq_decode_attention(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), *common,
                                    _dev(out, "out", w, _rows(L), _F32), _scores(L, scores, w), split_tokens,
                                    *_ws(L, ws, split_tokens, w), _stream(stream)), w)
+
+
+def decode_attention_static(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, out, split_tokens=0,
+                            stream=None):
+    """tq_decode_attention with the library's own device scratch instead of a workspace."""
+    w = "tq_decode_attention_static"
+    common = _decode_common(L, q_rot, q_sketch, k_cache, v_cache, seq_lens, None, w)
+    _check(lib.tq_decode_attention_static(ctypes.byref(L), ctypes.byref(cbk), ctypes.byref(cbv), *common,
+                                          _dev(out, "out", w, _rows(L), _F32), split_tokens, _stream(stream)), w)
 
 
 def decode_partial(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, ws, scores=None, split_tokens=0,

@@ -18,6 +18,7 @@
 #include <hip/hip_ext.h>
 
 #include <cmath>
+#include <mutex>
 #include <utility>
 
 #include "tq_device.h"
@@ -2033,3 +2034,53 @@ int tq_decode_attention_hybrid(const tq_layout* L, const tq_codebook* cbk, const
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate device memory
+// (code under graph capture, tight serving loops): the split records live in a
+// file-scope device array of fixed size, one copy per GPU the library runs on.  Its
+// address is taken once per device (the array's name in host code is only a host-side
+// stand-in) and kept per device.  All calls on one GPU share the array: calls that
+// overlap on one GPU race.  The two-launch decode needs nothing in it to start at zero.
+
+namespace tq {
+namespace {
+
+constexpr size_t kStaticScratchBytes = TQ_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+
+// The current device's copy of the scratch array (taken with that device current).
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return TQ_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TQ_OK;
+}
+
+}  // namespace
+}  // namespace tq
+
+extern "C" int tq_decode_attention_static(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
+                                          const float* q_rot, const float* q_sketch, const void* k_cache,
+                                          const void* v_cache, const int32_t* seq_lens, float* out,
+                                          int split_tokens, hipStream_t stream) {
+    using namespace tq;
+    const size_t need = workspace_bytes(L, split_tokens);
+    if (need == 0) return L && check_layout(L) != TQ_OK ? check_layout(L) : TQ_ERR_INVALID;
+    if (need > kStaticScratchBytes) return TQ_ERR_WORKSPACE;  // before any HIP call
+    void* ws = nullptr;
+    const int st = scratch_of_current_device(&ws);
+    if (st != TQ_OK) return st;
+    return tq_decode_attention(L, cbk, cbv, q_rot, q_sketch, k_cache, v_cache, seq_lens, out, nullptr, split_tokens,
+                               ws, kStaticScratchBytes, stream);
+}

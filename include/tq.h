@@ -368,6 +368,25 @@ int tq_decode_partial_sparse_v(const tq_layout* L, const tq_codebook* cbk, const
 int tq_decode_combine(const tq_layout* L, const tq_codebook* cbv, int split_tokens, const void* ws,
                       size_t ws_bytes, float* out, hipStream_t stream);
 
+/* Decode attention that allocates nothing, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation): tq_decode_attention (without scores) with its
+ * workspace in a library-owned device array of TQ_STATIC_SCRATCH_BYTES bytes,
+ * one copy per GPU, held until the process ends.  The call runs on the
+ * current device; its first call on a device looks up that device's copy.
+ * Every call on a GPU shares that GPU's array and leaves the last call's split
+ * records in it, so calls that overlap on one GPU (other streams, other host
+ * threads) race; nothing in the array needs to start at zero.  The caller
+ * still owns and passes inputs and outputs, as for tq_decode_attention.
+ * Errors: those of tq_decode_attention; TQ_ERR_WORKSPACE, before any device
+ * work, when tq_decode_workspace_bytes(L, split_tokens) exceeds
+ * TQ_STATIC_SCRATCH_BYTES; TQ_ERR_HIP if the array cannot be found.      */
+#define TQ_STATIC_SCRATCH_BYTES (8u << 20)
+int tq_decode_attention_static(const tq_layout* L, const tq_codebook* cbk, const tq_codebook* cbv,
+                               const float* q_rot, const float* q_sketch, const void* k_cache,
+                               const void* v_cache, const int32_t* seq_lens, float* out, int split_tokens,
+                               hipStream_t stream);
+
 /* ---- Capture ring and hybrid attention --------------------------------
  * [P2] "write path": the capture step keeps the newest tokens exact in a
  * ring buffer and quantizes the oldest batch into compressed blocks only

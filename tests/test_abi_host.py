@@ -226,3 +226,21 @@ def test_binding_refuses_bad_tensors_before_the_library():
         tq.quantize_append(L, cb, cb, None, None, None, [0, 1], cpu, cpu)
     with pytest.raises(tq.TQError, match="invalid layout or ring_cap"):
         tq.ring_append(L, 0, None, None, None, cpu, cpu)
+
+
+def test_static_decode_refuses_layouts_beyond_its_scratch():
+    """tq_decode_attention_static checks the workspace its layout needs against the size
+    of the library's device array before any device call (none happens here)."""
+    r = ctypes.byref
+    cb, _ = tq.build_codebook(128, 4, 0, 1, 2)
+    fake = ctypes.c_void_p(1 << 20)
+    big = tq.Layout(8, 64, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
+    assert tq.decode_workspace_bytes(big, 256) > tq.STATIC_SCRATCH_BYTES
+    f = tq.lib.tq_decode_attention_static
+    assert f(r(big), r(cb), r(cb), fake, None, fake, fake, fake, fake, 256, None) == -3
+    assert f(r(big), r(cb), r(cb), fake, None, fake, fake, fake, fake, 100, None) == -1  # split not a multiple of 256
+    bad = tq.Layout(1, 3, 2, 128, 128, tq.FMT_PQ4, tq.FMT_PQ4)
+    assert f(r(bad), r(cb), r(cb), fake, None, fake, fake, fake, fake, 0, None) == -1
+    text = open(HEADER).read()
+    m = re.search(r"#define TQ_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == tq.STATIC_SCRATCH_BYTES
