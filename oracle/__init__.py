@@ -20,7 +20,7 @@ Modules
 codebook   scalar quantizer tables for N(0, 1/d) (quantile means, Lloyd-Max)
 prng       splitmix64 stream, rotation signs, Box-Muller QJL matrix
 rotation   Walsh-Hadamard + random-sign rotation
-formats    encoders / block packers / decoders for PQ4, PQ3, TQ3K, GQ2V
+formats    encoders / block packers / decoders for PQ4, PQ3, TQ3K, GQ2V, GQ4V
 attention  textbook softmax attention over dequantized caches, split/combine
 
 Every function here is pinned by ``tests/test_oracle_*.py`` to something other

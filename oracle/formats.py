@@ -24,6 +24,12 @@ GQ2V 2-bit asymmetric group quantization of values, groups of 32 channels
      ("TurboQuant Triton deep dive", trick 3 and write path: v*scale+zero,
      bit packed): per group [fp16 scale][fp16 zero][q: 8 bytes, packed like
      the PQ3 low bits] = 12 bytes.
+GQ4V the same group quantization with 4-bit codes ("TurboQuant Triton deep
+     dive", write path: the value cache is group-quantized at 2 or 4 bits;
+     limits: 4-bit values where quality matters): per group
+     [fp16 scale][fp16 zero][q: 16 bytes, channel j of the group in byte
+     j/2, low nibble when j is even, the nibble order of the PQ4 block] =
+     20 bytes.
 
 The encoders work in float64 and round only where a format stores a value
 (fp16 norms, scales and zeros) or where a decision is taken (fp32 rotated
@@ -37,7 +43,7 @@ import numpy as np
 from . import codebook as cbmod
 from . import rotation
 
-PQ4, PQ3, TQ3K, GQ2V = 1, 2, 3, 4
+PQ4, PQ3, TQ3K, GQ2V, GQ4V = 1, 2, 3, 4, 5
 FP16_MAX = 65504.0
 GROUP = 32  # GQ2V channels per group
 QJL_CONST = np.sqrt(np.pi / 2.0)  # estimator scale is sqrt(pi/2)/d
@@ -55,6 +61,8 @@ def vector_bytes(fmt, d):
         return 4 + d // 4 + d // 8
     if fmt == GQ2V:
         return 12 * (d // GROUP)
+    if fmt == GQ4V:
+        return 20 * (d // GROUP)
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -348,6 +356,54 @@ def unpack_gq2v(blocks, d):
     return scale, zero, q
 
 
+def encode_gq4v(v16):
+    """GQ4V write path: per 32-channel group, min/max asymmetric 4-bit codes.
+
+    zero = fp16(min); scale = fp16(fp32(max - min) / 15); the code is
+    clamp(rint(fp32(v - zero) * fp32(1/scale)), 0, 15) in fp32 with
+    round-half-even, or 0 when the stored scale is zero; the decoder computes
+    q*scale + zero ("TurboQuant Triton deep dive", trick 3 and write path).
+    """
+    v = np.asarray(v16, dtype=np.float16)
+    n, d = v.shape
+    out = np.zeros((n, vector_bytes(GQ4V, d)), dtype=np.uint8)
+    codes = np.zeros((n, d), dtype=np.int64)
+    for g in range(d // GROUP):
+        grp = v[:, GROUP * g:GROUP * (g + 1)].astype(np.float32)
+        mn = grp.min(axis=1)
+        mx = grp.max(axis=1)
+        zero16 = mn.astype(np.float16)
+        scale16 = ((mx - mn) / np.float32(15.0)).astype(np.float16)
+        z32 = zero16.astype(np.float32)
+        s32 = scale16.astype(np.float32)
+        with np.errstate(divide="ignore"):
+            inv = np.where(s32 > 0, np.float32(1.0) / np.where(s32 > 0, s32, np.float32(1.0)),
+                           np.float32(0.0)).astype(np.float32)
+        t = ((grp - z32[:, None]).astype(np.float32) * inv[:, None]).astype(np.float32)
+        q = np.clip(np.rint(t), 0, 15).astype(np.int64)
+        q[s32 == 0] = 0
+        codes[:, GROUP * g:GROUP * (g + 1)] = q
+        base = 20 * g
+        sb, zb = scale16.view(np.uint16), zero16.view(np.uint16)
+        out[:, base], out[:, base + 1] = sb & 0xFF, sb >> 8
+        out[:, base + 2], out[:, base + 3] = zb & 0xFF, zb >> 8
+        out[:, base + 4:base + 20] = pack_nibbles(q)
+    return Encoded(out, np.zeros(n), np.zeros((n, 0)), codes, {})
+
+
+def unpack_gq4v(blocks, d):
+    n = blocks.shape[0]
+    scale = np.zeros((n, d // GROUP))
+    zero = np.zeros((n, d // GROUP))
+    q = np.zeros((n, d), dtype=np.int64)
+    for g in range(d // GROUP):
+        base = 20 * g
+        scale[:, g] = _fp16_from_bytes(blocks[:, base], blocks[:, base + 1])
+        zero[:, g] = _fp16_from_bytes(blocks[:, base + 2], blocks[:, base + 3])
+        q[:, GROUP * g:GROUP * (g + 1)] = unpack_nibbles(blocks[:, base + 4:base + 20], GROUP)
+    return scale, zero, q
+
+
 # ----------------------------------------------------------------------------
 # decoders (dequantize to float64 in the original, unrotated space)
 
@@ -376,6 +432,11 @@ def dequant_gq2v(blocks, d):
     return q * np.repeat(scale, GROUP, axis=1) + np.repeat(zero, GROUP, axis=1)
 
 
+def dequant_gq4v(blocks, d):
+    scale, zero, q = unpack_gq4v(blocks, d)
+    return q * np.repeat(scale, GROUP, axis=1) + np.repeat(zero, GROUP, axis=1)
+
+
 def dequant(blocks, fmt, d, tabs=None, signs=None, S=None):
     if fmt in (PQ4, PQ3):
         return dequant_rotated(blocks, fmt, d, tabs, signs)
@@ -383,4 +444,6 @@ def dequant(blocks, fmt, d, tabs=None, signs=None, S=None):
         return dequant_tq3k(blocks, d, tabs, signs, S)
     if fmt == GQ2V:
         return dequant_gq2v(blocks, d)
+    if fmt == GQ4V:
+        return dequant_gq4v(blocks, d)
     raise ValueError(f"unknown format {fmt}")
