@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     CB_LLOYD_MAX,
     CB_QUANTILE_MEAN,
     FMT_GQ2V,
+    FMT_GQ4V,
     FMT_PQ3,
     FMT_PQ4,
     FMT_TQ3K,

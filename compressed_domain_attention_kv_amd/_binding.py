@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-FMT_PQ4, FMT_PQ3, FMT_TQ3K, FMT_GQ2V = 1, 2, 3, 4
+FMT_PQ4, FMT_PQ3, FMT_TQ3K, FMT_GQ2V, FMT_GQ4V = 1, 2, 3, 4, 5
 CB_QUANTILE_MEAN, CB_LLOYD_MAX = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))

@@ -348,7 +348,7 @@ int combine(const tq_layout* L, const tq_codebook* cbk, const tq_codebook& cbv, 
         rmax = ring->ring_cap <= 128 ? 128 : 256;
     }
     const int rows = L->batch * L->n_q_heads;
-    const bool rot = L->v_format != TQ_FMT_GQ2V;
+    const bool rot = !is_group_quant(L->v_format);
     const DevCodebook cv = to_dev(cbv), ck = cbk ? to_dev(*cbk) : cv;
     if (L->head_dim == 128) {
         if (rot) launch_combine<128, true>(a, rows, rmax, ck, cv, stream);

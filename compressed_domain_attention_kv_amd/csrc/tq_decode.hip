@@ -34,7 +34,8 @@ constexpr int vbytes() {
     return FMT == TQ_FMT_PQ4 ? 68 * (D / 128)
          : FMT == TQ_FMT_PQ3 ? 14 * (D / 32)
          : FMT == TQ_FMT_TQ3K ? 4 + D / 4 + D / 8
-                              : 12 * (D / kGroup);
+         : FMT == TQ_FMT_GQ2V ? 12 * (D / kGroup)
+                              : 20 * (D / kGroup);
 }
 
 struct DecodeArgs {
@@ -317,7 +318,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
 #pragma unroll
                     for (int k = 0; k < DPL; ++k)
                         val[k] = n * sm.vtab[((lo >> (2 * k)) & 3u) | (((hi >> k) & 1u) << 2)];
-                } else {  // GQ2V
+                } else if constexpr (VF == TQ_FMT_GQ2V) {
                     constexpr int LPG = kGroup / DPL;
                     const int grp = lane / LPG, jb = DPL * (lane % LPG);
                     const uint8_t* gp = vb + 12 * grp;
@@ -326,6 +327,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
                     const uint32_t q = gp[4 + jb / 4] >> (2 * (jb % 4));
 #pragma unroll
                     for (int k = 0; k < DPL; ++k) val[k] = fmaf(static_cast<float>((q >> (2 * k)) & 3u), sc, zr);
+                } else {  // GQ4V: nibble codes, channel j of a group in byte j/2
+                    constexpr int LPG = kGroup / DPL;
+                    const int grp = lane / LPG, jb = DPL * (lane % LPG);
+                    const uint8_t* gp = vb + 20 * grp;
+                    const uint32_t sz = *reinterpret_cast<const uint32_t*>(gp);
+                    const float sc = half_bits_to_float(sz & 0xFFFFu), zr = half_bits_to_float(sz >> 16);
+                    // DPL nibbles from byte jb / 2 on (jb is a multiple of DPL: aligned reads)
+                    const uint32_t q = DPL == 2 ? gp[4 + jb / 2] : *reinterpret_cast<const uint16_t*>(gp + 4 + jb / 2);
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k) val[k] = fmaf(static_cast<float>((q >> (4 * k)) & 15u), sc, zr);
                 }
 #pragma unroll
                 for (int g = 0; g < G; ++g)
@@ -1879,6 +1890,7 @@ int dispatch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook&
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ3>(a, L, cbk, cbv, stream);
     if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) return dispatch_dim<TQ_FMT_PQ3, TQ_FMT_PQ4>(a, L, cbk, cbv, stream);
     if (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V) return dispatch_dim<TQ_FMT_TQ3K, TQ_FMT_GQ2V>(a, L, cbk, cbv, stream);
+    if (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ4V) return dispatch_dim<TQ_FMT_TQ3K, TQ_FMT_GQ4V>(a, L, cbk, cbv, stream);
     return TQ_ERR_UNSUPPORTED;
 }
 

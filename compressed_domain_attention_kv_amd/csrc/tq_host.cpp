@@ -125,11 +125,14 @@ size_t vector_bytes(int format, int d) {
         case TQ_FMT_PQ3: return static_cast<size_t>(14) * (d / 32);
         case TQ_FMT_TQ3K: return static_cast<size_t>(4 + d / 4 + d / 8);
         case TQ_FMT_GQ2V: return static_cast<size_t>(12) * (d / kGroup);
+        case TQ_FMT_GQ4V: return static_cast<size_t>(20) * (d / kGroup);
         default: return 0;
     }
 }
 
 bool is_rotated(int format) { return format == TQ_FMT_PQ4 || format == TQ_FMT_PQ3 || format == TQ_FMT_TQ3K; }
+
+bool is_group_quant(int format) { return format == TQ_FMT_GQ2V || format == TQ_FMT_GQ4V; }
 
 int format_bits(int format) {
     switch (format) {
@@ -151,7 +154,8 @@ int check_layout(const tq_layout* L) {
     if (L->head_dim != 128 && L->head_dim != 256) return TQ_ERR_UNSUPPORTED;
     const int kf = L->k_format, vf = L->v_format;
     const bool ok = (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) || (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) ||
-                    (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) || (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V);
+                    (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) || (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ2V) ||
+                    (kf == TQ_FMT_TQ3K && vf == TQ_FMT_GQ4V);
     if (!ok) return TQ_ERR_UNSUPPORTED;
     // every byte offset of a cache must fit in 63 bits and every index in 31
     const double vecs = static_cast<double>(L->batch) * L->n_kv_heads * L->capacity;
@@ -161,7 +165,7 @@ int check_layout(const tq_layout* L) {
 
 int check_codebook(const tq_codebook* cb, int format, int d) {
     if (!cb) return TQ_ERR_INVALID;
-    if (format == TQ_FMT_GQ2V) return TQ_OK;
+    if (is_group_quant(format)) return TQ_OK;  // no table: scale and zero per group
     if (cb->head_dim != d) return TQ_ERR_INVALID;
     if (cb->bits != format_bits(format) || cb->n_levels != (1 << cb->bits)) return TQ_ERR_INVALID;
     return TQ_OK;

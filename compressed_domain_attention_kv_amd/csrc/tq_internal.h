@@ -9,7 +9,7 @@
 
 namespace tq {
 
-constexpr int kGroup = 32;        // GQ2V channels per group
+constexpr int kGroup = 32;        // GQ2V / GQ4V channels per group
 constexpr int kTile = 64;         // tokens per wavefront tile in the decode kernel
 constexpr int kWaves = 4;         // wavefronts per decode workgroup
 constexpr int kSplitQuantum = kTile * kWaves;
@@ -76,6 +76,7 @@ int clear_words(uint32_t* p, size_t n, hipStream_t stream);
 
 size_t vector_bytes(int format, int d);
 bool is_rotated(int format);
+bool is_group_quant(int format);  // GQ2V, GQ4V: per-group scale and zero, no rotation
 int format_bits(int format);  // code bits per coordinate a format stores in its table
 int check_layout(const tq_layout* L);
 int check_codebook(const tq_codebook* cb, int format, int d);

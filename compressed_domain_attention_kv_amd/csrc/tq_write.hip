@@ -84,13 +84,16 @@ template <>
 struct FormatTraits<TQ_FMT_TQ3K> { static constexpr int kLevels = 4; };
 template <>
 struct FormatTraits<TQ_FMT_GQ2V> { static constexpr int kLevels = 4; };
+template <>
+struct FormatTraits<TQ_FMT_GQ4V> { static constexpr int kLevels = 16; };
 
 template <int FMT, int D>
 constexpr int vec_bytes_c() {
     return FMT == TQ_FMT_PQ4 ? 68 * (D / 128)
          : FMT == TQ_FMT_PQ3 ? 14 * (D / 32)
          : FMT == TQ_FMT_TQ3K ? 4 + D / 4 + D / 8
-                              : 12 * (D / kGroup);
+         : FMT == TQ_FMT_GQ2V ? 12 * (D / kGroup)
+                              : 20 * (D / kGroup);
 }
 
 // Vectors per lane group handled by one workgroup pass: every one of them has its
@@ -186,8 +189,11 @@ __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook
     }
 
     uint8_t* dst = a.out + tg.off;
-    if constexpr (FMT == TQ_FMT_GQ2V) {
-        // asymmetric 2-bit group quantization, groups of 32 channels = 4 lanes
+    if constexpr (FMT == TQ_FMT_GQ2V || FMT == TQ_FMT_GQ4V) {
+        // asymmetric 2- or 4-bit group quantization, groups of 32 channels = 4 lanes:
+        // zero = min, scale = (max - min) / (levels - 1), codes by rounding to the grid
+        constexpr int QMAX = FormatTraits<FMT>::kLevels - 1, QB = FMT == TQ_FMT_GQ2V ? 2 : 4;
+        constexpr int GB = 4 + kGroup * QB / 8;  // bytes per group
         float mn = v[0], mx = v[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) { mn = fminf(mn, v[e]); mx = fmaxf(mx, v[e]); }
@@ -197,7 +203,7 @@ __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook
             mx = fmaxf(mx, __shfl_xor(mx, m, LPV));
         }
         const uint32_t z16 = float_to_half_bits(mn);  // exact: mn is an fp16 value
-        const uint32_t s16 = float_to_half_bits(__fdiv_rn(mx - mn, 3.0f));
+        const uint32_t s16 = float_to_half_bits(__fdiv_rn(mx - mn, static_cast<float>(QMAX)));
         const float z = half_bits_to_float(z16), s = half_bits_to_float(s16);
         const float inv = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
         uint32_t packed = 0;
@@ -206,15 +212,16 @@ __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook
             uint32_t q = 0;
             if (s > 0.0f) {
                 const float t = rintf((v[e] - z) * inv);
-                q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), 3.0f));
+                q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), static_cast<float>(QMAX)));
             }
-            packed |= q << (2 * e);
+            packed |= q << (QB * e);
         }
         if (active) {
             const int grp = l >> 2, lg = l & 3;
-            uint8_t* g = dst + 12 * grp;
+            uint8_t* g = dst + GB * grp;
             if (lg == 0) *reinterpret_cast<uint32_t*>(g) = s16 | (z16 << 16);
-            *reinterpret_cast<uint16_t*>(g + 4 + 2 * lg) = static_cast<uint16_t>(packed);
+            if constexpr (QB == 2) *reinterpret_cast<uint16_t*>(g + 4 + 2 * lg) = static_cast<uint16_t>(packed);
+            else *reinterpret_cast<uint32_t*>(g + 4 + 4 * lg) = packed;
         }
     } else {
         constexpr float kInvSqrtD = D == 256 ? 0.0625f : 0.08838834764831845f;
@@ -548,6 +555,9 @@ int dispatch_quantize(int fmt, int d, const WriteArgs& a, const tq_codebook& cb,
         if (fmt == TQ_FMT_GQ2V)
             return d == 128 ? launch_quantize<TQ_FMT_GQ2V, 128, SRC>(a, cb, st)
                             : launch_quantize<TQ_FMT_GQ2V, 256, SRC>(a, cb, st);
+        if (fmt == TQ_FMT_GQ4V)
+            return d == 128 ? launch_quantize<TQ_FMT_GQ4V, 128, SRC>(a, cb, st)
+                            : launch_quantize<TQ_FMT_GQ4V, 256, SRC>(a, cb, st);
     }
 #undef TQ_Q
     return TQ_ERR_UNSUPPORTED;

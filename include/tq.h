@@ -31,7 +31,7 @@
  *   capacity must be a multiple of 64.
  * - Grouped-query attention: query head g reads KV head g / (Hq / Hkv).
  * - Supported head dims: 128 and 256.  Supported format pairs
- *   (K, V): (PQ4, PQ4), (PQ3, PQ3), (PQ3, PQ4), (TQ3K, GQ2V).
+ *   (K, V): (PQ4, PQ4), (PQ3, PQ3), (PQ3, PQ4), (TQ3K, GQ2V), (TQ3K, GQ4V).
  */
 #ifndef TQ_H
 #define TQ_H
@@ -76,12 +76,20 @@ typedef enum tq_status {
  *             channels ([P2] trick 3 and write path, v*scale + zero):
  *             per group [fp16 scale][fp16 zero][q: 8 B packed like the PQ3
  *             low bits].  48 B for d = 128.  Values only.
+ * TQ_FMT_GQ4V the same group quantization with 4-bit codes, for values where
+ *             the 2-bit codes limit quality ([P2] write path: the value cache
+ *             is group-quantized at 2 or 4 bits; [P2] limits: 4-bit values
+ *             for quality-sensitive use): per 32-channel group [fp16 scale]
+ *             [fp16 zero][q: 16 B, channel j in byte j/2, low nibble when j is
+ *             even, the PQ4 nibble order]; scale = fp16(fp32(max - min)/15).
+ *             80 B for d = 128.  Values only.
  */
 typedef enum tq_format {
     TQ_FMT_PQ4 = 1,
     TQ_FMT_PQ3 = 2,
     TQ_FMT_TQ3K = 3,
-    TQ_FMT_GQ2V = 4
+    TQ_FMT_GQ2V = 4,
+    TQ_FMT_GQ4V = 5
 } tq_format;
 
 /* Codebook constructions for the rotated-coordinate law N(0, 1/d)
@@ -170,7 +178,8 @@ int tq_cache_bytes(const tq_layout* L, size_t* k_bytes, size_t* v_bytes);
  * stores gamma = |r| of the unrotated residual r = u - Pi^T c[code] and the
  * signs [(S r)_i >= 0] ([P1] section 2; [P2] trick 2).  GQ2V stores
  * zero = min, scale = fp16(fp32(max - min)/3) per 32-channel group and codes
- * clamp(rint(fp32(v - zero) * fp32(1/scale)), 0, 3), or 0 when scale is 0.
+ * clamp(rint(fp32(v - zero) * fp32(1/scale)), 0, 3), or 0 when scale is 0;
+ * GQ4V the same with 15 in place of 3.
  *   cbk, cbv   host codebooks of the K and V formats
  *   S_dev      device fp32 d*d QJL matrix (TQ3K keys), else ignored
  *   k_new, v_new  device fp16 bits [T][Hkv][d]

@@ -38,7 +38,7 @@ from dataclasses import dataclass, field, replace
 
 import numpy as np
 
-PQ4, PQ3, TQ3K, GQ2V = 1, 2, 3, 4
+PQ4, PQ3, TQ3K, GQ2V, GQ4V = 1, 2, 3, 4, 5
 QUANTILE_MEAN, LLOYD_MAX = 0, 1
 K_TENSOR, V_TENSOR, Q_TENSOR, APPEND = 0, 1, 2, 3
 

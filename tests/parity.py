@@ -63,6 +63,8 @@ class Setup:
             return ofmt.encode_rotated(x16, fmt, tabs, signs)
         if fmt == ofmt.TQ3K:
             return ofmt.encode_tq3k(x16, tabs, signs, self.S_o)
+        if fmt == ofmt.GQ4V:
+            return ofmt.encode_gq4v(x16)
         return ofmt.encode_gq2v(x16)
 
     def oracle_dequant(self, tensor, blocks):
@@ -138,8 +140,8 @@ def compare_write(setup, tensor, gpu_blocks, enc):
     tabs = setup.tk if tensor == synth.K_TENSOR else setup.tv
     stats = {"vectors": gpu_blocks.shape[0], "code_flips": 0, "norm_flips": 0, "gamma_flips": 0, "qjl_flips": 0,
              "bytes_equal": bool(np.array_equal(gpu_blocks, enc.blocks))}
-    if fmt == synth.GQ2V:
-        assert np.array_equal(gpu_blocks, enc.blocks), "GQ2V blocks must be bit-exact"
+    if fmt in (synth.GQ2V, synth.GQ4V):
+        assert np.array_equal(gpu_blocks, enc.blocks), "group-quantized value blocks must be bit-exact"
         return stats
     if stats["bytes_equal"]:
         return stats

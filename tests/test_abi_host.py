@@ -68,6 +68,8 @@ def test_vector_and_cache_bytes():
     assert tq.vector_bytes(tq.FMT_PQ3, 128) == 56
     assert tq.vector_bytes(tq.FMT_TQ3K, 128) == 52
     assert tq.vector_bytes(tq.FMT_GQ2V, 128) == 48
+    assert tq.vector_bytes(tq.FMT_GQ4V, 128) == 80 and tq.vector_bytes(tq.FMT_GQ4V, 256) == 160
+    assert tq.cache_bytes(tq.Layout(1, 5, 1, 128, 64, tq.FMT_TQ3K, tq.FMT_GQ4V)) == (64 * 52, 64 * 80)
     assert tq.vector_bytes(tq.FMT_PQ4, 64) == 0
     L = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
     k, v = tq.cache_bytes(L)
@@ -85,6 +87,8 @@ def test_layout_validation_codes():
         (tq.Layout(1, 4, 2, 96, 128, tq.FMT_PQ4, tq.FMT_PQ4), -2),  # head dim
         (tq.Layout(1, 4, 2, 128, 128, tq.FMT_GQ2V, tq.FMT_PQ4), -2),  # format pair
         (tq.Layout(1, 4, 2, 128, 128, tq.FMT_TQ3K, tq.FMT_PQ4), -2),
+        (tq.Layout(1, 4, 2, 128, 128, tq.FMT_PQ4, tq.FMT_GQ4V), -2),
+        (tq.Layout(1, 4, 2, 128, 128, tq.FMT_GQ4V, tq.FMT_GQ4V), -2),
     ]:
         with pytest.raises(tq.TQError) as e:
             tq.cache_bytes(bad)

@@ -154,6 +154,11 @@ def test_c3_full_size():
     _run_full(synth.C3)
 
 
+def test_c3_shapes_with_gq4v_values_full_size():
+    """c3's shapes (40 / 8 heads, 30,000 tokens) with 4-bit group-quantized values."""
+    _run_full(synth.scaled(synth.C3, name="c3 with GQ4V values", v_format=synth.GQ4V, v_bits=4))
+
+
 def test_c5_bulk_prefill_then_decode():
     """131,072 tokens x 4 KV heads compressed in one call, then decoded as
     [32][2][8192] over the same bytes: stream (b, h) of the decode view is prefill head

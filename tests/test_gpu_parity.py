@@ -31,6 +31,11 @@ REDUCED = {
     "c4_g8": synth.scaled(synth.C4, batch=2, n_q_heads=16, n_kv_heads=2, context=1234, capacity=1280),
     "c4_g8_lloyd_v": synth.scaled(synth.C4, v_kind=synth.LLOYD_MAX, batch=1, n_q_heads=16, n_kv_heads=2,
                                   context=900, capacity=960),
+    # TQ3K keys with 4-bit group-quantized values, at d 128 and 256
+    "c3_gq4v": synth.scaled(synth.C3, v_format=synth.GQ4V, v_bits=4, batch=2, n_q_heads=10, n_kv_heads=2,
+                            context=999, capacity=1024),
+    "c3_gq4v_d256": synth.scaled(synth.C3, v_format=synth.GQ4V, v_bits=4, head_dim=256, batch=1, n_q_heads=8,
+                                 n_kv_heads=2, context=600, capacity=640),
 }
 
 
