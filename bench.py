@@ -452,17 +452,20 @@ def bench_hybrid(args):
     print(json.dumps(res), flush=True)
 
 
-SWEEP_NOTE = ("per-kernel times of a workload other than the headline one: decode_partial from events on its "
-              "own dispatch, the other calls as the mean over a replayed HIP graph of repeated calls (so "
-              "including the gap between kernels); algorithmic bytes as in the roofline of the "
-              "headline line; useful flops count the method's arithmetic only (2 G d FMA per token and KV "
-              "head, plus G d for the QJL term of TQ3K keys)")
+SWEEP_NOTE = ("per-kernel times of a workload other than the headline one, on a cold cache: before every timed "
+              "call a 512 MiB buffer is overwritten (twice the 256 MB Infinity Cache), so the call reads its bytes "
+              "from HBM; decode_partial from HIP events on its own dispatch, median over the calls; the write "
+              "path from events around the call; the combine (a few microseconds on records the partial just "
+              "wrote) as the mean over a replayed HIP graph of repeated calls; algorithmic bytes as in the "
+              "roofline of the headline line; useful flops count the method's arithmetic only (2 G d FMA per "
+              "token and KV head, plus G d for the QJL term of TQ3K keys)")
 
 
 def bench_sweep(args):
     """The write path at its bulk size (c5 prefill: 131,072 tokens x 4 KV heads at d 256) and the
-    decode of c1, c2, c3 and c5 at full size (and c2's shapes with PQ4 values), each timed on its
-    own, plus sparse V against the plain decode at c3 and c5; one JSON line per item."""
+    decode of every other workload at full size -- c1, c2, c3, c5, c3's shapes with GQ4V values,
+    c2's and c4's shapes with PQ3 keys (and PQ4 or PQ3 values) -- each timed alone on a cold cache,
+    plus sparse V against the plain decode at c3 and c5; one JSON line per item."""
     import numpy as np
     import torch
 
@@ -471,6 +474,27 @@ def bench_sweep(args):
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def cold_ms(fn, reps, attached):
+        """Median time of `reps` calls, each after the scrub.  attached: fn takes (start, stop)
+        raw events recorded on the kernel's own dispatch; else events are recorded around fn."""
+        times = []
+        for r in range(reps + 2):
+            scrub.fill_(r & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if attached:
+                e0.record()  # creates the HIP events before their handles are passed on
+                e1.record()
+                fn((e0.cuda_event, e1.cuda_event))
+            else:
+                e0.record()
+                fn(None)
+                e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:  # two untimed calls first
+                times.append(e0.elapsed_time(e1))
+        return float(np.median(times))
 
     def per_call_ms(fn, reps):
         """Mean time per call of `reps` calls captured in one HIP graph and replayed, so the
@@ -505,7 +529,7 @@ def bench_sweep(args):
         cbv, _ = tq.build_codebook(w.head_dim, w.v_bits, w.v_kind, w.rot_seed_v, w.qjl_seed + 1)
         return cbk, cbv, (torch.from_numpy(S).to(dev) if tq3k else None)
 
-    # ---- write path: c5 bulk prefill in one call (HBM-bound: fp16 rows in, blocks out)
+    # ---- write path: c5 bulk prefill in one call (fp16 rows in, blocks out)
     w5 = synth.C5
     T, Hp, d = w5.extra["prefill_tokens"], w5.extra["prefill_kv_heads"], w5.head_dim
     wp = synth.scaled(w5, batch=1, n_q_heads=Hp, n_kv_heads=Hp, capacity=T, context=T, prefill=T)
@@ -519,9 +543,9 @@ def bench_sweep(args):
     v_rows = torch.from_numpy(synth.batch_rows(wp, synth.V_TENSOR, 0, 0, T)).to(dev)
     dst = torch.arange(T, dtype=torch.int32, device=dev)
     _log(f"sweep: c5 prefill rows generated in {time.time() - t0:.1f}s")
-    ms = per_call_ms(lambda: tq.quantize_append(Lp, cbk5, cbv5, None, k_rows, v_rows, dst, kc5, vc5), 10)
+    ms = cold_ms(lambda ev: tq.quantize_append(Lp, cbk5, cbv5, None, k_rows, v_rows, dst, kc5, vc5), 10, False)
     nbytes = 2 * T * Hp * d * 2 + kb5 + vb5
-    emit("c5 bulk prefill (write path: norm, rotate, quantize, pack K and V)", kernel="quantize_kv_kernel",
+    emit("c5 bulk prefill (write path: norm, rotate, quantize, pack K and V)", kernel="quantize_pq4_kernel<256>",
          workload=f"{T} tokens x {Hp} KV heads, d {d}, PQ4 K and V", us=ms * 1e3, bytes=nbytes,
          roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
@@ -529,9 +553,12 @@ def bench_sweep(args):
     torch.cuda.synchronize()
 
     # ---- decode of the other workloads (c5 reads the prefill bytes as [32][2][8192])
-    # the asymmetric pair: turbo3-style keys with 4-bit values, at c2's shapes
-    asym = synth.scaled(synth.C2, name="c2 with PQ3 keys and PQ4 values", v_format=synth.PQ4, v_bits=4)
-    for w in (synth.C1, synth.C2, asym, synth.C3, synth.C5):
+    c2_asym = synth.scaled(synth.C2, name="c2 with PQ3 keys and PQ4 values", v_format=synth.PQ4, v_bits=4)
+    c3_gq4v = synth.scaled(synth.C3, name="c3 with GQ4V values", v_format=synth.GQ4V, v_bits=4)
+    c4_pq3 = synth.scaled(synth.C4, name="c4 shapes with PQ3 keys and values", k_format=synth.PQ3,
+                          v_format=synth.PQ3, k_bits=3, v_bits=3, prefill=synth.C4.context)
+    c4_asym = synth.scaled(c4_pq3, name="c4 shapes with PQ3 keys and PQ4 values", v_format=synth.PQ4, v_bits=4)
+    for w in (synth.C1, synth.C2, c2_asym, synth.C3, c3_gq4v, synth.C5, c4_pq3, c4_asym):
         B, Hq, Hkv, d, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
         L = tq.Layout(B, Hq, Hkv, d, w.capacity, w.k_format, w.v_format)
         if w is synth.C5:
@@ -542,37 +569,29 @@ def bench_sweep(args):
             kbytes, vbytes = tq.cache_bytes(L)
             kc = torch.zeros(kbytes, dtype=torch.uint8, device=dev)
             vc = torch.zeros(vbytes, dtype=torch.uint8, device=dev)
-            krows, vrows = gen_rows(w, synth.K_TENSOR, w.prefill), gen_rows(w, synth.V_TENSOR, w.prefill)
             for b in range(B):
+                krows = torch.from_numpy(synth.batch_rows(w, synth.K_TENSOR, b, 0, w.prefill)).to(dev)
+                vrows = torch.from_numpy(synth.batch_rows(w, synth.V_TENSOR, b, 0, w.prefill)).to(dev)
                 dst = torch.arange(b * w.capacity, b * w.capacity + w.prefill, dtype=torch.int32, device=dev)
-                tq.quantize_append(L, cbk, cbv, S, torch.from_numpy(krows[b]).to(dev),
-                                   torch.from_numpy(vrows[b]).to(dev), dst, kc, vc)
+                tq.quantize_append(L, cbk, cbv, S, krows, vrows, dst, kc, vc)
+                del krows, vrows
         q = torch.from_numpy(synth.queries(w)).to(dev)
         q_rot = torch.empty_like(q)
         q_sk = torch.empty_like(q) if S is not None else None
         out = torch.empty_like(q)
         seq = torch.full((B,), N, dtype=torch.int32, device=dev)
         ws = torch.empty(tq.decode_workspace_bytes(L), dtype=torch.uint8, device=dev)
-        reps = 200 if N * B <= 65536 else 50
-        rot_ms = per_call_ms(lambda: tq.rotate_sketch_query(L, cbk, S, q, q_rot, q_sk), reps)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e in ev:  # create the HIP events before handing their handles over
-            e[0].record()
-            e[1].record()
-        for i in range(3):
-            tq.decode_partial(L, cbk, cbv, q_rot, q_sk, kc, vc, seq, ws)
-        torch.cuda.synchronize()
-        for e in ev:
-            tq.decode_partial(L, cbk, cbv, q_rot, q_sk, kc, vc, seq, ws, events=(e[0].cuda_event, e[1].cuda_event))
-        torch.cuda.synchronize()
-        part_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-        comb_ms = per_call_ms(lambda: tq.decode_combine(L, cbv, ws, out), reps)
+        reps = 30
+        rot_ms = per_call_ms(lambda: tq.rotate_sketch_query(L, cbk, S, q, q_rot, q_sk), 100)
+        part_ms = cold_ms(lambda ev: tq.decode_partial(L, cbk, cbv, q_rot, q_sk, kc, vc, seq, ws, events=ev), reps,
+                          True)
+        comb_ms = per_call_ms(lambda: tq.decode_combine(L, cbv, ws, out), 100)
         alg = B * Hkv * N * (tq.vector_bytes(w.k_format, d) + tq.vector_bytes(w.v_format, d))
         fma = B * Hkv * N * w.group * d * (3 if w.k_format == synth.TQ3K else 2)
         gbs = alg / (part_ms * 1e-3) / 1e9
         emit(f"{w.name} decode", kernel="decode_partial + decode_combine",
              workload=f"batch {B}, {Hq} query / {Hkv} KV heads, d {d}, context {N}, formats K {w.k_format} V "
-                      f"{w.v_format} (1 PQ4, 2 PQ3, 3 TQ3K, 4 GQ2V)",
+                      f"{w.v_format} (1 PQ4, 2 PQ3, 3 TQ3K, 4 GQ2V, 5 GQ4V)",
              splits=tq.decode_splits(L), us={"rotate_query": rot_ms * 1e3, "decode_partial": part_ms * 1e3,
                                              "decode_combine": comb_ms * 1e3},
              bytes=alg, useful_tflops=2 * fma / (part_ms * 1e-3) / 1e12,
@@ -581,17 +600,17 @@ def bench_sweep(args):
         if w is synth.C3 or w is synth.C5:
             # sparse V against the plain call on the same cache, with queries four times as sharp
             # (logit spread about 8): most tokens then sit far below their wavefront's running
-            # maximum, the case the threshold is for
+            # maximum, the case the threshold is for (warm: a replayed graph of each call)
             qs = q * 4.0
             qs_rot = torch.empty_like(qs)
             qs_sk = torch.empty_like(qs) if S is not None else None
             tq.rotate_sketch_query(L, cbk, S, qs, qs_rot, qs_sk)
             tau = 1e-3
-            plain_ms = per_call_ms(lambda: tq.decode_partial(L, cbk, cbv, qs_rot, qs_sk, kc, vc, seq, ws), reps)
+            plain_ms = per_call_ms(lambda: tq.decode_partial(L, cbk, cbv, qs_rot, qs_sk, kc, vc, seq, ws), 50)
             sv_ms = per_call_ms(lambda: tq.decode_partial_sparse_v(L, cbk, cbv, qs_rot, qs_sk, kc, vc, seq, ws, tau),
-                                reps)
+                                50)
             emit(f"{w.name} decode, sparse V", kernel="decode_partial vs decode_partial_sparse_v",
-                 workload=f"as the {w.name} decode line, queries scaled by 4", threshold=tau,
+                 workload=f"as the {w.name} decode line, queries scaled by 4; warm (replayed graph)", threshold=tau,
                  us={"decode_partial": plain_ms * 1e3, "decode_partial_sparse_v": sv_ms * 1e3},
                  speedup=plain_ms / sv_ms)
         del kc, vc

@@ -1662,6 +1662,467 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     stream_finish<D, G, NT>(a, cbv, true, b, h, reinterpret_cast<float*>(&sm.u), &tail_flag);
 }
 
+// ---------------------------------------------------------------------------
+// TQ3K keys ([P2] trick 2: 2-bit MSE code plus 1-bit QJL sign per coordinate) with
+// GQ2V or GQ4V values ([P2] trick 3: v * scale + zero per group), d = 128, up to
+// eight query heads per KV head, on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16, fp32 accumulation).  Rows of every product are
+// (head h, half r of the hi/lo split of the query side), 16 rows for eight heads.
+//
+// Scores, columns = 16 tokens:
+//   MSE  D[(h,r)][t] += sum_{j,s} q_r[h][j] c_s[code_tj]: a lane's eight k are the
+//        four coordinates of one code byte with both centroid halves, read as one
+//        16-byte entry of a 256-entry LDS table (byte -> (c_hi, c_lo) x 4);
+//   QJL  D[(h,r)][t] += sum_j u_r[h][j] (2 b_tj - 1): a lane's eight k are one byte
+//        of sign bits, read from a 256-entry table of +-1 octets.
+//   The score is n_t (mse + gamma_t qjl) with log2(e)/sqrt(d) folded into both query
+//   operands and sqrt(pi/2)/d into the sketch's.  Each table has eight copies, one per
+//   lane of an eight-lane LDS phase, so that any bytes read conflict-free.
+// Values, per group gr of 32 channels, columns = 16 channels 32 gr + 2 col + hf for
+// the two products hf = 0, 1 (one code dword per token serves both):
+//   D[(h,r)][col] += sum_t w_r[h][t] (128 + q_tj) with w = p * scale_t,gr split hi/lo;
+//   the codes enter exactly as bf16(128 + q) = 0x4300 | q, two tokens per dword by one
+//   byte permute, a shift and a mask; then
+//   acc_hj = D_hi + D_lo - 128 sum_t (w_hi + w_lo) + sum_t p zero_t,gr,
+//   the two sums kept on the VALU by the lanes that own the token's weight.
+// Eight wavefronts per workgroup share the tables; each walks 32-token tiles of the
+// split with the next tile's keys (registers) and values (an LDS stage, by buffer
+// loads with an LDS destination) requested before the current tile's products.
+template <int VF>
+struct TqCfg {
+    static constexpr int D = 128, VBK = 52;
+    static constexpr int VBV = VF == TQ_FMT_GQ2V ? 48 : 80;  // value bytes per token
+    static constexpr int GB = VF == TQ_FMT_GQ2V ? 12 : 20;   // bytes per value group
+    static constexpr int QB = VF == TQ_FMT_GQ2V ? 2 : 4;     // code bits
+    static constexpr int WAVES = 8, TT = 32, NTB = TT / 16, NGRP = 4, COPIES = 8;
+    static constexpr int STAGE = TT * VBV;                   // a multiple of 256
+};
+
+template <int VF>
+struct SmemTq {
+    using C = TqCfg<VF>;
+    union {
+        struct {
+            u32x4 mse[256 * C::COPIES];  // entry (byte b, copy c) at b * COPIES + c
+            u32x4 qjl[256 * C::COPIES];
+        } tab;
+        float red[C::WAVES * 8 * (2 + C::D)];  // per-wavefront (m, l, acc) after the tile loop
+    } u;
+    alignas(16) uint16_t wa[C::WAVES][C::NGRP][16][C::TT];  // value A operands [group][row][token]
+};
+
+// A value tile of BYTES bytes (a multiple of 256), HBM -> LDS by buffer loads with an
+// LDS destination: whole kilobytes with 16 bytes per lane, then 256-byte pieces with 4.
+template <int BYTES>
+__device__ __forceinline__ void stage_bytes(__amdgpu_buffer_rsrc_t r, uint8_t* stage, int tile_off, int lane) {
+    static_assert(BYTES % 256 == 0, "whole 256-byte pieces");
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    constexpr int KB = BYTES / 1024, R = (BYTES % 1024) / 256;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * k), 16, 16 * lane, tile_off + 1024 * k, 0,
+                                                 kStreamPolicy);
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * KB + 256 * k), 4, 4 * lane,
+                                                 tile_off + 1024 * KB + 256 * k, 0, kStreamPolicy);
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Key bytes of a 16-token block for lane (n, g): token n's norms (n | gamma << 16),
+// code bytes 8g .. 8g+7 (coordinates 32g .. 32g+31) and sign byte group g (dword g of
+// the QJL bits: coordinates 32g .. 32g+31).
+struct TqKeys {
+    uint32_t norms[2];
+    u32x2 codes[2];
+    uint32_t signs[2];
+};
+
+__device__ __forceinline__ void load_tq_keys(TqKeys& k, __amdgpu_buffer_rsrc_t r, int lane_off, int g, int tile_off) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int o = lane_off + 16 * tb * 52;
+        k.norms[tb] = __builtin_amdgcn_raw_buffer_load_b32(r, o, tile_off, kStreamPolicy);
+        k.codes[tb] = __builtin_amdgcn_raw_buffer_load_b64(r, o + 4 + 8 * g, tile_off, kStreamPolicy);
+        k.signs[tb] = __builtin_amdgcn_raw_buffer_load_b32(r, o + 36 + 4 * g, tile_off, kStreamPolicy);
+    }
+}
+
+// bf16 (hi, lo) halves of x as (lo << 16) | hi, by the hardware round-to-nearest-even
+// conversion: hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ uint32_t bf16_split_hw(float x) {
+    const __bf16 hi = static_cast<__bf16>(x);
+    const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+    uint16_t hb, lb;
+    __builtin_memcpy(&hb, &hi, 2);
+    __builtin_memcpy(&lb, &lo, 2);
+    return hb | (static_cast<uint32_t>(lb) << 16);
+}
+
+template <int VF, int G>
+__global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_kernel(DecodeArgs a, DevCodebook cbk,
+                                                                                      DevCodebook cbv) {
+    using C = TqCfg<VF>;
+    static_assert(G <= 8, "eight heads fill the sixteen rows");
+    constexpr int D = C::D, VBK = C::VBK, VBV = C::VBV, GB = C::GB, TT = C::TT, NW = C::WAVES;
+    __shared__ __align__(16) SmemTq<VF> sm;
+    __shared__ __align__(16) uint8_t vst0[NW][C::STAGE];
+    __shared__ __align__(16) uint8_t vst1[NW][C::STAGE];
+
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
+    const int n = lane & 15, g = lane >> 4;
+    const int hq0 = h * G;
+    int N = a.seq_lens[b];
+    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
+    const int start = s * a.split_len;
+    const int end = min(start + a.split_len, N);
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+
+    if (start >= end) {
+        for (int gg = 0; gg < G; ++gg) {
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
+            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
+        }
+        return;
+    }
+
+    // ---- the small global reads first: the query entries of the operands this thread builds.
+    // Operand entry (job, lane l): jobs 0..7 are the MSE products I, whose lane (row i, group gg)
+    // holds coordinates 32 gg + 4 I .. + 3 of head i / 2, half i % 2, each duplicated for the
+    // two centroid halves; jobs 8..11 the QJL products I - 8, coordinates 32 gg + 8 (I - 8) .. + 7
+    // of the sketch.  768 entries, one or two per thread.
+    constexpr int NJOB = 12 * 64;
+    float ev[2][8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e = tid + NW * 64 * k;
+        const int job = (e < NJOB ? e : 0) >> 6, l = e & 63, ri = l & 15, gg = l >> 4;
+        const int hh = (ri >> 1) < G ? ri >> 1 : 0;
+        const size_t qrow = (static_cast<size_t>(b) * a.hq + hq0 + hh) * D + 32 * gg;
+        if (job < 8) {
+            const float4 v = *reinterpret_cast<const float4*>(a.q_rot + qrow + 4 * job);
+            ev[k][0] = v.x; ev[k][1] = v.y; ev[k][2] = v.z; ev[k][3] = v.w;
+            ev[k][4] = ev[k][5] = ev[k][6] = ev[k][7] = 0.0f;
+        } else {
+            const float4* sp = reinterpret_cast<const float4*>(a.q_sk + qrow + 8 * (job - 8));
+            const float4 v0 = sp[0], v1 = sp[1];
+            ev[k][0] = v0.x; ev[k][1] = v0.y; ev[k][2] = v0.z; ev[k][3] = v0.w;
+            ev[k][4] = v1.x; ev[k][5] = v1.y; ev[k][6] = v1.z; ev[k][7] = v1.w;
+        }
+    }
+
+    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
+    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VBK, static_cast<uint32_t>(a.capacity) * VBK);
+    const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VBV, static_cast<uint32_t>(a.capacity) * VBV);
+    const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
+    const int k_lane = n * VBK;
+
+    // the first tile of this wavefront (through the empty resource when it has none)
+    constexpr int kStep = NW * TT;
+    int t0 = start + w * TT;
+    TqKeys kt[2];
+    {
+        const bool any = t0 < end;
+        load_tq_keys(kt[0], any ? krs : krs_none, k_lane, g, t0 * VBK);
+        stage_bytes<C::STAGE>(any ? vrs : vrs_none, vst0[w], t0 * VBV, lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- tables: thread t fills entries t + 512 k (entry e is byte e / COPIES, copy e % COPIES)
+    {
+        uint32_t csp[4];  // (hi, lo) of the four key centroids
+#pragma unroll
+        for (int c = 0; c < 4; ++c) csp[c] = bf16_split_hw(cbk.centroids[c]);
+#pragma unroll
+        for (int k = 0; k < 256 * C::COPIES / (NW * 64); ++k) {
+            const int e = tid + NW * 64 * k;
+            const uint32_t byte = static_cast<uint32_t>(e) / C::COPIES;
+            u32x4 m, q;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t b0 = (byte >> (2 * c)) & 1u, b1 = (byte >> (2 * c + 1)) & 1u;
+                m[c] = b1 ? (b0 ? csp[3] : csp[2]) : (b0 ? csp[1] : csp[0]);
+                q[c] = (b0 ? 0x3F80u : 0xBF80u) | ((b1 ? 0x3F80u : 0xBF80u) << 16);
+            }
+            sm.u.tab.mse[e] = m;
+            sm.u.tab.qjl[e] = q;
+        }
+    }
+    // ---- query operands into LDS (the weight area, free until the first tile): the query times
+    // log2(e)/sqrt(d), the sketch also times sqrt(pi/2)/d, as bf16 halves (rows of heads >= G zero)
+    u32x4* opl = reinterpret_cast<u32x4*>(&sm.wa[0][0][0][0]);  // [job][lane]
+    static_assert(sizeof(sm.wa) >= sizeof(u32x4) * NJOB, "operands fit the weight area");
+    {
+        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+        const float sscale = qscale * (1.2533141373155003f / D);  // sqrt(pi/2)/d
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = tid + NW * 64 * k;
+            if (e < NJOB) {
+                const int job = e >> 6, ri = e & 15;
+                const bool live = (ri >> 1) < G;
+                const uint32_t sh = (ri & 1) * 16;  // half r of the split
+                u32x4 v;
+                if (job < 8) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t hv = live ? (bf16_split_hw(ev[k][c] * qscale) >> sh) & 0xFFFFu : 0u;
+                        v[c] = hv | (hv << 16);
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        const uint32_t h0 = (bf16_split_hw(ev[k][2 * c] * sscale) >> sh) & 0xFFFFu;
+                        const uint32_t h1 = (bf16_split_hw(ev[k][2 * c + 1] * sscale) >> sh) & 0xFFFFu;
+                        v[c] = live ? h0 | (h1 << 16) : 0u;
+                    }
+                }
+                opl[e] = v;
+            }
+        }
+    }
+    __syncthreads();
+    u32x4 qa[8], sa[4];
+#pragma unroll
+    for (int I = 0; I < 8; ++I) qa[I] = opl[I * 64 + lane];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) sa[I] = opl[(8 + I) * 64 + lane];
+    __syncthreads();  // every wavefront holds its operands before any writes weights there
+
+    // per lane: heads 2g + e (rows 4g + 2e + r of every product); rows of heads >= G stay at
+    // m = 0, p = 0
+    float m_run[2], l_run[2], zacc[2][4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        m_run[e] = (2 * g + e < G) ? -INFINITY : 0.0f;
+        l_run[e] = 0.0f;
+#pragma unroll
+        for (int gr = 0; gr < 4; ++gr) zacc[e][gr] = 0.0f;
+    }
+    f32x4 acc[4][2], wsum[4];  // value sums per group and product; sum of the weight halves per group
+#pragma unroll
+    for (int gr = 0; gr < 4; ++gr) acc[gr][0] = acc[gr][1] = wsum[gr] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const char* mtab = reinterpret_cast<const char*>(sm.u.tab.mse);
+    const char* stab = reinterpret_cast<const char*>(sm.u.tab.qjl);
+    const uint32_t copy_off = lds_offset((lane & 7) * 16u);
+    const float slack = a.v_skip > 0.0f ? 0.0f : kRescaleSlack;
+    // this lane's code dword of a group and the byte of it holding channels 2n, 2n + 1
+    constexpr int QB = C::QB;
+    const int cw_off = QB == 2 ? 4 + 4 * (n >> 3) : 4 + 4 * (n >> 2);
+    const uint32_t cbyte = QB == 2 ? (n & 7) >> 1 : (n & 3);
+    const uint32_t csh = QB == 2 ? 4 * (n & 1) : 0;  // bit of channel 2n within that byte
+    const uint32_t psel = cbyte | (0x0Cu << 8) | ((cbyte + 4u) << 16) | (0x0Cu << 24);
+    uint32_t cmask = QB == 2 ? 0x00030003u : 0x000F000Fu;
+    asm("" : "+v"(cmask));  // in a register, so that mask and or fuse into one instruction
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    uint16_t* wa_w = &sm.wa[w][0][0][0];
+
+    auto tile = [&](auto pc, const int t0) {
+        constexpr int P = decltype(pc)::value;
+        TqKeys& kc = kt[P];
+        const int nv = min(TT, end - t0);  // <= 0 for the odd tile after the last one
+        const bool more = t0 + kStep < end;
+        const int t_next = more ? t0 + kStep : t0;
+        const uint8_t* vcur = P == 0 ? vst0[w] : vst1[w];
+        stage_bytes<C::STAGE>(more ? vrs : vrs_none, P == 0 ? vst1[w] : vst0[w], t_next * VBV, lane);
+        load_tq_keys(kt[1 - P], more ? krs : krs_none, k_lane, g, t_next * VBK);
+
+        // ---- scores: job J is product I = J / 2 of token block J % 2 (I < 8: the MSE products,
+        // I = 8 .. 11: the QJL products), so that the two blocks' accumulator chains interleave
+        float tv[2][2];
+        {
+            f32x4 dm[2], dq[2];
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) dm[tb] = dq[tb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            constexpr int LA = 2, NJ = 24, R = LA + 1;
+            u32x4 ring[R];
+            static_for<NJ + LA>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int I = J / 2, TB = J % 2;
+                    if constexpr (I < 8) {
+                        const uint32_t word = I < 4 ? kc.codes[TB][0] : kc.codes[TB][1];
+                        const uint32_t by = __builtin_amdgcn_ubfe(word, 8 * (I % 4), 8);
+                        ring[J % R] = *reinterpret_cast<const u32x4*>(mtab + ((by << 7) | copy_off));
+                    } else {
+                        const uint32_t by = __builtin_amdgcn_ubfe(kc.signs[TB], 8 * (I - 8), 8);
+                        ring[J % R] = *reinterpret_cast<const u32x4*>(stab + ((by << 7) | copy_off));
+                    }
+                }
+                if constexpr (J >= LA) {
+                    constexpr int M = J - LA, I = M / 2, TB = M % 2;
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, ring[M % R]);
+                    if constexpr (I < 8)
+                        dm[TB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa[I]), bop, dm[TB],
+                                                                         0, 0, 0);
+                    else
+                        dq[TB] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, sa[I - 8]), bop,
+                                                                         dq[TB], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) {
+                const float nk = half_bits_to_float(kc.norms[tb] & 0xFFFFu);
+                const float gk = half_bits_to_float(kc.norms[tb] >> 16);
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const bool ok = 2 * g + e < G && 16 * tb + n < nv;
+                    const float sc = nk * fmaf(gk, dq[tb][2 * e] + dq[tb][2 * e + 1], dm[tb][2 * e] + dm[tb][2 * e + 1]);
+                    tv[tb][e] = ok ? sc : -INFINITY;
+                }
+            }
+        }
+        if (a.scores) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    if (tv[tb][e] != -INFINITY)
+                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 2 * g + e) * a.capacity + t0 + 16 * tb + n] =
+                            tv[tb][e] * kLn2;
+        }
+
+        // ---- online softmax; lane (n, g) owns token 16 tb + n of heads 2g, 2g + 1
+        float mx[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) mx[e] = fmaxf(tv[0][e], tv[1][e]);
+        if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + slack || mx[1] > m_run[1] + slack) != 0) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float mn = fmaxf(m_run[e], row16_max(mx[e]));
+                const float alpha = mn == m_run[e] ? 1.0f : __builtin_amdgcn_exp2f(m_run[e] - mn);
+                l_run[e] *= alpha;
+#pragma unroll
+                for (int gr = 0; gr < 4; ++gr) {
+                    zacc[e][gr] *= alpha;
+                    wsum[gr][2 * e] *= alpha;
+                    wsum[gr][2 * e + 1] *= alpha;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf) {
+                        acc[gr][hf][2 * e] *= alpha;
+                        acc[gr][hf][2 * e + 1] *= alpha;
+                    }
+                }
+                m_run[e] = mn;
+            }
+        }
+        // weights times each group's scale, as the A operands of the value products
+        bool keep = false;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+            const int t = 16 * tb + n;
+            const bool tok = t < nv;
+            float scl[4], zro[4];  // the token's group scales and zeros (0 past the end: never stale)
+#pragma unroll
+            for (int gr = 0; gr < 4; ++gr) {
+                const uint32_t hdr = *reinterpret_cast<const uint32_t*>(vcur + lds_offset(t * VBV) + GB * gr);
+                scl[gr] = tok ? half_bits_to_float(hdr & 0xFFFFu) : 0.0f;
+                zro[gr] = tok ? half_bits_to_float(hdr >> 16) : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float p = __builtin_amdgcn_exp2f(tv[tb][e] - m_run[e]);  // 0 for invalid tokens and rows
+                l_run[e] += p;
+                const float pk = p >= a.v_skip ? p : 0.0f;
+                keep = keep || pk != 0.0f;
+                uint16_t* dst = wa_w + lds_offset((4 * g + 2 * e) * TT + t);
+#pragma unroll
+                for (int gr = 0; gr < 4; ++gr) {
+                    zacc[e][gr] = fmaf(pk, zro[gr], zacc[e][gr]);
+                    const uint32_t sp = bf16_split_hw(pk * scl[gr]);
+                    dst[gr * 16 * TT] = static_cast<uint16_t>(sp);
+                    dst[gr * 16 * TT + TT] = static_cast<uint16_t>(sp >> 16);
+                }
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(keep) == 0) return;  // no value survives (uniform)
+        lds_order();
+
+        // ---- values: per group, the A operand (rows, tokens 8g .. 8g+7) and the code dwords
+        // of those tokens; product hf takes channels 32 gr + 2 col + hf, and a product with a
+        // B of ones sums the weight halves the value products used
+#pragma unroll
+        for (int gr = 0; gr < 4; ++gr) {
+            const u32x4 av = *reinterpret_cast<const u32x4*>(wa_w + lds_offset((gr * 16 + n) * TT + 8 * g));
+            uint32_t x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                x[u] = *reinterpret_cast<const uint32_t*>(vcur + lds_offset((8 * g + u) * VBV + cw_off) + GB * gr);
+            uint32_t pr[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_perm(x[2 * v + 1], x[2 * v], psel);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                u32x4 bv;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) bv[v] = ((pr[v] >> (csh + hf * QB)) & cmask) | 0x43004300u;
+                acc[gr][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                      __builtin_bit_cast(bf16x8, bv), acc[gr][hf], 0, 0, 0);
+            }
+            wsum[gr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                               __builtin_bit_cast(bf16x8, ones), wsum[gr], 0, 0, 0);
+        }
+        lds_order();
+    };
+    for (; t0 < end; t0 += 2 * kStep) {
+        tile(std::integral_constant<int, 0>{}, t0);
+        tile(std::integral_constant<int, 1>{}, t0 + kStep);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the last requests land before the LDS is released
+
+    // ---- the zero terms summed over the 16 token lanes, then the wavefronts merge
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        l_run[e] = row16_sum(l_run[e]);
+#pragma unroll
+        for (int gr = 0; gr < 4; ++gr) zacc[e][gr] = row16_sum(zacc[e][gr]);
+    }
+    __syncthreads();  // every table lookup of the workgroup is done: the tables become the merge buffer
+    float* red = sm.u.red;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int hh = 2 * g + e;
+        if (hh < G) {
+            float* r = red + (w * G + hh) * (2 + D);
+            if (n == 0) {
+                r[0] = m_run[e];
+                r[1] = l_run[e];
+            }
+#pragma unroll
+            for (int gr = 0; gr < 4; ++gr) {
+                const float corr = 128.0f * (wsum[gr][2 * e] + wsum[gr][2 * e + 1]);
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    r[2 + 32 * gr + 2 * n + hf] = ((acc[gr][hf][2 * e] + acc[gr][hf][2 * e + 1]) - corr) + zacc[e][gr];
+            }
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
+        const int gg = idx / D, j = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red[(ww * G + gg) * (2 + D)]);
+        float L = 0.0f, A = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float* r = red + (ww * G + gg) * (2 + D);
+            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+            L = fmaf(r[1], f, L);
+            A = fmaf(r[2 + j], f, A);
+        }
+        const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+        a.acc[rec * D + j] = A;
+        if (j == 0) a.ml[rec] = make_float2(M, L);
+    }
+}
+
 int auto_split_tokens(const tq_layout* L) {
     const long streams = static_cast<long>(L->batch) * L->n_kv_heads;
     const long max_splits = (L->capacity + kSplitQuantum - 1) / kSplitQuantum;
@@ -1671,9 +2132,12 @@ int auto_split_tokens(const tq_layout* L) {
     //   * PQ4 at d = 256, G = 4 or 8 (dense bf16 kernel): one split per 4-wavefront workgroup,
     //     best at two workgroups per CU (c5: 44 us at 512 splits, 47 at 256, 62 at 2048);
     //   * the generic kernel: about 2048 splits, two rounds of four workgroups per CU.
+    //   * TQ3K keys at d = 128 (matrix-core kernel, eight wavefronts and 136 KB of LDS per
+    //     workgroup): one workgroup per CU, about 256 splits;
     const int G = L->n_kv_heads > 0 ? L->n_q_heads / L->n_kv_heads : 0;
     const bool pq4 = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && (G == 4 || G == 8);
-    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 512) : 2048;
+    const bool tq3k = L->k_format == TQ_FMT_TQ3K && L->head_dim == 128 && G <= 8;
+    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 512) : tq3k ? 256 : 2048;
     long want = (target + streams - 1) / streams;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
@@ -1756,9 +2220,33 @@ int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebo
                          to_dev(cbv));
 }
 
+template <int VF, int G>
+int launch_partial_tq3k(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
+                        const Launch& l) {
+    dim3 grid(a.splits, L->n_kv_heads, L->batch);
+    return launch_kernel(decode_partial_tq3k_kernel<VF, G>, grid, dim3(TqCfg<VF>::WAVES * 64), l, a, to_dev(cbk),
+                         to_dev(cbv));
+}
+
 template <int KF, int VF, int D>
 int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                    const Launch& st) {
+    if constexpr (KF == TQ_FMT_TQ3K && D == 128) {
+        // the matrix-core kernel reads the query operands as 16-byte vectors and addresses a
+        // stream through a 32-bit buffer range
+        const bool ok = aligned(a.q_rot, 16) && aligned(a.q_sk, 16) &&
+                        static_cast<size_t>(L->capacity) * vbytes<VF, D>() <= 0x7FFFFFFFu;
+        if (ok) {
+            switch (G) {
+                case 1: return launch_partial_tq3k<VF, 1>(a, L, cbk, cbv, st);
+                case 2: return launch_partial_tq3k<VF, 2>(a, L, cbk, cbv, st);
+                case 4: return launch_partial_tq3k<VF, 4>(a, L, cbk, cbv, st);
+                case 5: return launch_partial_tq3k<VF, 5>(a, L, cbk, cbv, st);
+                case 8: return launch_partial_tq3k<VF, 8>(a, L, cbk, cbv, st);
+                default: break;
+            }
+        }
+    }
     if constexpr (KF == TQ_FMT_PQ4 && VF == TQ_FMT_PQ4) {
         // the matrix-core kernel addresses a stream through a 32-bit buffer range
         const bool fits = static_cast<size_t>(L->capacity) * vbytes<TQ_FMT_PQ4, D>() <= 0x7FFFFFFFu;

@@ -65,7 +65,8 @@ def _oracle_streams(st, rows_of, n_of, q, gpu_k, gpu_v, host_k, host_v, cmp_of=N
         host_k[b, h, :n] = ek.blocks
         host_v[b, h, :n] = ev.blocks
         kd, vd = st.oracle_dequant(synth.K_TENSOR, ek.blocks), st.oracle_dequant(synth.V_TENSOR, ev.blocks)
-        refs = {(b, g): P.oatt.softmax_attention(q[b, g], kd, vd) for g in range(h * G, (h + 1) * G)}
+        refs = {(b, g): P.oatt.softmax_attention(q[b, g], kd, vd) + (P.cs_scale(q[b, g], kd),)
+                for g in range(h * G, (h + 1) * G)}
         return refs, sk, sv
 
     refs, flips = {}, {"code_flips": 0, "norm_flips": 0, "gamma_flips": 0, "qjl_flips": 0}
@@ -81,12 +82,12 @@ def _check_all(st, L, q, kc, vc, lens, refs, scores_too=True):
     out, scores, _, _ = P.gpu_decode(st, L, q, kc, vc, lens, split_tokens=0, want_scores=scores_too)
     assert np.all(np.isfinite(out))
     worst_s = worst_o = 0.0
-    for (b, g), (ref, logits) in refs.items():
+    for (b, g), (ref, logits, cs) in refs.items():
         eo = float(P.rel_err_rows(out[b, g], ref))
         worst_o = max(worst_o, eo)
         assert eo <= P.OUT_TOL, (b, g, eo)
         if scores_too:
-            es = float(P.rel_err_rows(scores[b, g, :lens[b]], logits))
+            es = P.score_err(scores[b, g, :lens[b]], logits, cs)
             worst_s = max(worst_s, es)
             assert es <= P.SCORE_TOL, (b, g, es)
     assert len(refs) == L.batch * L.n_q_heads, "every query head is checked"
@@ -264,7 +265,7 @@ def test_c4_full_size_fused_step():
     _say(f"  appended rows differing from the oracle's bytes (boundary ties): K {diff_k}, V {diff_v} of "
          f"{w.batch * w.n_kv_heads} each")
     worst = 0.0
-    for (b, g), (ref, _) in refs.items():
+    for (b, g), (ref, _, _) in refs.items():
         e = float(P.rel_err_rows(out[b, g], ref))
         worst = max(worst, e)
         assert e <= P.OUT_TOL, (b, g, e)

@@ -280,6 +280,30 @@ def test_decode_edge_lengths():
             assert np.all(np.isnan(scores[b, :, n:]))
 
 
+@pytest.mark.parametrize("vfmt", [synth.GQ2V, synth.GQ4V])
+@pytest.mark.parametrize("G", [1, 2, 4, 5, 8])
+def test_tq3k_keys_every_group_size_and_ragged_lengths(G, vfmt):
+    """TQ3K keys with group-quantized values at d 128 for every group size the matrix-core
+    kernel is built for: contexts of 0, 1, a token block, a tile, one past it, one split,
+    one past a split and the full capacity, with the automatic and a 256-token split."""
+    w = synth.scaled(synth.C3, v_format=vfmt, v_bits=2 if vfmt == synth.GQ2V else 4, batch=8, n_q_heads=2 * G,
+                     n_kv_heads=2, context=1024, capacity=1024)
+    st = P.Setup(w)
+    L = st.layout()
+    lens = [0, 1, 16, 33, 255, 257, 700, 1024]
+    kb, vb, kdq, vdq = _oracle_cache(st, w, lens)
+    kc = _garbage_cache(st, L, synth.K_TENSOR, kb)
+    vc = _garbage_cache(st, L, synth.V_TENSOR, vb)
+    q = synth.queries(w)
+    for split in (0, 256):
+        out, scores, _, _ = P.gpu_decode(st, L, q, kc, vc, lens, split_tokens=split)
+        es, eo = P.check_read(st, q, kdq, vdq, lens, out, scores, w.capacity)
+        assert np.all(out[0] == 0.0)
+        for b, n in enumerate(lens):  # scores are written only below the context length
+            assert np.all(np.isnan(scores[b, :, n:]))
+        _say(f"tq3k G={G} v={vfmt} split={split}: score err {es:.2e}, output err {eo:.2e}")
+
+
 def test_timed_partial_matches_untimed():
     """tq_decode_partial_timed writes the same records as tq_decode_partial and
     its events span a positive kernel time."""
