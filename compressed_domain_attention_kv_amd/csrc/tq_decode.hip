@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <utility>
@@ -1188,35 +1189,146 @@ struct SpCfg {
     static constexpr int RED = kPairWaves * G * (2 + D);
 };
 
-template <int G, bool VTAB>
+template <int G, bool VTAB, int KF, int VF>
 struct SmemSp {
     using C = SpCfg<G>;
+    static constexpr bool K3 = KF == TQ_FMT_PQ3, V3 = VF == TQ_FMT_PQ3;
+    // PQ3 table bytes are 6-bit indexes (64 entries), PQ4 bytes two 4-bit codes (256)
+    static constexpr int KENT = (K3 ? 64 : 256) * kPairCopies;
+    static constexpr int VENT = VTAB ? (V3 ? 64 : 256) * kPairCopies : 1;
+    static constexpr int NQW = V3 ? 4 : 1;  // value A operands per token block (PQ3: one per block of 32)
     union {
         struct {
-            uint2 table[256 * kPairCopies];          // entry (byte b, copy c) at b * 32 + c
-            uint2 vtable[VTAB ? 256 * kPairCopies : 1];  // the values' own table when their centroids differ
+            uint2 table[KENT];                       // entry (byte b, copy c) at b * 32 + c
+            uint2 vtable[VENT];                      // the values' own table when their centroids differ
             alignas(16) u32x4 qa[C::RB][4][64];      // compressed score A operand per row block, product, lane
+            // PQ3 values: per wavefront [tb][token][pair slot j] index words (byte Q: pair j of block Q),
+            // token rows of 20 words so the four token quads of a read fall on distinct banks
+            alignas(16) uint32_t vidx[V3 ? kPairWaves : 1][V3 ? C::NTB * 16 * 20 : 4];
         } op;
         float red[C::RED];                           // per-wavefront (m, l, acc) after the tile loop
     } u;
-    alignas(16) uint32_t wa[kPairWaves][C::WA];
+    alignas(16) uint32_t wa[kPairWaves][C::WA * NQW];
 };
 
-template <int G, bool VTAB>
+// A value tile of BYTES bytes (a multiple of 256), HBM -> LDS by buffer loads with an
+// LDS destination: whole kilobytes with 16 bytes per lane, then 256-byte pieces with 4.
+template <int BYTES>
+__device__ __forceinline__ void stage_bytes(__amdgpu_buffer_rsrc_t r, uint8_t* stage, int tile_off, int lane) {
+    static_assert(BYTES % 256 == 0, "whole 256-byte pieces");
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    constexpr int KB = BYTES / 1024, R = (BYTES % 1024) / 256;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * k), 16, 16 * lane, tile_off + 1024 * k, 0,
+                                                 kStreamPolicy);
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * KB + 256 * k), 4, 4 * lane,
+                                                 tile_off + 1024 * KB + 256 * k, 0, kStreamPolicy);
+}
+
+// ---------------------------------------------------------------------------
+// turbo3 (PQ3) blocks on the same matrix products.  A 32-coordinate PQ3 block ([fp16 norm]
+// [8 bytes of low bit pairs][4 bytes of high bits], [P1] sections 2 and 4) is the slice of a
+// vector that one lane group of a score product covers, so a lane loads one block of one
+// token (16 bytes at the block's 4-byte-aligned start) and turns each run of 8 coordinates
+// into a word of four table indexes, one per coordinate pair: the pair's two low bit pairs
+// in bits 0-3 and its two high bits in bits 4-5 (a 64-entry table gives both centroids).
+// Each block has its own norm, so every product must cover one block: a transpose across
+// the four lane groups (two lane-swap steps) gives lane group g run g of every block.
+
+// Index word of a run: lo = its low bits placed by a byte permute as [b0, 0, b1, 0]
+// (coordinate e of the run at bits 2e of b1:b0), hi = its high-bit byte (coordinate e at
+// bit e) alone in bits 0-7.
+__device__ __forceinline__ uint32_t pq3_index_word(uint32_t lo, uint32_t hi) {
+    lo = ((lo << 4) | lo) & 0x0F0F0F0Fu;    // nibble k (pair k's low bits) in byte k
+    hi = ((hi << 12) | hi) & 0x000F000Fu;   // pairs 0, 1 in bits 0-3, pairs 2, 3 in bits 16-19
+    hi = ((hi << 6) | hi) & 0x03030303u;    // pair k's high bits in bits 0-1 of byte k
+    return (hi << 4) | lo;
+}
+
+// Byte-permute selectors of a lane whose block starts off = 0 or 2 bytes into its aligned
+// 16 bytes r0..r3: run s's two low-bit bytes (block bytes 2 + 2s, 3 + 2s) out of (r1:r0)
+// for s = 0, 1 and (r2:r1) for s = 2, 3, and its high-bit byte (block byte 10 + s) out of (r3:r2).
+struct Pq3Sel {
+    uint32_t lo_a, lo_b, hi0;
+};
+__device__ __forceinline__ Pq3Sel pq3_selectors(uint32_t off) {
+    const uint32_t a = off + 2, b = off + 4;
+    return {0x0C000C00u | a | (a + 1) << 16, 0x0C000C00u | b | (b + 1) << 16, 0x0C0C0C00u | (off + 2)};
+}
+
+// The four index words (runs 0..3) and the fp16 norm bits of the block in r.
+__device__ __forceinline__ void pq3_block(const u32x4u& r, const Pq3Sel& sel, uint32_t off8, uint32_t (&w)[4],
+                                          uint32_t& norm) {
+    norm = __builtin_amdgcn_ubfe(r[0], off8, 16);
+    w[0] = pq3_index_word(__builtin_amdgcn_perm(r[1], r[0], sel.lo_a), __builtin_amdgcn_perm(r[3], r[2], sel.hi0));
+    w[1] = pq3_index_word(__builtin_amdgcn_perm(r[1], r[0], sel.lo_b),
+                          __builtin_amdgcn_perm(r[3], r[2], sel.hi0 + 1));
+    w[2] = pq3_index_word(__builtin_amdgcn_perm(r[2], r[1], sel.lo_a),
+                          __builtin_amdgcn_perm(r[3], r[2], sel.hi0 + 2));
+    w[3] = pq3_index_word(__builtin_amdgcn_perm(r[2], r[1], sel.lo_b),
+                          __builtin_amdgcn_perm(r[3], r[2], sel.hi0 + 3));
+}
+
+// 4 x 4 transpose across the lane groups (rows of 16 lanes): on return x[i] of lane group
+// g holds what x[g] of lane group i held.
+__device__ __forceinline__ void group_transpose(uint32_t (&x)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    x[0] = c[0];
+    x[1] = c[1];
+    x[2] = d[0];
+    x[3] = d[1];
+}
+
+// x of lane group i, for i = 0..3, in every lane group
+__device__ __forceinline__ void group_broadcast(uint32_t x, uint32_t (&out)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);  // [x0 x1 x0 x1], [x2 x3 x2 x3]
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+    out[0] = b[0];
+    out[1] = b[1];
+    out[2] = c[0];
+    out[3] = c[1];
+}
+
+// 4 x 4 byte transpose inside a lane: byte q of out[k] is byte k of x[q].
+__device__ __forceinline__ void byte_transpose(const uint32_t (&x)[4], uint32_t (&out)[4]) {
+    const uint32_t p01 = __builtin_amdgcn_perm(x[1], x[0], 0x05010400u);  // x0b0 x1b0 x0b1 x1b1
+    const uint32_t p23 = __builtin_amdgcn_perm(x[3], x[2], 0x05010400u);
+    const uint32_t q01 = __builtin_amdgcn_perm(x[1], x[0], 0x07030602u);  // x0b2 x1b2 x0b3 x1b3
+    const uint32_t q23 = __builtin_amdgcn_perm(x[3], x[2], 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(p23, p01, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(q23, q01, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(q23, q01, 0x07060302u);
+}
+
+template <int G, bool VTAB, int KF = TQ_FMT_PQ4, int VF = TQ_FMT_PQ4>
 __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_partial_sparse_kernel(
     DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
     static_assert(G == 4 || G == 8, "four heads per 16-row block");
     static_assert(!VTAB || G == 4, "two tables fit the LDS at G = 4 only");
     using C = SpCfg<G>;
-    constexpr int D = C::D, VB = C::VB, NTB = C::NTB, RB = C::RB, TT = C::TT;
-    // values through LDS where the two stages fit next to the table (G = 4, one table)
+    constexpr int D = C::D, NTB = C::NTB, RB = C::RB, TT = C::TT;
+    constexpr bool K3 = KF == TQ_FMT_PQ3, V3 = VF == TQ_FMT_PQ3, PQ4PAIR = !K3 && !V3;
+    constexpr int VBK = K3 ? 56 : 68, VBV = V3 ? 56 : 68;  // bytes per token of keys and values
+    // values through LDS where the two stages fit next to the table (G = 4, one table); PQ3
+    // values instead come through registers (two tile buffers) and an LDS index tile
     constexpr bool VLDS = G == 4 && !VTAB;
-    constexpr int STAGE = StageShape<TT * VB>::SIZE;
-    __shared__ __align__(16) SmemSp<G, VTAB> sm;
+    static_assert(!V3 || (VLDS && K3), "PQ3 values with PQ3 keys and one table");
+    static_assert(PQ4PAIR || G == 4, "PQ3 at four query heads per KV head");
+    constexpr bool STAGED = VLDS && !V3;  // value stages filled by buffer-to-LDS loads
+    constexpr int STAGE = StageShape<TT * (V3 ? 68 : VBV)>::SIZE;  // (no stages with PQ3 values)
+    __shared__ __align__(16) SmemSp<G, VTAB, KF, VF> sm;
     // two stages in distinct LDS objects: the compiler's wait for one stage's loads then
     // ignores the other stage's
-    __shared__ __align__(16) uint8_t vst0[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
-    __shared__ __align__(16) uint8_t vst1[VLDS ? kPairWaves : 1][VLDS ? STAGE : 16];
+    __shared__ __align__(16) uint8_t vst0[STAGED ? kPairWaves : 1][STAGED ? STAGE : 16];
+    __shared__ __align__(16) uint8_t vst1[STAGED ? kPairWaves : 1][STAGED ? STAGE : 16];
     // the rotated query heads of the group, when the kernel rotates the query itself
     __shared__ __align__(16) float qrot_sh[G][D];
     // key and value boundaries of the encoder, when the kernel appends the step's token
@@ -1236,12 +1348,31 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     const int end = s < a.splits ? min(start + a.split_len, N) : start;  // no tokens past the last split
 
     const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
-    const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
-    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
-    const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t krs =
+        stream_rsrc(a.k_cache + stream_row * VBK, static_cast<uint32_t>(a.capacity) * VBK);
+    const __amdgpu_buffer_rsrc_t vrs =
+        stream_rsrc(a.v_cache + stream_row * VBV, static_cast<uint32_t>(a.capacity) * VBV);
     const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
-    const int k_norm = n * VB, k_word = n * VB + 4 + 16 * g, v_norm = n * VB, v_word = 4 * g * VB + 4 + 4 * n;
+    // PQ4 keys: the norm and code words 4g..4g+3 of token n.  PQ3 keys and values: block g
+    // of token n, from the 4-byte-aligned start of its 14 bytes (p3_off bytes before it; a
+    // token's 56 bytes start aligned, so blocks 1 and 3 start 2 bytes into a dword)
+    const uint32_t p3_off = (14u * g) & 3u;
+    const int p3_word = n * 56 + 14 * g - static_cast<int>(p3_off);
+    const int k_norm = n * VBK, k_word = K3 ? p3_word : n * VBK + 4 + 16 * g;
+    const int v_norm = n * VBV, v_word = 4 * g * VBV + 4 + 4 * n;
+    const Pq3Sel p3_sel = pq3_selectors(p3_off);
     uint32_t* wa = sm.wa[wi];
+    // the keys of a tile: PQ4 through load_keys, PQ3 one 16-byte block per token block
+    auto p3_load = [&](KeyTile<NTB, 1>& k, __amdgpu_buffer_rsrc_t r, int tile_off) __attribute__((always_inline)) {
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+            k.w[tb][0] = __builtin_bit_cast(u32x4u, __builtin_amdgcn_raw_buffer_load_b128(r, p3_word + 16 * tb * 56,
+                                                                                         tile_off, kStreamPolicy));
+    };
+    auto keys_in = [&](KeyTile<NTB, 1>& k, __amdgpu_buffer_rsrc_t r, int tile_off) __attribute__((always_inline)) {
+        if constexpr (K3) p3_load(k, r, tile_off);
+        else load_keys<VBK>(k, r, k_norm, k_word, tile_off);
+    };
 
     // The small global reads of the prologue come first: a tile load issued before them would
     // have to complete before their values can be used (the memory counter drains in order).
@@ -1252,21 +1383,27 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     //     wi / 4; lane (row n, group g) holds, per group q, the pair (q_r, q_r) of coordinate
     //     2m + p, where m is the code byte that B lane group sp_lane_group(4g + q) reads as
     //     element quad sp_quad(4g + q).
+    //     PQ3 tables hold bytes 0..63 (k = 0, 1): byte i / 32 = t / 32 + 32 k has the first
+    //     code (t / 32) % 4 + 4 ((t / 512) % 2), the same for both k, and the second
+    //     (t / 128) % 4 + 4 k;
     static_assert(kPairWaves * 64 == 1024, "the table fill assumes 1024 threads");
-    const int lo_nib = (tid >> 5) & 15, hi_base = tid >> 9;
-    float ck_lo = cbk.centroids[lo_nib], ck_hi[8], cv_lo = 0.0f, cv_hi[8];
+    constexpr int KFILL = K3 ? 2 : 8, VFILL = V3 ? 2 : 8;
+    const int tb5 = tid >> 5;
+    auto code0 = [&](bool pq3) { return pq3 ? (tb5 & 3) | ((tb5 >> 4) & 1) << 2 : tb5 & 15; };
+    auto code1 = [&](bool pq3, int k) { return pq3 ? ((tb5 >> 2) & 3) | k << 2 : (tb5 >> 4) + 2 * k; };
+    float ck_lo = cbk.centroids[code0(K3)], ck_hi[KFILL], cv_lo = 0.0f, cv_hi[VFILL];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) ck_hi[k] = cbk.centroids[hi_base + 2 * k];
+    for (int k = 0; k < KFILL; ++k) ck_hi[k] = cbk.centroids[code1(K3, k)];
     if constexpr (VTAB) {
-        cv_lo = cbv.centroids[lo_nib];
+        cv_lo = cbv.centroids[code0(V3)];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) cv_hi[k] = cbv.centroids[hi_base + 2 * k];
+        for (int k = 0; k < VFILL; ++k) cv_hi[k] = cbv.centroids[code1(V3, k)];
     }
     // an unrotated query (values through LDS only): wavefronts wi < G / 4 rotate it below,
     // four heads each, with the arithmetic of the query rotation kernel (16 lanes per head,
     // 8 coordinates per lane: signs, Walsh-Hadamard butterflies, 1/sqrt(d)), so the rotated
     // values are the same bits.  The query and its sign word are read here, before the tiles.
-    const bool raw = VLDS && a.q_raw != nullptr;  // uniform
+    const bool raw = VLDS && PQ4PAIR && a.q_raw != nullptr;  // uniform
     const int rh = 4 * wi + (lane >> 4), rl = lane & 15;
     float rv[8];
     uint32_t rsign = 0;
@@ -1285,7 +1422,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     // when the position lies in one, else before the barrier that precedes every other tile.
     bool app = false, app_first = false;
     int apos = 0;
-    if (VLDS && a.new_pos != nullptr) {
+    if (VLDS && PQ4PAIR && a.new_pos != nullptr) {
         apos = a.new_pos[b];
         if (apos >= 0 && apos < a.capacity) {
             const int sp = min(apos / a.split_len, a.splits - 1);
@@ -1320,7 +1457,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             uint32_t n16, words[2];
             pq4_encode<128, 8>(araw, smask, b3, b7, b11, reinterpret_cast<const float4*>(app_sb[app_v ? 1 : 0]), al,
                                n16, words);
-            uint8_t* out = (app_v ? a.v_wr : a.k_wr) + ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + apos) * VB;
+            uint8_t* out = (app_v ? a.v_wr : a.k_wr) + ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + apos) * 68;
             pq4_store<128, 8>(out, al, n16, words);
         }
     };
@@ -1335,7 +1472,11 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int gd = 4 * g + q;
-            qv[q] = qg[2 * (16 * sp_lane_group(gd) + 4 * qI + sp_quad(gd)) + qp];
+            // the code byte (coordinate pair) that B lane group sp_lane_group(gd) reads as quad
+            // sp_quad(gd) of product qI: PQ4 word qI of its code group, PQ3 run g of block qI
+            const int m = K3 ? 16 * qI + 4 * sp_lane_group(gd) + sp_quad(gd)
+                             : 16 * sp_lane_group(gd) + 4 * qI + sp_quad(gd);
+            qv[q] = qg[2 * m + qp];
         }
     }
 
@@ -1344,20 +1485,24 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     // it through the empty resource (zeros, no memory read)
     int t0 = start + w * TT;
     KeyTile<NTB, 1> kt[VLDS ? 2 : 1];
+    KeyTile<NTB, 1> vraw[V3 ? 2 : 1];  // PQ3 value blocks, loaded as the keys are
     ValueTile<NTB, 1> vt;
     {
         const bool any = t0 < end;
         const __amdgpu_buffer_rsrc_t kr0 = any ? krs : krs_none, vr0 = any ? vrs : vrs_none;
-        load_keys<VB>(kt[0], kr0, k_norm, k_word, t0 * VB);
-        if constexpr (VLDS) stage_tile<TT * VB>(vr0, vst0[wi], t0 * VB, lane);
-        else load_values<VB>(vt, vr0, v_norm, v_word, t0 * VB);
+        keys_in(kt[0], kr0, t0 * VBK);
+        if constexpr (V3) p3_load(vraw[0], vr0, t0 * VBV);
+        else if constexpr (VLDS) stage_tile<TT * VBV>(vr0, vst0[wi], t0 * VBV, lane);
+        else load_values<VBV>(vt, vr0, v_norm, v_word, t0 * VBV);
     }
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        sm.u.op.table[tid + 1024 * k] = make_uint2(bf16_split(ck_lo), bf16_split(ck_hi[k]));
-        if constexpr (VTAB) sm.u.op.vtable[tid + 1024 * k] = make_uint2(bf16_split(cv_lo), bf16_split(cv_hi[k]));
+    for (int k = 0; k < KFILL; ++k) sm.u.op.table[tid + 1024 * k] = make_uint2(bf16_split(ck_lo), bf16_split(ck_hi[k]));
+    if constexpr (VTAB) {
+#pragma unroll
+        for (int k = 0; k < VFILL; ++k)
+            sm.u.op.vtable[tid + 1024 * k] = make_uint2(bf16_split(cv_lo), bf16_split(cv_hi[k]));
     }
     if (app && !app_first) append_token();  // its tile is requested after the barrier below
     if (raw) {
@@ -1437,27 +1582,66 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
         const uint8_t* vcur = P == 0 ? vst0[wi] : vst1[wi];
         if constexpr (VLDS) {
-            stage_tile<TT * VB>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VB, lane);
-            load_keys<VB>(kt[1 - P], krn, k_norm, k_word, t_next * VB);
+            if constexpr (V3) p3_load(vraw[1 - P], vrn, t_next * VBV);
+            else stage_tile<TT * VBV>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VBV, lane);
+            keys_in(kt[1 - P], krn, t_next * VBK);
         }
 
         // ---- scores: job J = I * NTB + tb reads bytes 0..3 of key word I of block tb
-        f32x4 dsc[NTB][RB];
+        // PQ4: the four products of a token block accumulate in dsc.  PQ3: one product per
+        // block of 32 coordinates, each from zero into a ring slot and folded into sacc with its
+        // block's norm one job later (so no product waits on the previous one)
+        constexpr int NI = K3 ? 4 : 1;
+        f32x4 dsc[NTB][RB], dring[K3 ? 2 : 1][RB];
+        float sacc[NTB][RB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) dsc[tb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int rb = 0; rb < RB; ++rb) {
+                dsc[tb][rb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                sacc[tb][rb] = 0.0f;
+            }
+        // this lane's four code words of each token block (PQ3: the index words of run g of
+        // blocks 0..3) and the key norms of its token (PQ3: of blocks 0..3)
+        // (PQ3: fp16 norms of blocks 0..3, token blocks 0 and 1 in the low and high halves)
+        uint32_t kw[NTB][4], knorm[4];
         float nk[NTB];
+        if constexpr (K3) {
+            static_assert(NTB == 2, "two token blocks share one norm word");
+            uint32_t nb[NTB];
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) nk[tb] = half_bits_to_float(kc.norm[tb][0]);
+            for (int tb = 0; tb < NTB; ++tb) {
+                pq3_block(kc.w[tb][0], p3_sel, 8u * p3_off, kw[tb], nb[tb]);
+                group_transpose(kw[tb]);
+            }
+            group_broadcast(nb[0] | nb[1] << 16, knorm);
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) kw[tb][i] = kc.w[tb][0][i];
+                nk[tb] = half_bits_to_float(kc.norm[tb][0]);
+            }
+        }
         {
             constexpr int NJ = 4 * NTB;
             u32x8 ring[R];
+            // fold product M of a PQ3 key tile: its block's norm times its row-summed column
+            auto fold = [&](auto mc) __attribute__((always_inline)) {
+                constexpr int M = decltype(mc)::value, I = M / NTB, TB = M % NTB;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const f32x4 d4 = dring[M % 2][rb];
+                    const float nrm = half_bits_to_float((knorm[I] >> (16 * TB)) & 0xFFFFu);
+                    sacc[TB][rb] = fmaf(nrm, (d4[0] + d4[1]) + (d4[2] + d4[3]), sacc[TB][rb]);
+                }
+            };
             static_for<NJ + LA>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
+                if constexpr (K3 && J >= LA + 1) fold(std::integral_constant<int, J - LA - 1>{});
                 if constexpr (J < NJ) {
                     constexpr int I = J / NTB, TB = J % NTB;
-                    const uint32_t x = kc.w[TB][0][I];
+                    const uint32_t x = kw[TB][I];
                     put_byte1<0>(addr[0], x);
                     put_byte1<1>(addr[1], x);
                     put_byte1<2>(addr[2], x);
@@ -1475,21 +1659,49 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         const u32x4 aop = RB == 1 ? qreg[RB == 1 ? I : 0] : sm.u.op.qa[rb][I][lane];
-                        dsc[TB][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, aop), bop,
-                                                                               dsc[TB][rb], sp_idx, 0, 0);
+                        if constexpr (K3)
+                            dring[M % 2][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+                                __builtin_bit_cast(bf16x8, aop), bop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sp_idx, 0, 0);
+                        else
+                            dsc[TB][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, aop), bop,
+                                                                                   dsc[TB][rb], sp_idx, 0, 0);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
+            if constexpr (K3) fold(std::integral_constant<int, NJ - 1>{});
         }
-        if constexpr (!VLDS) load_keys<VB>(kt[0], krn, k_norm, k_word, t_next * VB);
-        if constexpr (VLDS) {  // this tile's value words and norms, from its stage
+        if constexpr (!VLDS) keys_in(kt[0], krn, t_next * VBK);
+        // PQ3 value norms of token 16 tb + n, blocks 0..3 (fp16, token blocks in the two halves)
+        uint32_t vnorm[4];
+        if constexpr (V3) {
+            // this tile's value blocks as index words: lane (n, g) turns block g of token n into
+            // the words of pairs 4g .. 4g+3 of all four blocks (byte Q: block Q) and stores them
+            // in token n's row; lane (n, g) then reads word n of tokens 4g .. 4g+3, whose byte Q
+            // the value product for block Q looks up
+            uint32_t* vi = sm.u.op.vidx[wi];
+            uint32_t nb[NTB];
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
-                vt.norm[tb][0] = *reinterpret_cast<const uint16_t*>(vcur + (16 * tb + n) * VB);
+                uint32_t x[4], t4[4];
+                pq3_block(vraw[P].w[tb][0], p3_sel, 8u * p3_off, x, nb[tb]);
+                group_transpose(x);
+                byte_transpose(x, t4);
+                *reinterpret_cast<u32x4*>(vi + lds_offset((16 * tb + n) * 20 + 4 * g)) = u32x4{t4[0], t4[1], t4[2], t4[3]};
+            }
+            group_broadcast(nb[0] | nb[1] << 16, vnorm);
+            lds_order();
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vt.w[tb][0][u] = vi[lds_offset((16 * tb + 4 * g + u) * 20 + n)];
+        } else if constexpr (VLDS) {  // this tile's value words and norms, from its stage
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) {
+                vt.norm[tb][0] = *reinterpret_cast<const uint16_t*>(vcur + (16 * tb + n) * VBV);
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    vt.w[tb][0][u] = *reinterpret_cast<const uint32_t*>(vcur + (16 * tb + 4 * g + u) * VB + 4 + 4 * n);
+                    vt.w[tb][0][u] = *reinterpret_cast<const uint32_t*>(vcur + (16 * tb + 4 * g + u) * VBV + 4 + 4 * n);
             }
         }
 
@@ -1504,7 +1716,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const f32x4 d4 = dsc[tb][rb];
-                const float sc = nk[tb] * ((d4[0] + d4[1]) + (d4[2] + d4[3]));
+                const float sc = K3 ? sacc[tb][rb] : nk[tb] * ((d4[0] + d4[1]) + (d4[2] + d4[3]));
                 tv[tb][rb] = ok ? sc : -INFINITY;
                 mx[rb] = fmaxf(mx[rb], tv[tb][rb]);
             }
@@ -1537,7 +1749,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             // rows past the sequence end hold whatever the cache held: weight exactly 0
-            const float nvn = 16 * tb + n < nv ? half_bits_to_float(vt.norm[tb][0]) : 0.0f;
+            const float nvn = 16 * tb + n < nv ? (V3 ? 1.0f : half_bits_to_float(vt.norm[tb][0])) : 0.0f;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const float p = __builtin_amdgcn_exp2f(tv[tb][rb] - m_run[rb]);
@@ -1554,30 +1766,45 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int tb = 0; tb < NTB; ++tb) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const float wt = wts[tb][rb];
-                    const uint32_t bits = __float_as_uint(wt);
-                    const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                    uint32_t* dst = wa + lds_offset<VLDS>(w_lane + (tb * G + 4 * rb) * 32);
-                    dst[0] = dup_hi16(bits);
-                    dst[16] = dup_hi16(__float_as_uint(lo));
+#pragma unroll
+                    for (int i = 0; i < (V3 ? 4 : 1); ++i) {  // PQ3: the weight times the norm of block i
+                        // (past the end the weight is 0 and the norm bits are not read)
+                        const float wt = V3 ? (wts[tb][rb] != 0.0f
+                                                   ? wts[tb][rb] * half_bits_to_float((vnorm[i] >> (16 * tb)) & 0xFFFFu)
+                                                   : 0.0f)
+                                            : wts[tb][rb];
+                        const uint32_t bits = __float_as_uint(wt);
+                        const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
+                        uint32_t* dst = wa + lds_offset<VLDS>(i * C::WA + w_lane + (tb * G + 4 * rb) * 32);
+                        dst[0] = dup_hi16(bits);
+                        dst[16] = dup_hi16(__float_as_uint(lo));
+                    }
                 }
             }
             lds_order();
 
             // ---- values: job J = tb * 4 + Q reads byte Q of code word n of tokens 4g .. 4g+3
             {
-                u32x4 av[NTB][RB];
-#pragma unroll
-                for (int tb = 0; tb < NTB; ++tb)
+                // A operands: PQ4 one per token block, read here; PQ3 one per (token block, block
+                // of 32), read with the lookups of their job into a ring
+                u32x4 av[V3 ? R : NTB][RB];
+                auto read_a = [&](u32x4 (&dst)[RB], int i, int tb) __attribute__((always_inline)) {
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
-                        av[tb][rb] = *reinterpret_cast<const u32x4*>(wa + lds_offset<VLDS>(rd_lane + (tb * G + 4 * rb) * 32));
+                        dst[rb] = *reinterpret_cast<const u32x4*>(
+                            wa + lds_offset<VLDS>(i * C::WA + rd_lane + (tb * G + 4 * rb) * 32));
+                };
+                if constexpr (!V3) {
+#pragma unroll
+                    for (int tb = 0; tb < NTB; ++tb) read_a(av[tb], 0, tb);
+                }
                 constexpr int NJ = 4 * NTB;
                 u32x8 ring[R];
                 static_for<NJ + LA>([&](auto jc) {
                     constexpr int J = decltype(jc)::value;
                     if constexpr (J < NJ) {
                         constexpr int TB = J / 4, Q = J % 4;
+                        if constexpr (V3) read_a(av[J % R], Q, TB);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB][0][u]);
 #pragma unroll
@@ -1592,15 +1819,15 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                         const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
 #pragma unroll
                         for (int rb = 0; rb < RB; ++rb)
-                            acc[rb][Q] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av[TB][rb]), bop,
-                                                                                  acc[rb][Q], sp_idx, 0, 0);
+                            acc[rb][Q] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+                                __builtin_bit_cast(bf16x8, av[V3 ? M % R : TB][rb]), bop, acc[rb][Q], sp_idx, 0, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
             }
             lds_order();
         }
-        if constexpr (!VLDS) load_values<VB>(vt, vrn, v_norm, v_word, t_next * VB);
+        if constexpr (!VLDS) load_values<VBV>(vt, vrn, v_norm, v_word, t_next * VBV);
     };
     if constexpr (VLDS) {
         // pairs of tiles, so that the parity is static; the second tile of the last pair may be
@@ -1631,7 +1858,8 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int Q = 0; Q < 4; ++Q)
 #pragma unroll
-            for (int p = 0; p < 2; ++p) r[2 + 8 * n + 2 * Q + p] = acc[rb][Q][p] + acc[rb][Q][2 + p];
+            for (int p = 0; p < 2; ++p)  // coordinate 2m + p of pair m: PQ4 byte Q of word n, PQ3 pair n of block Q
+                r[2 + (V3 ? 32 * Q + 2 * n : 8 * n + 2 * Q) + p] = acc[rb][Q][p] + acc[rb][Q][2 + p];
     }
     __syncthreads();
     if (s < a.splits) {
@@ -1710,23 +1938,6 @@ struct SmemTq {
     } u;
     alignas(16) uint16_t wa[C::WAVES][C::NGRP][16][C::TT];  // value A operands [group][row][token]
 };
-
-// A value tile of BYTES bytes (a multiple of 256), HBM -> LDS by buffer loads with an
-// LDS destination: whole kilobytes with 16 bytes per lane, then 256-byte pieces with 4.
-template <int BYTES>
-__device__ __forceinline__ void stage_bytes(__amdgpu_buffer_rsrc_t r, uint8_t* stage, int tile_off, int lane) {
-    static_assert(BYTES % 256 == 0, "whole 256-byte pieces");
-    using lds_ptr = __attribute__((address_space(3))) void*;
-    constexpr int KB = BYTES / 1024, R = (BYTES % 1024) / 256;
-#pragma unroll
-    for (int k = 0; k < KB; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * k), 16, 16 * lane, tile_off + 1024 * k, 0,
-                                                 kStreamPolicy);
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * KB + 256 * k), 4, 4 * lane,
-                                                 tile_off + 1024 * KB + 256 * k, 0, kStreamPolicy);
-}
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -2135,9 +2346,11 @@ int auto_split_tokens(const tq_layout* L) {
     //   * TQ3K keys at d = 128 (matrix-core kernel, eight wavefronts and 136 KB of LDS per
     //     workgroup): one workgroup per CU, about 256 splits;
     const int G = L->n_kv_heads > 0 ? L->n_q_heads / L->n_kv_heads : 0;
+    //   * PQ3 keys at d = 128, G = 4 (the 2:4-sparse kernel too): as PQ4.
     const bool pq4 = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && (G == 4 || G == 8);
+    const bool pq3 = L->k_format == TQ_FMT_PQ3 && L->head_dim == 128 && G == 4;
     const bool tq3k = L->k_format == TQ_FMT_TQ3K && L->head_dim == 128 && G <= 8;
-    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 512) : tq3k ? 256 : 2048;
+    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 512) : pq3 ? 1024 : tq3k ? 256 : 2048;
     long want = (target + streams - 1) / streams;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
@@ -2179,12 +2392,12 @@ int launch_partial(const DecodeArgs& a, const tq_layout* L, const tq_codebook& c
 // tokens per wavefront tile of the bf16 decode kernel (16 or a multiple of 16 dividing 64)
 constexpr int kBf16Tile = 32;
 
-template <int G, bool VTAB>
+template <int G, bool VTAB, int KF = TQ_FMT_PQ4, int VF = TQ_FMT_PQ4>
 int launch_partial_sparse(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                           const Launch& l) {
     dim3 grid((a.splits + kPairSub - 1) / kPairSub, L->n_kv_heads, L->batch);
-    return launch_kernel(decode_partial_sparse_kernel<G, VTAB>, grid, dim3(kPairWaves * 64), l, a, to_dev(cbk),
-                         to_dev(cbv));
+    return launch_kernel(decode_partial_sparse_kernel<G, VTAB, KF, VF>, grid, dim3(kPairWaves * 64), l, a,
+                         to_dev(cbk), to_dev(cbv));
 }
 
 // K and V decode through one table only when their centroids are identical
@@ -2203,13 +2416,23 @@ bool rotates_in_kernel(const tq_layout* L, const tq_codebook& cbk, const tq_code
            same_centroids(cbk, cbv);
 }
 
-// The kernels that merge a stream's records themselves when given an output: the
-// 2:4-sparse PQ4 kernel (d 128, G = 4, or G = 8 with one table).  Mirrors dispatch_group.
+// The layouts that decode on the 2:4-sparse kernel (which also merges a stream's records
+// itself when given an output): d 128 with PQ4 keys and values at G = 4, or at G = 8 with
+// one table; PQ3 keys with PQ3 values of the same table, or with PQ4 values, at G = 4.
+// dispatch_group launches it exactly for these.
+bool sparse_kernel_serves(const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv) {
+    if (L->head_dim != 128) return false;
+    const int kf = L->k_format, vf = L->v_format, G = L->n_q_heads / L->n_kv_heads;
+    const size_t row = std::max(tq::vector_bytes(kf, 128), tq::vector_bytes(vf, 128));
+    if (static_cast<size_t>(L->capacity) * row > 0x7FFFFFFFu) return false;  // 32-bit buffer ranges
+    if (kf == TQ_FMT_PQ4 && vf == TQ_FMT_PQ4) return G == 4 || (G == 8 && same_centroids(cbk, cbv));
+    if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ3) return G == 4 && same_centroids(cbk, cbv);
+    if (kf == TQ_FMT_PQ3 && vf == TQ_FMT_PQ4) return G == 4;
+    return false;
+}
+
 bool merges_in_kernel(const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv) {
-    if (L->k_format != TQ_FMT_PQ4 || L->v_format != TQ_FMT_PQ4 || L->head_dim != 128) return false;
-    if (static_cast<size_t>(L->capacity) * 68 > 0x7FFFFFFFu) return false;
-    const int G = L->n_q_heads / L->n_kv_heads;
-    return G == 4 || (G == 8 && same_centroids(cbk, cbv));
+    return sparse_kernel_serves(L, cbk, cbv);
 }
 
 template <int D, int G>
@@ -2247,15 +2470,20 @@ int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_code
             }
         }
     }
+    if constexpr (D == 128 && KF == TQ_FMT_PQ3) {
+        if (sparse_kernel_serves(L, cbk, cbv)) {
+            if constexpr (VF == TQ_FMT_PQ3) return launch_partial_sparse<4, false, KF, VF>(a, L, cbk, cbv, st);
+            else if constexpr (VF == TQ_FMT_PQ4) return launch_partial_sparse<4, true, KF, VF>(a, L, cbk, cbv, st);
+        }
+    }
     if constexpr (KF == TQ_FMT_PQ4 && VF == TQ_FMT_PQ4) {
         // the matrix-core kernel addresses a stream through a 32-bit buffer range
         const bool fits = static_cast<size_t>(L->capacity) * vbytes<TQ_FMT_PQ4, D>() <= 0x7FFFFFFFu;
         if constexpr (D == 128) {
-            if (fits) {
-                const bool same = same_centroids(cbk, cbv);
-                if (G == 4) return same ? launch_partial_sparse<4, false>(a, L, cbk, cbv, st)
-                                        : launch_partial_sparse<4, true>(a, L, cbk, cbv, st);
-                if (G == 8 && same) return launch_partial_sparse<8, false>(a, L, cbk, cbv, st);
+            if (sparse_kernel_serves(L, cbk, cbv)) {
+                if (G == 4) return same_centroids(cbk, cbv) ? launch_partial_sparse<4, false>(a, L, cbk, cbv, st)
+                                                            : launch_partial_sparse<4, true>(a, L, cbk, cbv, st);
+                return launch_partial_sparse<8, false>(a, L, cbk, cbv, st);
             }
         }
         if (fits && G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);

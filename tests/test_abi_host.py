@@ -99,7 +99,9 @@ def test_splits_and_workspace_arithmetic():
     L = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
     s = tq.decode_splits(L)
     assert s >= 1 and 8 * 8 * s >= 1024  # PQ4, d 128, G 4: four splits per workgroup, one per CU
-    other = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ3, tq.FMT_PQ3)
+    pq3 = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ3, tq.FMT_PQ3)
+    assert 8 * 8 * tq.decode_splits(pq3) >= 1024  # PQ3 keys, d 128, G 4: the same 2:4-sparse kernel
+    other = tq.Layout(8, 40, 8, 128, 65536, tq.FMT_PQ3, tq.FMT_PQ3)
     assert 8 * 8 * tq.decode_splits(other) >= 2048  # one split per workgroup elsewhere
     # (m, l) records, value sums and one arrival counter per stream, each region 256-byte aligned
     recs = 8 * 32 * s

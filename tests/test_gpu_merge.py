@@ -11,8 +11,9 @@ workgroup that finishes a stream last merges it), on the GPU through the C ABI:
 * with an appended token, cache bytes and output equal those of the step without
   an output followed by the combine;
 * every output agrees with the oracle at the output tolerance.
-Layouts whose kernel does not merge (d 256, PQ3, five heads) run the combine after
-the partial and must give the same results too."""
+The 2:4-sparse kernel merges (PQ4 at four or eight heads, PQ3 keys at four); layouts
+whose kernel does not (d 256, five heads) run the combine after the partial and must give
+the same results too."""
 
 import numpy as np
 import pytest

@@ -304,6 +304,32 @@ def test_tq3k_keys_every_group_size_and_ragged_lengths(G, vfmt):
         _say(f"tq3k G={G} v={vfmt} split={split}: score err {es:.2e}, output err {eo:.2e}")
 
 
+@pytest.mark.parametrize("pair", ["pq3_pq3", "pq3_pq4", "pq3_pq3_two_tables"])
+def test_pq3_keys_ragged_lengths(pair):
+    """turbo3 keys on the 2:4-sparse kernel (PQ3 values of the same table, PQ4 values) and on
+    the generic kernel (PQ3 values of another table): contexts of 0, 1, a token block, a tile,
+    one past it, one split, one past a split and the full capacity over garbage-filled caches,
+    with the automatic and a 256-token split."""
+    vf, vb, vk = {"pq3_pq3": (synth.PQ3, 3, synth.QUANTILE_MEAN), "pq3_pq4": (synth.PQ4, 4, synth.QUANTILE_MEAN),
+                  "pq3_pq3_two_tables": (synth.PQ3, 3, synth.LLOYD_MAX)}[pair]
+    w = synth.scaled(synth.C2, v_format=vf, v_bits=vb, v_kind=vk, batch=8, n_q_heads=8, n_kv_heads=2, context=1024,
+                     capacity=1024)
+    st = P.Setup(w)
+    L = st.layout()
+    lens = [0, 1, 16, 33, 255, 257, 700, 1024]
+    kb, vbytes, kdq, vdq = _oracle_cache(st, w, lens)
+    kc = _garbage_cache(st, L, synth.K_TENSOR, kb)
+    vc = _garbage_cache(st, L, synth.V_TENSOR, vbytes)
+    q = synth.queries(w)
+    for split in (0, 256):
+        out, scores, _, _ = P.gpu_decode(st, L, q, kc, vc, lens, split_tokens=split)
+        es, eo = P.check_read(st, q, kdq, vdq, lens, out, scores, w.capacity)
+        assert np.all(out[0] == 0.0)
+        for b, n in enumerate(lens):  # scores are written only below the context length
+            assert np.all(np.isnan(scores[b, :, n:]))
+        _say(f"pq3 keys {pair} split={split}: score err {es:.2e}, output err {eo:.2e}")
+
+
 def test_timed_partial_matches_untimed():
     """tq_decode_partial_timed writes the same records as tq_decode_partial and
     its events span a positive kernel time."""
