@@ -1564,8 +1564,13 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     // small as they can be and more values drop (not in the kernels that hold the values in
     // registers: the register costs them a spill)
     const float slack = VLDS && a.v_skip > 0.0f ? 0.0f : kRescaleSlack;
-    const uint32_t w_lane = g * 32 + sp_group(n >> 2, n & 3);
-    const uint32_t rd_lane = ((n >> 2) * 2 + ((n >> 1) & 1)) * 16 + 4 * g;
+    // (lane parts of LDS word offsets, kept whole once so per-tile constants fold into the
+    // instructions' offset fields)
+    const uint32_t w_lane = lds_offset<VLDS>(g * 32 + sp_group(n >> 2, n & 3));
+    const uint32_t rd_lane = lds_offset<VLDS>(((n >> 2) * 2 + ((n >> 1) & 1)) * 16 + 4 * g);
+    // PQ3 value index tile: lane (n, g) writes words 4g .. 4g+3 of token n's row and reads word n
+    // of the rows of tokens 4g .. 4g+3
+    const uint32_t vi_wr = lds_offset(n * 20 + 4 * g), vi_rd = lds_offset(4 * g * 20 + n);
     constexpr int kStep = kWaves * TT;
     constexpr int LA = kSpLookahead, R = LA + 1;
 
@@ -1590,9 +1595,9 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         // ---- scores: job J = I * NTB + tb reads bytes 0..3 of key word I of block tb
         // PQ4: the four products of a token block accumulate in dsc.  PQ3: one product per
         // block of 32 coordinates, each from zero into a ring slot and folded into sacc with its
-        // block's norm one job later (so no product waits on the previous one)
+        // block's norm after the next job's lookups (so no fold waits on a product in flight)
         constexpr int NI = K3 ? 4 : 1;
-        f32x4 dsc[NTB][RB], dring[K3 ? 2 : 1][RB];
+        f32x4 dsc[NTB][RB], dring[K3 ? 3 : 1][RB];
         float sacc[NTB][RB];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb)
@@ -1631,14 +1636,13 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 constexpr int M = decltype(mc)::value, I = M / NTB, TB = M % NTB;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const f32x4 d4 = dring[M % 2][rb];
+                    const f32x4 d4 = dring[M % 3][rb];
                     const float nrm = half_bits_to_float((knorm[I] >> (16 * TB)) & 0xFFFFu);
                     sacc[TB][rb] = fmaf(nrm, (d4[0] + d4[1]) + (d4[2] + d4[3]), sacc[TB][rb]);
                 }
             };
-            static_for<NJ + LA>([&](auto jc) {
+            static_for<NJ + LA + (K3 ? 1 : 0)>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
-                if constexpr (K3 && J >= LA + 1) fold(std::integral_constant<int, J - LA - 1>{});
                 if constexpr (J < NJ) {
                     constexpr int I = J / NTB, TB = J % NTB;
                     const uint32_t x = kw[TB][I];
@@ -1653,14 +1657,15 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                         ring[J % R][2 * e + 1] = v.y;
                     }
                 }
-                if constexpr (J >= LA) {
+                if constexpr (K3 && J >= LA + 2) fold(std::integral_constant<int, J - LA - 2>{});
+                if constexpr (J >= LA && J < NJ + LA) {
                     constexpr int M = J - LA, I = M / NTB, TB = M % NTB;
                     const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
                         const u32x4 aop = RB == 1 ? qreg[RB == 1 ? I : 0] : sm.u.op.qa[rb][I][lane];
                         if constexpr (K3)
-                            dring[M % 2][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+                            dring[M % 3][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
                                 __builtin_bit_cast(bf16x8, aop), bop, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, sp_idx, 0, 0);
                         else
                             dsc[TB][rb] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, aop), bop,
@@ -1669,7 +1674,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
-            if constexpr (K3) fold(std::integral_constant<int, NJ - 1>{});
+            if constexpr (K3) fold(std::integral_constant<int, NJ - 1>{});  // (NJ - 2 folded in the last job)
         }
         if constexpr (!VLDS) keys_in(kt[0], krn, t_next * VBK);
         // PQ3 value norms of token 16 tb + n, blocks 0..3 (fp16, token blocks in the two halves)
@@ -1685,16 +1690,17 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int tb = 0; tb < NTB; ++tb) {
                 uint32_t x[4], t4[4];
                 pq3_block(vraw[P].w[tb][0], p3_sel, 8u * p3_off, x, nb[tb]);
+                nb[tb] = 16 * tb + n < nv ? nb[tb] : 0u;  // past the end: norm 0 (the bits may be NaN)
                 group_transpose(x);
                 byte_transpose(x, t4);
-                *reinterpret_cast<u32x4*>(vi + lds_offset((16 * tb + n) * 20 + 4 * g)) = u32x4{t4[0], t4[1], t4[2], t4[3]};
+                *reinterpret_cast<u32x4*>(vi + vi_wr + 16 * 20 * tb) = u32x4{t4[0], t4[1], t4[2], t4[3]};
             }
             group_broadcast(nb[0] | nb[1] << 16, vnorm);
             lds_order();
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
-                for (int u = 0; u < 4; ++u) vt.w[tb][0][u] = vi[lds_offset((16 * tb + 4 * g + u) * 20 + n)];
+                for (int u = 0; u < 4; ++u) vt.w[tb][0][u] = vi[vi_rd + (16 * tb + u) * 20];
         } else if constexpr (VLDS) {  // this tile's value words and norms, from its stage
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
@@ -1768,14 +1774,11 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
                     for (int i = 0; i < (V3 ? 4 : 1); ++i) {  // PQ3: the weight times the norm of block i
-                        // (past the end the weight is 0 and the norm bits are not read)
-                        const float wt = V3 ? (wts[tb][rb] != 0.0f
-                                                   ? wts[tb][rb] * half_bits_to_float((vnorm[i] >> (16 * tb)) & 0xFFFFu)
-                                                   : 0.0f)
-                                            : wts[tb][rb];
+                        const float wt =
+                            V3 ? wts[tb][rb] * half_bits_to_float((vnorm[i] >> (16 * tb)) & 0xFFFFu) : wts[tb][rb];
                         const uint32_t bits = __float_as_uint(wt);
                         const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                        uint32_t* dst = wa + lds_offset<VLDS>(i * C::WA + w_lane + (tb * G + 4 * rb) * 32);
+                        uint32_t* dst = wa + w_lane + (i * C::WA + (tb * G + 4 * rb) * 32);
                         dst[0] = dup_hi16(bits);
                         dst[16] = dup_hi16(__float_as_uint(lo));
                     }
@@ -1792,7 +1795,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
                         dst[rb] = *reinterpret_cast<const u32x4*>(
-                            wa + lds_offset<VLDS>(i * C::WA + rd_lane + (tb * G + 4 * rb) * 32));
+                            wa + rd_lane + (i * C::WA + (tb * G + 4 * rb) * 32));
                 };
                 if constexpr (!V3) {
 #pragma unroll
