@@ -10,6 +10,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <cmath>
+#include <mutex>
+
 #include "tq_device.h"
 #include "tq_pq4.h"
 
@@ -404,6 +408,238 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
     }
 }
 
+// ---------------------------------------------------------------------------
+// PQ4 at d = 256 on the matrix cores.  The Sylvester transform of order 256 is
+// H[c'][c] = (-1)^popcount(c' & c), so splitting the 8 index bits into any two groups of four
+// makes it the Kronecker square of the order-16 one: with coordinate c = 64 g + 4 a + e
+// (a in 0..15, g and e in 0..3) read as M[a][4g + e] = s_c x_c, the rotated row is
+// Y = H16 M H16 / (16 n) with y_(64 g' + 4 a' + e') = Y[a'][4g' + e'] ([P1] section 1: norm,
+// normalize, rotate, nearest centroid); this split lets lane l read bytes 8l .. 8l+7 of the row.  M H16 is one fp16 product
+// (the inputs and the +-1 entries are exact in fp16, the sums fp32); its fp32 result, scaled
+// by 1 / (16 n), is already laid out as the second operand of H16 (M H16) and enters it as an
+// fp16 part plus the fp16 rounding of the remainder (two more products), so nothing moves
+// between lanes.  The codes come from a
+// 64-cell table: cell(y) = clamp(trunc(A y + B)) is monotone in y and each cell holds at
+// most one boundary (the host checks this in the same fp32 arithmetic), so
+// #{k : b_k < y} = #{k : cell(b_k) < cell(y)} + (y > the boundary of cell(y)).
+
+// 4 x 4 transpose across the lane groups (rows of 16 lanes): on return x[i] of lane group
+// g holds what x[g] of lane group i held.
+__device__ __forceinline__ void group_transpose(uint32_t (&x)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    x[0] = c[0];
+    x[1] = c[1];
+    x[2] = d[0];
+    x[3] = d[1];
+}
+
+// x of lane group i, for i = 0..3, in every lane group
+__device__ __forceinline__ void group_broadcast(uint32_t x, uint32_t (&out)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(a[0], a[0], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[1], a[1], false, false);
+    out[0] = b[0];
+    out[1] = b[1];
+    out[2] = c[0];
+    out[3] = c[1];
+}
+
+constexpr int kLutCells = 64, kLutCopies = 32;  // one copy per LDS bank pair
+constexpr int kD256Rows = 64;                   // rows per chunk: one row target per lane
+constexpr int kD256Chunks = 1;                  // chunks per wavefront
+constexpr int kD256Unroll = 4;                  // rows in flight per wavefront
+
+__device__ __forceinline__ uint32_t lut_cell(float y, float A, float B) {
+    return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(fmaf(y, A, B), 0.0f, static_cast<float>(kLutCells - 1)));
+}
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+template <Src SRC>
+__global__ __launch_bounds__(kWriteThreads) __attribute__((amdgpu_waves_per_eu(4))) void quantize_pq4_d256_kernel(
+    WriteArgs ak, WriteArgs av, DevCodebook cbk, DevCodebook cbv, int kblocks, int nblocks) {
+    static_assert(SRC != Src::kRotated, "fp16 sources");
+    constexpr int D = 256, U = kD256Unroll, NW = kWriteThreads / 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: row targets stay scalar
+    const int li = lane & 15, lg = lane >> 4;  // row of M (a) / column of the products (j); lane group
+
+    __shared__ uint2 lut[kLutCells * kLutCopies];  // (boundary bits, #{k : cell(b_k) < cell}) of (cell, copy)
+    __shared__ uint2 cells[kLutCells];
+    __shared__ uint8_t codes[NW][U][D];            // codes of the rows in flight, by coordinate
+
+    // H16[r][c] = (-1)^popcount(r & c): the second operand of M H16 (lane (j, g): H16[4g + i][j])
+    // is, H16 being symmetric, also the first operand of H16 (M H16) (lane (i, g): H16[i][4g + t])
+    half4_t hb;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) hb[t] = static_cast<_Float16>((__builtin_popcount((4 * lg + t) & li) & 1) ? -1.0f : 1.0f);
+
+    // Workgroups stay resident and take blocks of NW x 64 rows in turn: the key blocks first, then
+    // the value blocks, so a workgroup builds each table at most once.
+    int table = -1;  // 0: the keys' table is in LDS, 1: the values'
+    float A = 0.0f, B = 0.0f;
+    uint32_t sm0 = 0, sm1 = 0;
+    for (int blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const bool is_k = blk < kblocks;
+    // copies chosen by a uniform condition (a reference chosen at run time would put the kernel
+    // arguments in scratch memory)
+    const WriteArgs a = is_k ? ak : av;
+    const int block = is_k ? blk : blk - kblocks;
+    if (table != (is_k ? 0 : 1)) {
+        table = is_k ? 0 : 1;
+        const DevCodebook cb = is_k ? cbk : cbv;
+        A = static_cast<float>(kLutCells - 2) / (cb.bounds[14] - cb.bounds[0]);
+        B = fmaf(-cb.bounds[0], A, 1.0f);
+        __syncthreads();  // the previous table's last lookups are done
+        if (tid < kLutCells) {
+            uint32_t k0 = 0;
+            float bs = INFINITY;
+#pragma unroll
+            for (int k = 0; k < 15; ++k) {
+                const uint32_t ck = lut_cell(cb.bounds[k], A, B);
+                k0 += ck < static_cast<uint32_t>(tid) ? 1u : 0u;
+                bs = ck == static_cast<uint32_t>(tid) ? cb.bounds[k] : bs;
+            }
+            cells[tid] = make_uint2(__float_as_uint(bs), k0);
+        }
+        // this lane's rotation signs (coordinates 64 lg + 4 li .. + 3; the word selected, not
+        // indexed, so the arguments stay out of scratch) as XOR masks of its two fp16 pairs
+        uint32_t sw = cb.sign_bits[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            if (2 * lg + (li >> 3) == i) sw = cb.sign_bits[i];
+        const uint32_t s4 = (sw >> (4 * (li & 7))) & 0xFu;
+        sm0 = ((s4 & 1u) << 15) | (((s4 >> 1) & 1u) << 31);
+        sm1 = (((s4 >> 2) & 1u) << 15) | (((s4 >> 3) & 1u) << 31);
+        __syncthreads();
+        for (int i = tid; i < kLutCells * kLutCopies; i += kWriteThreads) lut[i] = cells[i / kLutCopies];
+        __syncthreads();
+    }
+
+    // the wavefront's chunks of 64 rows: lane i finds the target of row i of a chunk once,
+    // rows read it by lane
+    static_assert(kD256Rows == 64, "one row target per lane");
+    const uint32_t copy = lane & (kLutCopies - 1);
+    for (int chunk = 0; chunk < kD256Chunks; ++chunk) {
+    const int vbase = ((block * NW + wv) * kD256Chunks + chunk) * kD256Rows;
+    const VecTarget<TQ_FMT_PQ4, D, SRC> mine = vec_target<TQ_FMT_PQ4, D, SRC>(a, vbase + lane);
+    const uint64_t active_rows = __builtin_amdgcn_ballot_w64(mine.active);
+    const uint32_t src_lo = static_cast<uint32_t>(mine.src_row), src_hi = static_cast<uint32_t>(mine.src_row >> 32);
+    const uint32_t off_lo = static_cast<uint32_t>(mine.off), off_hi = static_cast<uint32_t>(mine.off >> 32);
+    auto src_of = [&](int r) __attribute__((always_inline)) {
+        return static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(src_lo, r))) |
+               static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(src_hi, r))) << 32;
+    };
+    auto load_rows = [&](uint2 (&dst)[U], int first) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            dst[u] = *reinterpret_cast<const uint2*>(a.x + src_of(first + u) * D + 4 * lane);
+    };
+    uint2 raw[U], nxt[U];
+    load_rows(nxt, 0);
+    for (int it = 0; it < kD256Rows; it += U) {
+        // each stage runs over the U rows in flight, so the products of one row overlap the
+        // work on the others; the next rows' loads are in flight meanwhile
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = nxt[u];
+        if (it + U < kD256Rows) load_rows(nxt, it + U);
+        uint32_t x01[U], x23[U];
+        float ss[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            x01[u] = raw[u].x ^ sm0;
+            x23[u] = raw[u].y ^ sm1;
+            const half2_t h01 = __builtin_bit_cast(half2_t, x01[u]), h23 = __builtin_bit_cast(half2_t, x23[u]);
+            ss[u] = __builtin_amdgcn_fdot2(h23, h23, __builtin_amdgcn_fdot2(h01, h01, 0.0f, false), false);
+        }
+        f32x4_t p[U], y[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            p[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, make_uint2(x01[u], x23[u])), hb,
+                                                         f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        // the four norms at once: after a transpose across the lane groups, lane group g holds
+        // the partial sums of row g from all four groups; their sum over the group's 16 lanes is
+        // row g's squared norm, whose root and reciprocal every lane group takes for its row
+        static_assert(U % 4 == 0, "one row per lane group");
+        constexpr int NG = U / 4;
+        uint32_t scl[U], n16g[NG];
+#pragma unroll
+        for (int q = 0; q < NG; ++q) {
+            uint32_t part[4] = {__float_as_uint(ss[4 * q]), __float_as_uint(ss[4 * q + 1]),
+                                __float_as_uint(ss[4 * q + 2]), __float_as_uint(ss[4 * q + 3])};
+            group_transpose(part);
+            float sq = (__uint_as_float(part[0]) + __uint_as_float(part[1])) +
+                       (__uint_as_float(part[2]) + __uint_as_float(part[3]));
+            sq += lane_xor<1>(sq);
+            sq += lane_xor<2>(sq);
+            sq += lane_xor<4>(sq);
+            sq += lane_xor<8>(sq);
+            // the hardware root and reciprocal (within an ulp of the rounded results): the norm's
+            // fp16 rounding can move only within 1e-7 of an fp16 midpoint, y by under 1e-7 relative
+            const float n = __builtin_amdgcn_sqrtf(sq);
+            n16g[q] = float_to_half_bits(fminf(n, kFp16Max));
+            const float scale_g = (n > 0.0f ? __builtin_amdgcn_rcpf(n) : 0.0f) * 0.0625f;  // 1 / (n sqrt(256))
+            uint32_t b4[4];
+            group_broadcast(__float_as_uint(scale_g), b4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) scl[4 * q + i] = b4[i];
+        }
+        // H16 P1 / (16 n) as two fp16 products: P1 / (16 n) (at most 1/4 in size) split into an
+        // fp16 part and the fp16 rounding of its remainder, 22 significant bits together
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float sc = __uint_as_float(scl[u]);
+            const float v0 = p[u][0] * sc, v1 = p[u][1] * sc, v2 = p[u][2] * sc, v3 = p[u][3] * sc;
+            const half2_t h01 = __builtin_convertvector((float2_t{v0, v1}), half2_t);
+            const half2_t h23 = __builtin_convertvector((float2_t{v2, v3}), half2_t);
+            const half2_t l01 = __builtin_convertvector(
+                (float2_t{v0 - static_cast<float>(h01[0]), v1 - static_cast<float>(h01[1])}), half2_t);
+            const half2_t l23 = __builtin_convertvector(
+                (float2_t{v2 - static_cast<float>(h23[0]), v3 - static_cast<float>(h23[1])}), half2_t);
+            const half4_t hi{h01[0], h01[1], h23[0], h23[1]}, lo{l01[0], l01[1], l23[0], l23[1]};
+            y[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(hb, hi, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            y[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(hb, lo, y[u], 0, 0, 0);
+        }
+        // y[u][r] = Y[4 lg + r][li] of row u: rotated coordinate 64 (li / 4) + 16 lg + 4 r + li % 4
+        const int cbase = 64 * (li >> 2) + 16 * lg + (li & 3);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint2 e = lut[lut_cell(y[u][r], A, B) * kLutCopies + copy];
+                codes[wv][u][cbase + 4 * r] = static_cast<uint8_t>(e.y + (y[u][r] > __uint_as_float(e.x) ? 1u : 0u));
+            }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lanes 0..31 pack coordinates 8 lane .. 8 lane + 7 into a code word of the lane's block;
+        // lanes 32, 33 write the [fp16 norm][0] headers of blocks 0 and 1
+        const bool packer = lane < 32;
+        const uint32_t dst_off = packer ? 68 * (lane >> 4) + 4 + 4 * (lane & 15) : 68 * (lane - 32);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint2 c8 = *reinterpret_cast<const uint2*>(&codes[wv][u][8 * (lane & 31)]);
+            const uint32_t t0 = c8.x | (c8.x >> 4), t1 = c8.y | (c8.y >> 4);  // bytes 0, 2: two codes each
+            const uint32_t word =
+                packer ? __builtin_amdgcn_perm(t1, t0, 0x06040200u) : __builtin_amdgcn_readlane(n16g[u / 4], 16 * (u % 4));
+            const size_t off = static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(off_lo, it + u))) |
+                               static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(off_hi, it + u))) << 32;
+            if (((active_rows >> (it + u)) & 1u) && lane < 34) *reinterpret_cast<uint32_t*>(a.out + off + dst_off) = word;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    }
+    }
+}
+
 template <int FMT, int D, Src SRC>
 __global__ __launch_bounds__(kWriteThreads) void quantize_kernel(WriteArgs a, DevCodebook cb) {
     quantize_rows<FMT, D, SRC>(a, cb, blockIdx.x);
@@ -493,12 +729,62 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
     }
 }
 
+// Workgroups of kWriteThreads threads of `kernel` that the current device holds at once
+// (resident on every CU), found once per device and kernel.
+template <typename K>
+int resident_workgroups(K kernel) {
+    static std::mutex mu;
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 20;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWriteThreads, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
+            cus < 1)
+            return 1 << 20;  // unknown: one workgroup per block
+        cached[dev] = per_cu * cus;
+    }
+    return cached[dev];
+}
+
+// Whether the 64-cell code table of quantize_pq4_d256_kernel serves a codebook: finite
+// increasing boundaries b_0 .. b_14 whose cells, in the kernel's own fp32 arithmetic
+// (A = 62 / (b_14 - b_0), B = fma(-b_0, A, 1), cell = clamp(trunc(fma(b, A, B)), 0, 63)),
+// all differ, so no cell holds two boundaries.
+bool pq4_lut_serves(const tq_codebook& cb) {
+    for (int k = 0; k < 15; ++k)
+        if (!std::isfinite(cb.bounds[k])) return false;
+    if (!(cb.bounds[14] > cb.bounds[0])) return false;
+    const float A = static_cast<float>(kLutCells - 2) / (cb.bounds[14] - cb.bounds[0]);
+    const float B = std::fmaf(-cb.bounds[0], A, 1.0f);
+    long prev = -1;
+    for (int k = 0; k < 15; ++k) {
+        const float t = std::fmin(std::fmax(std::fmaf(cb.bounds[k], A, B), 0.0f), static_cast<float>(kLutCells - 1));
+        const long c = static_cast<long>(t);
+        if (c <= prev) return false;
+        prev = c;
+    }
+    return true;
+}
+
 // PQ4 from fp16 rows: keys (ak) and, when av.nvec > 0, values in one launch
 template <int D, Src SRC>
 int launch_pq4(const WriteArgs& ak, const WriteArgs& av, const tq_codebook& cbk, const tq_codebook& cbv,
                hipStream_t st) {
     constexpr int VPP = kWriteThreads / pq4_lanes<D>();  // vectors per pass
     if (ak.nvec + av.nvec == 0) return TQ_OK;
+    if constexpr (D == 256) {
+        if (pq4_lut_serves(cbk) && (av.nvec == 0 || pq4_lut_serves(cbv))) {
+            constexpr int VPG = kWriteThreads / 64 * kD256Rows * kD256Chunks;  // vectors per block
+            const int kblocks = (ak.nvec + VPG - 1) / VPG, vblocks = (av.nvec + VPG - 1) / VPG;
+            const int grid = std::min(kblocks + vblocks, resident_workgroups(quantize_pq4_d256_kernel<SRC>));
+            hipLaunchKernelGGL((quantize_pq4_d256_kernel<SRC>), dim3(grid), dim3(kWriteThreads), 0, st, ak, av,
+                               to_dev(cbk), to_dev(cbv), kblocks, kblocks + vblocks);
+            return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+        }
+    }
     if (static_cast<long>(ak.nvec) + av.nvec <= kPq4SmallVectors) {
         const int kblocks = (ak.nvec + VPP - 1) / VPP, vblocks = (av.nvec + VPP - 1) / VPP;
         hipLaunchKernelGGL((quantize_pq4_kernel<D, SRC, 1>), dim3(kblocks + vblocks), dim3(kWriteThreads), 0, st, ak,
