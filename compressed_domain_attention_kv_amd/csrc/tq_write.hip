@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <vector>
 
 #include "tq_device.h"
 #include "tq_pq4.h"
@@ -729,24 +730,211 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
     }
 }
 
+// ---------------------------------------------------------------------------
+// TQ3K keys at d = 128 with the QJL sketch on the matrix cores ([P2] write path: 2-bit
+// MSE codes of the rotated unit vector, then the sign bits of S r for the residual r
+// rotated back, with its norm gamma).  A workgroup takes batches of 64 vectors:
+//   1. sixteen lanes per vector, 8 coordinates each, compute the norm, the rotation, the
+//      codes, the residual and gamma with the same arithmetic as the generic kernel, the
+//      lane moves of the transforms and sums done by DPP; the residual, scaled by 2^10
+//      (a power of two: the signs do not change, and its small entries stay normal fp16
+//      numbers), goes to LDS as an fp16 part and the fp16 rounding of the remainder;
+//   2. S R for the 64 residuals on the fp16 matrix cores, wavefront w taking rows
+//      32w .. 32w+31 of S, held in registers as fp16 parts and remainders; the products
+//      hi*hi + hi*lo + lo*hi keep about 22 significant bits (the signs flip only where
+//      |(S r)_i| is within about 1e-6 of |S_i| |r|); each row's sign goes to LDS as a byte
+//      already shifted to its bit of the output byte;
+//   3. each thread ORs 8 of those bytes into one sketch byte, four per output dword.
+constexpr int kTq3kBatch = 64;   // vectors per batch
+constexpr int kTq3kRow = 136;    // halves per residual row in LDS (16 B of padding: distinct banks)
+constexpr int kTq3kSgnRow = 132; // bytes per sign row in LDS
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// v <- H v for 8 coordinates per lane over the 16 lanes of a DPP row (coordinate 8 l + e)
+__device__ __forceinline__ void wht8_row16(float (&v)[8], int l) {
+#pragma unroll
+    for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & st) == 0) {
+                const float x = v[e], y = v[e + st];
+                v[e] = x + y;
+                v[e + st] = x - y;
+            }
+    static_for<4>([&](auto mc) {
+        constexpr int M = 1 << decltype(mc)::value;
+        const bool upper = (l & M) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = lane_xor<M>(v[e]);
+            v[e] = upper ? (p - v[e]) : (v[e] + p);
+        }
+    });
+}
+
+__device__ __forceinline__ float row16_total(float x) {
+    x += lane_xor<1>(x);
+    x += lane_xor<2>(x);
+    x += lane_xor<4>(x);
+    x += lane_xor<8>(x);
+    return x;
+}
+
+template <Src SRC>
+__global__ __launch_bounds__(kWriteThreads) void quantize_tq3k_mfma_kernel(WriteArgs a, DevCodebook cb, int nbatches) {
+    static_assert(SRC != Src::kRotated, "fp16 sources");
+    constexpr int D = 128, LPV = 16, VPP = kWriteThreads / LPV, NB = kTq3kBatch;
+    constexpr float kInvSqrtD = 0.08838834764831845f, kRScale = 1024.0f;
+    __shared__ __align__(16) _Float16 rhi[NB][kTq3kRow];
+    __shared__ __align__(16) _Float16 rlo[NB][kTq3kRow];
+    __shared__ __align__(16) uint8_t sgn_sh[NB][kTq3kSgnRow];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid % LPV, slot = tid / LPV;  // phase 1: lane in the vector, vector in the pass
+    const int li = lane & 15, lg = lane >> 4;   // phase 2: MFMA row / column, k group
+    const uint32_t sgn = sign_byte(cb, l);
+
+    // rows 32 wv + 16 rt + li of S, columns 32 c + 8 lg .. + 7, as fp16 part and remainder
+    half8_t shi[2][4], slo[2][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float4* src = reinterpret_cast<const float4*>(a.S + (32 * wv + 16 * rt + li) * D + 32 * c + 8 * lg);
+            const float4 p0 = src[0], p1 = src[1];
+            const float f[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                shi[rt][c][e] = static_cast<_Float16>(f[e]);
+                slo[rt][c][e] = static_cast<_Float16>(f[e] - static_cast<float>(shi[rt][c][e]));
+            }
+        }
+
+    for (int batch = blockIdx.x; batch < nbatches; batch += gridDim.x) {
+        // ---- 1. codes, headers and residuals of the batch's 64 vectors, 16 per pass
+        VecTarget<TQ_FMT_TQ3K, D, SRC> tg[NB / VPP];
+        RowPiece in[NB / VPP];
+#pragma unroll
+        for (int p = 0; p < NB / VPP; ++p) {
+            tg[p] = vec_target<TQ_FMT_TQ3K, D, SRC>(a, batch * NB + p * VPP + slot);
+            in[p] = load_piece<D, SRC>(a, tg[p].src_row, l);
+        }
+#pragma unroll
+        for (int p = 0; p < NB / VPP; ++p) {
+            float v[8];
+            const uint32_t w[4] = {in[p].x.x, in[p].x.y, in[p].x.z, in[p].x.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            float ss = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
+            const float n = sqrtf(row16_total(ss));
+            const uint32_t n16 = float_to_half_bits(fminf(n, kFp16Max));
+            const float inv = n > 0.0f ? __fdiv_rn(1.0f, n) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * (((sgn >> e) & 1u) ? -1.0f : 1.0f);
+            wht8_row16(v, l);
+            uint32_t low = 0;
+            float r[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                v[e] *= kInvSqrtD;
+                const uint32_t code = code_of<4>(v[e], cb);
+                low |= code << (2 * e);
+                r[e] = v[e] - cb.centroids[code];  // residual in the rotated basis, rotated back below
+            }
+            wht8_row16(r, l);
+            float g2 = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                r[e] = r[e] * kInvSqrtD * (((sgn >> e) & 1u) ? -1.0f : 1.0f);
+                g2 += r[e] * r[e];
+            }
+            const uint32_t g16 = float_to_half_bits(fminf(sqrtf(row16_total(g2)), kFp16Max));
+            if (tg[p].active) {
+                uint8_t* dst = a.out + tg[p].off;
+                if (l == 0) *reinterpret_cast<uint32_t*>(dst) = n16 | (g16 << 16);
+                *reinterpret_cast<uint16_t*>(dst + 4 + 2 * l) = static_cast<uint16_t>(low);
+            }
+            half8_t h, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = r[e] * kRScale;
+                h[e] = static_cast<_Float16>(x);
+                lo[e] = static_cast<_Float16>(x - static_cast<float>(h[e]));
+            }
+            *reinterpret_cast<half8_t*>(&rhi[p * VPP + slot][8 * l]) = h;
+            *reinterpret_cast<half8_t*>(&rlo[p * VPP + slot][8 * l]) = lo;
+        }
+        __syncthreads();
+
+        // ---- 2. signs of S R: wavefront wv, rows 32 wv + 16 rt + 4 lg + i, vectors 16 ct + li
+#pragma unroll
+        for (int ct = 0; ct < NB / 16; ++ct) {
+            f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const half8_t bh = *reinterpret_cast<const half8_t*>(&rhi[16 * ct + li][32 * c + 8 * lg]);
+                const half8_t bl = *reinterpret_cast<const half8_t*>(&rlo[16 * ct + li][32 * c + 8 * lg]);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi[rt][c], bh, acc[rt], 0, 0, 0);
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(shi[rt][c], bl, acc[rt], 0, 0, 0);
+                    acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(slo[rt][c], bh, acc[rt], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                uint32_t word = 0;  // byte i: row 4 lg + i of the tile, its bit of the sketch byte set when >= 0
+#pragma unroll
+                for (int i = 0; i < 4; ++i) word |= (acc[rt][i] >= 0.0f ? 1u : 0u) << (((4 * lg + i) & 7) + 8 * i);
+                *reinterpret_cast<uint32_t*>(&sgn_sh[16 * ct + li][32 * wv + 16 * rt + 4 * lg]) = word;
+            }
+        }
+        __syncthreads();
+
+        // ---- 3. sketch bytes: thread t, vector t / 4, bytes 4 (t % 4) .. + 3 (rows 32 (t % 4) ..)
+        {
+            const int v = tid >> 2, q = tid & 3;
+            const uint32_t* sp = reinterpret_cast<const uint32_t*>(&sgn_sh[v][32 * q]);
+            uint32_t out = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t x = sp[2 * j] | sp[2 * j + 1];
+                x |= x >> 16;
+                x |= x >> 8;
+                out |= (x & 0xFFu) << (8 * j);
+            }
+            const VecTarget<TQ_FMT_TQ3K, D, SRC> t = vec_target<TQ_FMT_TQ3K, D, SRC>(a, batch * NB + v);
+            if (t.active) *reinterpret_cast<uint32_t*>(a.out + t.off + 4 + D / 4 + 4 * q) = out;
+        }
+        __syncthreads();  // the batch's LDS is read before the next batch writes it
+    }
+}
+
 // Workgroups of kWriteThreads threads of `kernel` that the current device holds at once
 // (resident on every CU), found once per device and kernel.
 template <typename K>
 int resident_workgroups(K kernel) {
+    struct Entry {
+        const void* fn;
+        int dev, count;
+    };
     static std::mutex mu;
-    static int cached[64] = {};
+    static std::vector<Entry> cache;
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1 << 20;
+    if (hipGetDevice(&dev) != hipSuccess) return 1 << 20;
+    const void* fn = reinterpret_cast<const void*>(kernel);
     std::lock_guard<std::mutex> lock(mu);
-    if (cached[dev] == 0) {
-        int per_cu = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWriteThreads, 0) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 ||
-            cus < 1)
-            return 1 << 20;  // unknown: one workgroup per block
-        cached[dev] = per_cu * cus;
-    }
-    return cached[dev];
+    for (const Entry& e : cache)
+        if (e.fn == fn && e.dev == dev) return e.count;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWriteThreads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu < 1 || cus < 1)
+        return 1 << 20;  // unknown: one workgroup per block
+    cache.push_back({fn, dev, per_cu * cus});
+    return per_cu * cus;
 }
 
 // Whether the 64-cell code table of quantize_pq4_d256_kernel serves a codebook: finite
@@ -804,6 +992,14 @@ int launch_quantize(const WriteArgs& a, const tq_codebook& cb, hipStream_t st) {
         WriteArgs none = a;
         none.nvec = 0;
         return launch_pq4<D, SRC>(a, none, cb, cb, st);
+    }
+    if constexpr (FMT == TQ_FMT_TQ3K && D == 128 && SRC != Src::kRotated) {
+        const int nbatches = (a.nvec + kTq3kBatch - 1) / kTq3kBatch;
+        if (nbatches == 0) return TQ_OK;
+        const int grid = std::min(nbatches, resident_workgroups(quantize_tq3k_mfma_kernel<SRC>));
+        hipLaunchKernelGGL((quantize_tq3k_mfma_kernel<SRC>), dim3(grid), dim3(kWriteThreads), 0, st, a, to_dev(cb),
+                           nbatches);
+        return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_HIP;
     }
     constexpr int VPG = kWriteThreads / (D / 8) * kWriteUnroll;  // vectors per workgroup
     const int grid = (a.nvec + VPG - 1) / VPG;
