@@ -387,7 +387,10 @@ def bench_hybrid(args):
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     ws = torch.empty(tq.decode_hybrid_workspace_bytes(L, args.split_tokens), dtype=torch.uint8, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(total)]
-    n_probe = min(args.warmup, 50)
+    # the breakdown comes from every 8th timed step (events between the calls), as in the
+    # headline line: no warm-up or first-launch step enters it
+    probe = [s for s in range(args.warmup, total) if (s - args.warmup) % 8 == 0]
+    probe_set = set(probe)
 
     def step(s, marks):
         e = ev[s]
@@ -409,16 +412,15 @@ def bench_hybrid(args):
             e[4].record()
 
     for s in range(args.warmup):
-        step(s, s >= args.warmup - n_probe)
+        step(s, False)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.warmup, total):
-        step(s, False)
+        step(s, s in probe_set)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
     ms_step = t_total / args.steps * 1e3
     attended = float(np.mean([sched[s][3] + sched[s][4] for s in range(args.warmup, total)]))
-    probe = range(args.warmup - n_probe, args.warmup)
 
     def mean_ms(i, j, steps):
         return float(np.mean([ev[s][i].elapsed_time(ev[s][j]) for s in steps])) if len(steps) else None
@@ -445,7 +447,7 @@ def bench_hybrid(args):
         "step_breakdown_ms": {"ring_append": mean_ms(0, 1, probe), "rotate_query": mean_ms(2, 3, probe),
                               "decode_attention_hybrid": mean_ms(3, 4, probe),
                               "ring_flush_when_it_runs": mean_ms(1, 2, flush_steps)},
-        "step_breakdown_note": f"the last {n_probe} warm-up steps, with events between the calls",
+        "step_breakdown_note": f"{len(probe)} sampled timed steps (every 8th), events between the calls",
         "roofline": None,
         "cpu_baseline": None,
     }
@@ -462,7 +464,8 @@ SWEEP_NOTE = ("per-kernel times of a workload other than the headline one, on a 
 
 
 def bench_sweep(args):
-    """The write path at its bulk size (c5 prefill: 131,072 tokens x 4 KV heads at d 256) and the
+    """The write path at its bulk sizes (c5 prefill: 131,072 tokens x 4 KV heads at d 256; c3
+    prefill: 30,000 tokens x 8 KV heads, TQ3K keys and GQ2V values) and the
     decode of every other workload at full size -- c1, c2, c3, c5, c3's shapes with GQ4V values,
     c2's and c4's shapes with PQ3 keys (and PQ4 or PQ3 values) -- each timed alone on a cold cache,
     plus sparse V against the plain decode at c3 and c5; one JSON line per item."""
@@ -550,6 +553,27 @@ def bench_sweep(args):
          roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                    "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
     del k_rows, v_rows
+    torch.cuda.synchronize()
+
+    # ---- write path: c3 prefill (TQ3K keys with their QJL sketch, GQ2V values) in one call
+    w3 = synth.C3
+    L3 = tq.Layout(1, w3.n_q_heads, w3.n_kv_heads, w3.head_dim, w3.capacity, w3.k_format, w3.v_format)
+    cbk3, cbv3, S3 = codebooks(w3)
+    kb3, vb3 = tq.cache_bytes(L3)
+    kc3 = torch.empty(kb3, dtype=torch.uint8, device=dev)
+    vc3 = torch.empty(vb3, dtype=torch.uint8, device=dev)
+    k3 = torch.from_numpy(synth.batch_rows(w3, synth.K_TENSOR, 0, 0, w3.prefill)).to(dev)
+    v3 = torch.from_numpy(synth.batch_rows(w3, synth.V_TENSOR, 0, 0, w3.prefill)).to(dev)
+    dst3 = torch.arange(w3.prefill, dtype=torch.int32, device=dev)
+    ms = cold_ms(lambda ev: tq.quantize_append(L3, cbk3, cbv3, S3, k3, v3, dst3, kc3, vc3), 10, False)
+    nbytes = 2 * w3.prefill * w3.n_kv_heads * w3.head_dim * 2 + w3.prefill * w3.n_kv_heads * (
+        tq.vector_bytes(w3.k_format, w3.head_dim) + tq.vector_bytes(w3.v_format, w3.head_dim))
+    emit("c3 prefill (write path: TQ3K keys with the QJL sketch, GQ2V values)",
+         kernel="quantize_tq3k_mfma_kernel + quantize_kernel<GQ2V>",
+         workload=f"{w3.prefill} tokens x {w3.n_kv_heads} KV heads, d {w3.head_dim}", us=ms * 1e3, bytes=nbytes,
+         roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                   "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS})
+    del k3, v3, kc3, vc3
     torch.cuda.synchronize()
 
     # ---- decode of the other workloads (c5 reads the prefill bytes as [32][2][8192])
