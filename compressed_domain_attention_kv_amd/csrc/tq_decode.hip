@@ -1113,6 +1113,21 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 }
 
 // ---------------------------------------------------------------------------
+// o, marked as changed at this point: an address built from it is formed here instead of
+// being hoisted out of a loop into a register of its own.
+__device__ __forceinline__ uint32_t refresh(uint32_t o) {
+    asm volatile("" : "+v"(o));
+    return o;
+}
+
+// This lane's index in its wavefront, computed where it is used (a volatile asm, so the
+// value is not hoisted and held in a register across a loop).
+__device__ __forceinline__ int lane_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Byte-pair centroid table of the PQ4 sparse-matrix decode.  A lookup decodes
 // a whole code byte: entry b of a 256-entry table holds the bf16 (hi, lo)
 // pairs of both nibbles, (P[b & 15], P[b >> 4]), 8 bytes read by one
@@ -1185,7 +1200,10 @@ template <int G>
 struct SpCfg {
     static constexpr int D = 128, VB = 68, TT = 32, NTB = TT / 16;
     static constexpr int RB = G / 4;                   // 16-row blocks of (head, r, p)
-    static constexpr int WA = NTB * G * 2 * 16;         // weight words per wavefront: [tb][head][r][k-group]
+    // token blocks whose weights are in LDS at once: at G = 8 one (the LDS holds the value
+    // stages next to the table only so)
+    static constexpr int WTB = G == 8 ? 1 : NTB;
+    static constexpr int WA = WTB * G * 2 * 16;         // weight words per wavefront: [tb][head][r][k-group]
     static constexpr int RED = kPairWaves * G * (2 + D);
 };
 
@@ -1226,6 +1244,23 @@ __device__ __forceinline__ void stage_bytes(__amdgpu_buffer_rsrc_t r, uint8_t* s
     for (int k = 0; k < R; ++k)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * KB + 256 * k), 4, 4 * lane,
                                                  tile_off + 1024 * KB + 256 * k, 0, kStreamPolicy);
+}
+
+// A value tile of whole kilobytes and 128 bytes into exactly that much LDS, 16 bytes per
+// lane: the kilobytes with all lanes, the last 128 bytes with lanes 0..7 (one offset
+// register serves every load).
+template <int BYTES>
+__device__ __forceinline__ void stage_tight(__amdgpu_buffer_rsrc_t r, uint8_t* stage, int tile_off, int lane) {
+    static_assert(BYTES % 1024 == 128, "whole kilobytes and 128 bytes");
+    using lds_ptr = __attribute__((address_space(3))) void*;
+    constexpr int KB = BYTES / 1024;
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * k), 16, 16 * lane, tile_off + 1024 * k, 0,
+                                                 kStreamPolicy);
+    if (lane < 8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)(stage + 1024 * KB), 16, 16 * lane, tile_off + 1024 * KB, 0,
+                                                 kStreamPolicy);
 }
 
 // ---------------------------------------------------------------------------
@@ -1317,20 +1352,26 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     constexpr int D = C::D, NTB = C::NTB, RB = C::RB, TT = C::TT;
     constexpr bool K3 = KF == TQ_FMT_PQ3, V3 = VF == TQ_FMT_PQ3, PQ4PAIR = !K3 && !V3;
     constexpr int VBK = K3 ? 56 : 68, VBV = V3 ? 56 : 68;  // bytes per token of keys and values
-    // values through LDS where the two stages fit next to the table (G = 4, one table); PQ3
-    // values instead come through registers (two tile buffers) and an LDS index tile
-    constexpr bool VLDS = G == 4 && !VTAB;
+    // values through LDS where the two stages fit next to the table (one table; at G = 8 with
+    // stages of exactly a tile and the weights of one token block at a time); PQ3 values
+    // instead come through registers (two tile buffers) and an LDS index tile
+    constexpr bool VLDS = !VTAB;
     static_assert(!V3 || (VLDS && K3), "PQ3 values with PQ3 keys and one table");
     static_assert(PQ4PAIR || G == 4, "PQ3 at four query heads per KV head");
     constexpr bool STAGED = VLDS && !V3;  // value stages filled by buffer-to-LDS loads
-    constexpr int STAGE = StageShape<TT * (V3 ? 68 : VBV)>::SIZE;  // (no stages with PQ3 values)
+    constexpr bool TIGHT = G == 8;        // stages of exactly TT * VBV bytes
+    constexpr int STAGE = TIGHT ? TT * VBV : StageShape<TT * (V3 ? 68 : VBV)>::SIZE;  // (no stages with PQ3 values)
+    constexpr int WTB = C::WTB;
+    // G = 8: score products token block by token block (see the tile's scores), and a few lane
+    // offsets formed in the tile instead of held across the tile loop
+    constexpr bool TBMAJ = RB == 2;
     __shared__ __align__(16) SmemSp<G, VTAB, KF, VF> sm;
     // two stages in distinct LDS objects: the compiler's wait for one stage's loads then
     // ignores the other stage's
     __shared__ __align__(16) uint8_t vst0[STAGED ? kPairWaves : 1][STAGED ? STAGE : 16];
     __shared__ __align__(16) uint8_t vst1[STAGED ? kPairWaves : 1][STAGED ? STAGE : 16];
-    // the rotated query heads of the group, when the kernel rotates the query itself
-    __shared__ __align__(16) float qrot_sh[G][D];
+    // the rotated query heads of the group, when the kernel rotates the query itself (G = 4)
+    __shared__ __align__(16) float qrot_sh[G == 4 ? G : 1][G == 4 ? D : 4];
     // key and value boundaries of the encoder, when the kernel appends the step's token
     __shared__ __align__(16) float app_sb[2][4][4];
     __shared__ uint32_t tail_flag;  // this workgroup finished its stream last
@@ -1403,7 +1444,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     // four heads each, with the arithmetic of the query rotation kernel (16 lanes per head,
     // 8 coordinates per lane: signs, Walsh-Hadamard butterflies, 1/sqrt(d)), so the rotated
     // values are the same bits.  The query and its sign word are read here, before the tiles.
-    const bool raw = VLDS && PQ4PAIR && a.q_raw != nullptr;  // uniform
+    const bool raw = G == 4 && VLDS && PQ4PAIR && a.q_raw != nullptr;  // uniform
     const int rh = 4 * wi + (lane >> 4), rl = lane & 15;
     float rv[8];
     uint32_t rsign = 0;
@@ -1422,7 +1463,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     // when the position lies in one, else before the barrier that precedes every other tile.
     bool app = false, app_first = false;
     int apos = 0;
-    if (VLDS && PQ4PAIR && a.new_pos != nullptr) {
+    if (G == 4 && VLDS && PQ4PAIR && a.new_pos != nullptr) {
         apos = a.new_pos[b];
         if (apos >= 0 && apos < a.capacity) {
             const int sp = min(apos / a.split_len, a.splits - 1);
@@ -1492,6 +1533,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         const __amdgpu_buffer_rsrc_t kr0 = any ? krs : krs_none, vr0 = any ? vrs : vrs_none;
         keys_in(kt[0], kr0, t0 * VBK);
         if constexpr (V3) p3_load(vraw[0], vr0, t0 * VBV);
+        else if constexpr (TIGHT) stage_tight<TT * VBV>(vr0, vst0[wi], t0 * VBV, lane);
         else if constexpr (VLDS) stage_tile<TT * VBV>(vr0, vst0[wi], t0 * VBV, lane);
         else load_values<VBV>(vt, vr0, v_norm, v_word, t0 * VBV);
     }
@@ -1573,6 +1615,18 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
     const uint32_t vi_wr = lds_offset(n * 20 + 4 * g), vi_rd = lds_offset(4 * g * 20 + n);
     constexpr int kStep = kWaves * TT;
     constexpr int LA = kSpLookahead, R = LA + 1;
+    const uint8_t* vcur = nullptr;  // the value stage of the tile in progress
+    // lane parts of this lane's value norm and words in a stage (G = 8: marked as changed in
+    // every tile, so that each stage's address is formed there and not held per stage)
+    const uint32_t vn_lane = lds_offset(n * VBV), vw_lane = lds_offset(4 * g * VBV + 4 + 4 * n);
+    uint32_t vw_here = vw_lane;
+    // code words n of tokens 16 tb + 4g .. +3 of the tile in progress, from its stage
+    auto read_vwords = [&](int tb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            vt.w[tb][0][u] = TBMAJ ? *reinterpret_cast<const uint32_t*>(vcur + vw_here + (16 * tb + u) * VBV)
+                                   : *reinterpret_cast<const uint32_t*>(vcur + (16 * tb + 4 * g + u) * VBV + 4 + 4 * n);
+    };
 
     // One tile of TT tokens at t0.  With values through LDS the tiles alternate between
     // two key register sets and two value stages (P = tile parity): the next tile's keys
@@ -1585,9 +1639,10 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         const bool more = t0 + kStep < end;
         const int t_next = more ? t0 + kStep : t0;
         const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
-        const uint8_t* vcur = P == 0 ? vst0[wi] : vst1[wi];
+        vcur = P == 0 ? vst0[wi] : vst1[wi];
         if constexpr (VLDS) {
             if constexpr (V3) p3_load(vraw[1 - P], vrn, t_next * VBV);
+            else if constexpr (TIGHT) stage_tight<TT * VBV>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VBV, lane);
             else stage_tile<TT * VBV>(vrn, P == 0 ? vst1[wi] : vst0[wi], t_next * VBV, lane);
             keys_in(kt[1 - P], krn, t_next * VBK);
         }
@@ -1595,8 +1650,10 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         // ---- scores: job J = I * NTB + tb reads bytes 0..3 of key word I of block tb
         // PQ4: the four products of a token block accumulate in dsc.  PQ3: one product per
         // block of 32 coordinates, each from zero into a ring slot and folded into sacc with its
-        // block's norm after the next job's lookups (so no fold waits on a product in flight)
-        constexpr int NI = K3 ? 4 : 1;
+        // block's norm after the next job's lookups (so no fold waits on a product in flight).
+        // G = 8 (two row blocks, no query operand in registers): job J = tb * 4 + I, and a token
+        // block's scores are folded into sacc once the next block's first product is issued,
+        // which keeps one block's accumulators live instead of all
         f32x4 dsc[NTB][RB], dring[K3 ? 3 : 1][RB];
         float sacc[NTB][RB];
 #pragma unroll
@@ -1641,10 +1698,19 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                     sacc[TB][rb] = fmaf(nrm, (d4[0] + d4[1]) + (d4[2] + d4[3]), sacc[TB][rb]);
                 }
             };
+            // fold token block TB of a G = 8 tile: its key norm times its row-summed columns
+            auto fold_tb = [&](auto tc) __attribute__((always_inline)) {
+                constexpr int TB = decltype(tc)::value;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const f32x4 d4 = dsc[TB][rb];
+                    sacc[TB][rb] = nk[TB] * ((d4[0] + d4[1]) + (d4[2] + d4[3]));
+                }
+            };
             static_for<NJ + LA + (K3 ? 1 : 0)>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 if constexpr (J < NJ) {
-                    constexpr int I = J / NTB, TB = J % NTB;
+                    constexpr int I = TBMAJ ? J % 4 : J / NTB, TB = TBMAJ ? J / 4 : J % NTB;
                     const uint32_t x = kw[TB][I];
                     put_byte1<0>(addr[0], x);
                     put_byte1<1>(addr[1], x);
@@ -1659,7 +1725,10 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 }
                 if constexpr (K3 && J >= LA + 2) fold(std::integral_constant<int, J - LA - 2>{});
                 if constexpr (J >= LA && J < NJ + LA) {
-                    constexpr int M = J - LA, I = M / NTB, TB = M % NTB;
+                    constexpr int M = J - LA, I = TBMAJ ? M % 4 : M / NTB, TB = TBMAJ ? M / 4 : M % NTB;
+                    // the previous token block's accumulators are folded before this block's
+                    // first product, so the two sets never live at once
+                    if constexpr (TBMAJ && I == 0 && TB > 0) fold_tb(std::integral_constant<int, TB - 1>{});
                     const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb) {
@@ -1675,6 +1744,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 __builtin_amdgcn_sched_barrier(0);
             });
             if constexpr (K3) fold(std::integral_constant<int, NJ - 1>{});  // (NJ - 2 folded in the last job)
+            if constexpr (TBMAJ) fold_tb(std::integral_constant<int, NTB - 1>{});
         }
         if constexpr (!VLDS) keys_in(kt[0], krn, t_next * VBK);
         // PQ3 value norms of token 16 tb + n, blocks 0..3 (fp16, token blocks in the two halves)
@@ -1701,39 +1771,44 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) vt.w[tb][0][u] = vi[vi_rd + (16 * tb + u) * 20];
-        } else if constexpr (VLDS) {  // this tile's value words and norms, from its stage
+        } else if constexpr (VLDS) {  // this tile's value norms and words, from its stage
+            const uint32_t vn_here = TBMAJ ? refresh(vn_lane) : 0u;
+            if constexpr (TBMAJ) vw_here = refresh(vw_lane);
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) {
-                vt.norm[tb][0] = *reinterpret_cast<const uint16_t*>(vcur + (16 * tb + n) * VBV);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-                    vt.w[tb][0][u] = *reinterpret_cast<const uint32_t*>(vcur + (16 * tb + 4 * g + u) * VBV + 4 + 4 * n);
+                vt.norm[tb][0] = TBMAJ ? *reinterpret_cast<const uint16_t*>(vcur + vn_here + 16 * tb * VBV)
+                                       : *reinterpret_cast<const uint16_t*>(vcur + (16 * tb + n) * VBV);
+                if constexpr (WTB == NTB) read_vwords(tb);  // (else in the value pass of the block)
             }
         }
 
         // ---- online softmax: lane (n, g) owns head 4 rb + g, token 16 tb + n
+        // (at G = 8 n is recomputed here rather than held across the tile loop)
+        const int nt = TBMAJ ? (lane_here() & 15) : n;
         float tv[NTB][RB];
         float mx[RB];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) mx[rb] = -INFINITY;
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
-            const bool ok = 16 * tb + n < nv;
+            const bool ok = 16 * tb + nt < nv;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const f32x4 d4 = dsc[tb][rb];
-                const float sc = K3 ? sacc[tb][rb] : nk[tb] * ((d4[0] + d4[1]) + (d4[2] + d4[3]));
+                const float sc = K3 || TBMAJ ? sacc[tb][rb] : nk[tb] * ((d4[0] + d4[1]) + (d4[2] + d4[3]));
                 tv[tb][rb] = ok ? sc : -INFINITY;
                 mx[rb] = fmaxf(mx[rb], tv[tb][rb]);
             }
         }
         if (a.scores) {
+            // (at G = 8 the lane index is recomputed here rather than held for this path)
+            const int sl = TBMAJ ? lane_here() : lane, sn = sl & 15, sg4 = sl >> 4;
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     if (tv[tb][rb] != -INFINITY)
-                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 4 * rb + g) * a.capacity + t0 + 16 * tb + n] =
+                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 4 * rb + sg4) * a.capacity + t0 + 16 * tb + sn] =
                             tv[tb][rb] * kLn2;
         }
         bool grow = false;
@@ -1755,7 +1830,7 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
             // rows past the sequence end hold whatever the cache held: weight exactly 0
-            const float nvn = 16 * tb + n < nv ? (V3 ? 1.0f : half_bits_to_float(vt.norm[tb][0])) : 0.0f;
+            const float nvn = 16 * tb + nt < nv ? (V3 ? 1.0f : half_bits_to_float(vt.norm[tb][0])) : 0.0f;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 const float p = __builtin_amdgcn_exp2f(tv[tb][rb] - m_run[rb]);
@@ -1768,48 +1843,54 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
         // kernels that load values into registers keep one path (the branch costs them
         // registers)
         if (!VLDS || __builtin_amdgcn_ballot_w64(keep) != 0) {
+            // passes of WTB token blocks: their weights to LDS, then their value products (a
+            // pass rewrites the weight words only after the previous pass has read them)
+            static_for<NTB / WTB>([&](auto pc2) {
+                constexpr int TB0 = decltype(pc2)::value * WTB;
+                if constexpr (TB0 > 0) lds_order();
+                if constexpr (STAGED && WTB < NTB) read_vwords(TB0);
 #pragma unroll
-            for (int tb = 0; tb < NTB; ++tb) {
+                for (int sl = 0; sl < WTB; ++sl) {
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
+                    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-                    for (int i = 0; i < (V3 ? 4 : 1); ++i) {  // PQ3: the weight times the norm of block i
-                        const float wt =
-                            V3 ? wts[tb][rb] * half_bits_to_float((vnorm[i] >> (16 * tb)) & 0xFFFFu) : wts[tb][rb];
-                        const uint32_t bits = __float_as_uint(wt);
-                        const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
-                        uint32_t* dst = wa + w_lane + (i * C::WA + (tb * G + 4 * rb) * 32);
-                        dst[0] = dup_hi16(bits);
-                        dst[16] = dup_hi16(__float_as_uint(lo));
+                        for (int i = 0; i < (V3 ? 4 : 1); ++i) {  // PQ3: the weight times the norm of block i
+                            const int tb = TB0 + sl;
+                            const float wt = V3 ? wts[tb][rb] * half_bits_to_float((vnorm[i] >> (16 * tb)) & 0xFFFFu)
+                                                : wts[tb][rb];
+                            const uint32_t bits = __float_as_uint(wt);
+                            const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
+                            uint32_t* dst = wa + w_lane + (i * C::WA + (sl * G + 4 * rb) * 32);
+                            dst[0] = dup_hi16(bits);
+                            dst[16] = dup_hi16(__float_as_uint(lo));
+                        }
                     }
                 }
-            }
-            lds_order();
+                lds_order();
 
-            // ---- values: job J = tb * 4 + Q reads byte Q of code word n of tokens 4g .. 4g+3
-            {
-                // A operands: PQ4 one per token block, read here; PQ3 one per (token block, block
-                // of 32), read with the lookups of their job into a ring
-                u32x4 av[V3 ? R : NTB][RB];
-                auto read_a = [&](u32x4 (&dst)[RB], int i, int tb) __attribute__((always_inline)) {
+                // ---- values: job J = sl * 4 + Q reads byte Q of code word n of tokens
+                // 16 (TB0 + sl) + 4g .. +3
+                // A operands: PQ4 one per token block, read here; PQ3 one per (token block,
+                // block of 32), read with the lookups of their job into a ring
+                u32x4 av[V3 ? R : WTB][RB];
+                auto read_a = [&](u32x4 (&dst)[RB], int i, int sl) __attribute__((always_inline)) {
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
-                        dst[rb] = *reinterpret_cast<const u32x4*>(
-                            wa + rd_lane + (i * C::WA + (tb * G + 4 * rb) * 32));
+                        dst[rb] = *reinterpret_cast<const u32x4*>(wa + rd_lane + (i * C::WA + (sl * G + 4 * rb) * 32));
                 };
                 if constexpr (!V3) {
 #pragma unroll
-                    for (int tb = 0; tb < NTB; ++tb) read_a(av[tb], 0, tb);
+                    for (int sl = 0; sl < WTB; ++sl) read_a(av[sl], 0, sl);
                 }
-                constexpr int NJ = 4 * NTB;
+                constexpr int NJ = 4 * WTB;
                 u32x8 ring[R];
                 static_for<NJ + LA>([&](auto jc) {
                     constexpr int J = decltype(jc)::value;
                     if constexpr (J < NJ) {
-                        constexpr int TB = J / 4, Q = J % 4;
-                        if constexpr (V3) read_a(av[J % R], Q, TB);
+                        constexpr int SL = J / 4, Q = J % 4;
+                        if constexpr (V3) read_a(av[J % R], Q, SL);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB][0][u]);
+                        for (int u = 0; u < 4; ++u) put_byte1<Q>(addr[u], vt.w[TB0 + SL][0][u]);
 #pragma unroll
                         for (int u = 0; u < 4; ++u) {
                             const uint2 v = *reinterpret_cast<const uint2*>(vtab + addr[u]);
@@ -1818,16 +1899,16 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                         }
                     }
                     if constexpr (J >= LA) {
-                        constexpr int M = J - LA, TB = M / 4, Q = M % 4;
+                        constexpr int M = J - LA, SL = M / 4, Q = M % 4;
                         const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
 #pragma unroll
                         for (int rb = 0; rb < RB; ++rb)
                             acc[rb][Q] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
-                                __builtin_bit_cast(bf16x8, av[V3 ? M % R : TB][rb]), bop, acc[rb][Q], sp_idx, 0, 0);
+                                __builtin_bit_cast(bf16x8, av[V3 ? M % R : SL][rb]), bop, acc[rb][Q], sp_idx, 0, 0);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
-            }
+            });
             lds_order();
         }
         if constexpr (!VLDS) load_values<VBV>(vt, vrn, v_norm, v_word, t_next * VBV);
