@@ -45,7 +45,34 @@ struct WriteArgs {
     const int32_t* first;
     int ring_cap;
     int count;
+    // floor(2^32 / d) (2^32 - 1 for d = 1) of the divisors hkv, capacity, count, ring_cap
+    uint32_t hkv_m, cap_m, count_m, ring_m;
 };
+
+// The reciprocals of a write's divisors (host side, once per call).
+uint32_t div_magic(int d) {
+    return d <= 1 ? 0xFFFFFFFFu : static_cast<uint32_t>((uint64_t{1} << 32) / static_cast<uint64_t>(d));
+}
+void set_divisors(WriteArgs& a) {
+    a.hkv_m = div_magic(a.hkv);
+    a.cap_m = div_magic(a.capacity);
+    a.count_m = div_magic(a.count);
+    a.ring_m = div_magic(a.ring_cap);
+}
+
+// q = n / d and r = n % d for 0 <= n < 2^31 and d >= 1, given m = floor(2^32 / d) (2^32 - 1
+// for d = 1): mulhi(n, m) is floor(n / d) or one less (n m / 2^32 lies within n / 2^32 < 1 below
+// n / d), and one remainder test settles which.
+__device__ __forceinline__ void divmod(int n, int d, uint32_t m, int& q, int& r) {
+    uint32_t qq = __umulhi(static_cast<uint32_t>(n), m);
+    uint32_t rr = static_cast<uint32_t>(n) - qq * static_cast<uint32_t>(d);
+    if (rr >= static_cast<uint32_t>(d)) {
+        ++qq;
+        rr -= static_cast<uint32_t>(d);
+    }
+    q = static_cast<int>(qq);
+    r = static_cast<int>(rr);
+}
 
 // Index of the first fp32 boundary not below y, i.e. #{k : bounds[k] < y}.
 template <int NLEV>
@@ -121,23 +148,28 @@ __device__ __forceinline__ VecTarget<FMT, D, SRC> vec_target(const WriteArgs& a,
     constexpr int VB = vec_bytes_c<FMT, D>();
     VecTarget<FMT, D, SRC> t{vec < a.nvec, 0, 0};
     if constexpr (SRC == Src::kRing) {
-        const int tk = vec / a.hkv, h = vec % a.hkv;
-        const int bb = (t.active ? tk : 0) / a.count, i = tk % a.count;
+        int tk, h, bb, i;
+        divmod(t.active ? vec : 0, a.hkv, a.hkv_m, tk, h);
+        divmod(tk, a.count, a.count_m, bb, i);
         const int f = a.first[bb];
         const int pos = f + i;
         if (!t.active || f < 0 || pos >= a.capacity) t.active = false;
         else t.off = ((static_cast<size_t>(bb) * a.hkv + h) * a.capacity + pos) * VB;
-        t.src_row = t.active ? (static_cast<size_t>(bb) * a.hkv + h) * a.ring_cap + pos % a.ring_cap : 0;
+        int wrap, slot;
+        divmod(t.active ? pos : 0, a.ring_cap, a.ring_m, wrap, slot);
+        t.src_row = t.active ? (static_cast<size_t>(bb) * a.hkv + h) * a.ring_cap + slot : 0;
     } else {
         t.src_row = t.active ? static_cast<size_t>(vec) : 0;
         if (t.active) {
             if (a.dst_row) {
-                const int tk = vec / a.hkv, h = vec % a.hkv;
+                int tk, h;
+                divmod(vec, a.hkv, a.hkv_m, tk, h);
                 const int r = a.dst_row[tk];
                 if (r < 0 || r >= a.batch * a.capacity) {
                     t.active = false;
                 } else {
-                    const int b = r / a.capacity, pos = r % a.capacity;
+                    int b, pos;
+                    divmod(r, a.capacity, a.cap_m, b, pos);
                     t.off = ((static_cast<size_t>(b) * a.hkv + h) * a.capacity + pos) * VB;
                 }
             } else {
@@ -146,6 +178,15 @@ __device__ __forceinline__ VecTarget<FMT, D, SRC> vec_target(const WriteArgs& a,
         }
     }
     return t;
+}
+
+// The source row of vector `vec`, without its destination: any row of the write for a vector
+// that stores nothing (fp16 rows: the vector itself, so the row loads need not wait for the
+// destination rows; ring: as vec_target finds it).
+template <int FMT, int D, Src SRC>
+__device__ __forceinline__ size_t src_row_of(const WriteArgs& a, int vec) {
+    if constexpr (SRC == Src::kRing) return vec_target<FMT, D, SRC>(a, vec).src_row;
+    else return vec < a.nvec ? static_cast<size_t>(vec) : 0;
 }
 
 // The 8 coordinates 8l .. 8l+7 of one source row, as loaded (not yet converted).
@@ -210,16 +251,15 @@ __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook
         const uint32_t z16 = float_to_half_bits(mn);  // exact: mn is an fp16 value
         const uint32_t s16 = float_to_half_bits(__fdiv_rn(mx - mn, static_cast<float>(QMAX)));
         const float z = half_bits_to_float(z16), s = half_bits_to_float(s16);
-        const float inv = s > 0.0f ? __fdiv_rn(1.0f, s) : 0.0f;
+        // no branches: with inv = 0 (scale 0, or NaN) every code is 0 (fmaxf(NaN, 0) = 0), as it
+        // is by definition for a zero scale
+        const float inv_s = __fdiv_rn(1.0f, s);
+        const float inv = s > 0.0f ? inv_s : 0.0f;
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            uint32_t q = 0;
-            if (s > 0.0f) {
-                const float t = rintf((v[e] - z) * inv);
-                q = static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), static_cast<float>(QMAX)));
-            }
-            packed |= q << (QB * e);
+            const float t = rintf((v[e] - z) * inv);
+            packed |= static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), static_cast<float>(QMAX))) << (QB * e);
         }
         if (active) {
             const int grp = l >> 2, lg = l & 3;
@@ -336,7 +376,7 @@ __device__ __forceinline__ void quantize_rows(const WriteArgs& a, const DevCodeb
     for (int u = 0; u < U; ++u) tg[u] = vec_target<FMT, D, SRC>(a, (block * U + u) * VPB + slot);
     RowPiece in[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) in[u] = load_piece<D, SRC>(a, tg[u].src_row, l);
+    for (int u = 0; u < U; ++u) in[u] = load_piece<D, SRC>(a, src_row_of<FMT, D, SRC>(a, (block * U + u) * VPB + slot), l);
 #pragma unroll
     for (int u = 0; u < U; ++u) encode_vec<FMT, D, SRC>(a, cb, tg[u], in[u], sgn, l, slot, r_sh, qjl_sh);
 }
@@ -399,7 +439,8 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_pq4_kernel(WriteArgs a
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int c = 0; c < NPC; ++c)
-            raw[u][c] = *reinterpret_cast<const uint4*>(a.x + tg[u].src_row * D + CPL * l + 8 * c);
+            raw[u][c] = *reinterpret_cast<const uint4*>(
+                a.x + src_row_of<TQ_FMT_PQ4, D, SRC>(a, (block * U + u) * VPP + slot) * D + CPL * l + 8 * c);
 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -531,7 +572,8 @@ __global__ __launch_bounds__(kWriteThreads) __attribute__((amdgpu_waves_per_eu(4
     const int vbase = ((block * NW + wv) * kD256Chunks + chunk) * kD256Rows;
     const VecTarget<TQ_FMT_PQ4, D, SRC> mine = vec_target<TQ_FMT_PQ4, D, SRC>(a, vbase + lane);
     const uint64_t active_rows = __builtin_amdgcn_ballot_w64(mine.active);
-    const uint32_t src_lo = static_cast<uint32_t>(mine.src_row), src_hi = static_cast<uint32_t>(mine.src_row >> 32);
+    const size_t src_mine = src_row_of<TQ_FMT_PQ4, D, SRC>(a, vbase + lane);
+    const uint32_t src_lo = static_cast<uint32_t>(src_mine), src_hi = static_cast<uint32_t>(src_mine >> 32);
     const uint32_t off_lo = static_cast<uint32_t>(mine.off), off_hi = static_cast<uint32_t>(mine.off >> 32);
     auto src_of = [&](int r) __attribute__((always_inline)) {
         return static_cast<size_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(src_lo, r))) |
@@ -731,145 +773,236 @@ __global__ __launch_bounds__(kWriteThreads) void rotate_query_kernel(const float
 }
 
 // ---------------------------------------------------------------------------
-// TQ3K keys at d = 128 with the QJL sketch on the matrix cores ([P2] write path: 2-bit
-// MSE codes of the rotated unit vector, then the sign bits of S r for the residual r
-// rotated back, with its norm gamma).  A workgroup takes batches of 64 vectors:
-//   1. sixteen lanes per vector, 8 coordinates each, compute the norm, the rotation, the
-//      codes, the residual and gamma with the same arithmetic as the generic kernel, the
-//      lane moves of the transforms and sums done by DPP; the residual, scaled by 2^10
-//      (a power of two: the signs do not change, and its small entries stay normal fp16
-//      numbers), goes to LDS as an fp16 part and the fp16 rounding of the remainder;
-//   2. S R for the 64 residuals on the fp16 matrix cores, wavefront w taking rows
-//      32w .. 32w+31 of S, held in registers as fp16 parts and remainders; the products
-//      hi*hi + hi*lo + lo*hi keep about 22 significant bits (the signs flip only where
-//      |(S r)_i| is within about 1e-6 of |S_i| |r|); each row's sign goes to LDS as a byte
-//      already shifted to its bit of the output byte;
-//   3. each thread ORs 8 of those bytes into one sketch byte, four per output dword.
+// TQ3K keys at d = 128 on the matrix cores ([P2] write path: 2-bit MSE codes of the rotated
+// unit vector, then the sign bits of S r for the residual r rotated back, with its norm
+// gamma).  A workgroup takes batches of 64 vectors, each wavefront two vectors at a time:
+//   1. Rotation.  H_128 = H_8 (x) H_16 for coordinate c = 16 a + b.  The 16 x 16 fp16 matrix
+//      M of two vectors (row 8 v + a, column b; the rotation signs applied to the fp16 sign
+//      bits) is loaded with 8 bytes per lane; one product gives P = M H_16 (exact inputs,
+//      fp32 sums), which is scaled by 1 / (n sqrt(d)) per vector and split into an fp16 part
+//      and the fp16 rounding of its remainder (22 significant bits); a second product, with
+//      P in the operand position of its transpose, gives Y^T = P^T diag(H_8, H_8), so lane
+//      (j, g) ends up with coordinates 16 (j & 7) + 4 g .. + 3 of vector j >> 3.
+//   2. Codes by the three boundaries, the residual r' = y - c in the rotated basis and
+//      gamma = |r'| (the rotation is orthogonal: |r| = |r'|); the codes, the [n16 | gamma16]
+//      header and r' (scaled by 2^10, a power of two: the signs do not change, and its small
+//      entries stay normal fp16 numbers, as an fp16 part and remainder) go to LDS.
+//   3. Sketch.  S r = S Pi^T r' = S' r' with S' = S diag(s) H / sqrt(d), formed once per
+//      workgroup from S and held in registers as fp16 parts and remainders (wavefront w: rows
+//      32 w .. 32 w + 31), so r is never rotated back; S' R' for the batch on the fp16 matrix
+//      cores, hi*hi + hi*lo + lo*hi (a sign flips only where |(S r)_i| is within about 1e-6 of
+//      |S_i| |r|); each row's sign goes to LDS as a byte already shifted to its bit of the
+//      output byte.
+//   4. Four threads per vector OR 8 of those bytes into each sketch byte and write the block.
 constexpr int kTq3kBatch = 64;   // vectors per batch
 constexpr int kTq3kRow = 136;    // halves per residual row in LDS (16 B of padding: distinct banks)
 constexpr int kTq3kSgnRow = 132; // bytes per sign row in LDS
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
-// v <- H v for 8 coordinates per lane over the 16 lanes of a DPP row (coordinate 8 l + e)
-__device__ __forceinline__ void wht8_row16(float (&v)[8], int l) {
-#pragma unroll
-    for (int st = 1; st < 8; st <<= 1)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if ((e & st) == 0) {
-                const float x = v[e], y = v[e + st];
-                v[e] = x + y;
-                v[e + st] = x - y;
-            }
-    static_for<4>([&](auto mc) {
-        constexpr int M = 1 << decltype(mc)::value;
-        const bool upper = (l & M) != 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = lane_xor<M>(v[e]);
-            v[e] = upper ? (p - v[e]) : (v[e] + p);
-        }
-    });
+// x as a materialized fp32 value.  An fp16 part and remainder of a product must both be
+// taken from its fp32 rounding: left to itself the compiler forms the part by a fused
+// multiply-convert of the exact product (one rounding) and the remainder against the other,
+// and the two disagree by an fp16 ulp whenever the two roundings differ.
+__device__ __forceinline__ float rounded(float x) {
+    asm("" : "+v"(x));
+    return x;
 }
 
-__device__ __forceinline__ float row16_total(float x) {
+// Sum over the 32 lanes of one vector of a pair: lanes 8 v .. 8 v + 7 of every row of 16
+// lanes (v = 0, 1); the eight inside a row by DPP moves, the four rows by two lane swaps.
+__device__ __forceinline__ float pair_vector_sum(float x) {
     x += lane_xor<1>(x);
     x += lane_xor<2>(x);
     x += lane_xor<4>(x);
-    x += lane_xor<8>(x);
-    return x;
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    const float y = __uint_as_float(h[0]) + __uint_as_float(h[1]);  // rows 0 + 2 and 1 + 3, in both halves
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 template <Src SRC>
 __global__ __launch_bounds__(kWriteThreads) void quantize_tq3k_mfma_kernel(WriteArgs a, DevCodebook cb, int nbatches) {
     static_assert(SRC != Src::kRotated, "fp16 sources");
-    constexpr int D = 128, LPV = 16, VPP = kWriteThreads / LPV, NB = kTq3kBatch;
+    constexpr int D = 128, NB = kTq3kBatch, NW = kWriteThreads / 64, PPW = NB / NW / 2;  // vector pairs per wavefront
+    constexpr int U = 4;                                                                  // pairs in flight
     constexpr float kInvSqrtD = 0.08838834764831845f, kRScale = 1024.0f;
+    // the rotated coordinates are formed as 2^8 y (exact power-of-two scaling), so that the
+    // fp16 remainders of the second product stay normal numbers; boundaries and centroids
+    // are scaled alike
+    constexpr float kYs = 256.0f;
     __shared__ __align__(16) _Float16 rhi[NB][kTq3kRow];
     __shared__ __align__(16) _Float16 rlo[NB][kTq3kRow];
     __shared__ __align__(16) uint8_t sgn_sh[NB][kTq3kSgnRow];
+    __shared__ __align__(16) uint32_t blk_sh[NB][9];  // per vector: n16 | gamma16 << 16, then the 8 code dwords
     const int tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int l = tid % LPV, slot = tid / LPV;  // phase 1: lane in the vector, vector in the pass
-    const int li = lane & 15, lg = lane >> 4;   // phase 2: MFMA row / column, k group
-    const uint32_t sgn = sign_byte(cb, l);
+    const int li = lane & 15, lg = lane >> 4;  // MFMA row / column, k group
 
-    // rows 32 wv + 16 rt + li of S, columns 32 c + 8 lg .. + 7, as fp16 part and remainder
+    // ---- S' = S diag(s) H / sqrt(d): rows 32 wv + 16 rt + li, columns 32 c + 8 lg + e, as
+    // fp16 part and remainder.  The column's bits e (0-2) and c (5-6) are in registers, lg
+    // (3-4) across the lane groups.
     half8_t shi[2][4], slo[2][4];
+    {
+        uint32_t sb[4];  // bit e: the sign of column 32 c + 8 lg + e
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+        for (int c = 0; c < 4; ++c) sb[c] = cb.sign_bits[c] >> (8 * lg);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const float4* src = reinterpret_cast<const float4*>(a.S + (32 * wv + 16 * rt + li) * D + 32 * c + 8 * lg);
-            const float4 p0 = src[0], p1 = src[1];
-            const float f[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+        for (int rt = 0; rt < 2; ++rt) {
+            float x[4][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                shi[rt][c][e] = static_cast<_Float16>(f[e]);
-                slo[rt][c][e] = static_cast<_Float16>(f[e] - static_cast<float>(shi[rt][c][e]));
+            for (int c = 0; c < 4; ++c) {
+                const float4* src = reinterpret_cast<const float4*>(a.S + (32 * wv + 16 * rt + li) * D + 32 * c + 8 * lg);
+                const float4 p0 = src[0], p1 = src[1];
+                const float f[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[c][e] = ((sb[c] >> e) & 1u) ? -f[e] : f[e];
             }
+#pragma unroll
+            for (int st = 1; st < 8; st <<= 1)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if ((e & st) == 0) {
+                            const float u = x[c][e], v = x[c][e + st];
+                            x[c][e] = u + v;
+                            x[c][e + st] = u - v;
+                        }
+#pragma unroll
+            for (int st = 1; st < 4; st <<= 1)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if ((c & st) == 0)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float u = x[c][e], v = x[c + st][e];
+                            x[c][e] = u + v;
+                            x[c + st][e] = u - v;
+                        }
+#pragma unroll
+            for (int m = 16; m < 64; m <<= 1)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float p = __shfl_xor(x[c][e], m);
+                        x[c][e] = (lane & m) ? p - x[c][e] : x[c][e] + p;
+                    }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float f = rounded(x[c][e] * kInvSqrtD);
+                    shi[rt][c][e] = static_cast<_Float16>(f);
+                    slo[rt][c][e] = static_cast<_Float16>(f - static_cast<float>(shi[rt][c][e]));
+                }
         }
+    }
+
+    // H16 (second operand of M H16: lane (j, g) holds H16[4g + t][j]) and diag(H8, H8)
+    // (second operand of P^T diag(H8, H8), rows 4g + t, column j)
+    half4_t h16, d8;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int r = 4 * lg + t;
+        h16[t] = static_cast<_Float16>((__builtin_popcount(r & li) & 1) ? -1.0f : 1.0f);
+        d8[t] = static_cast<_Float16>((r >> 3) != (li >> 3) ? 0.0f : (__builtin_popcount(r & li & 7) & 1) ? -1.0f : 1.0f);
+    }
+    // this lane's rotation signs (coordinates 16 (li & 7) + 4 lg .. + 3: word (li & 7) / 2, the
+    // word selected, not indexed, so the arguments stay out of scratch) as XOR masks of its
+    // two fp16 pairs
+    const int aa = li & 7;
+    uint32_t sw = cb.sign_bits[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+        if ((aa >> 1) == i) sw = cb.sign_bits[i];
+    const uint32_t s4 = (sw >> (16 * (aa & 1) + 4 * lg)) & 0xFu;
+    const uint32_t sm0 = ((s4 & 1u) << 15) | (((s4 >> 1) & 1u) << 31);
+    const uint32_t sm1 = (((s4 >> 2) & 1u) << 15) | (((s4 >> 3) & 1u) << 31);
+    const float m0 = cb.bounds[0] * kYs, m1 = cb.bounds[1] * kYs, m2 = cb.bounds[2] * kYs;
+    const float c0 = cb.centroids[0] * kYs, c1 = cb.centroids[1] * kYs, c2 = cb.centroids[2] * kYs,
+                c3 = cb.centroids[3] * kYs;
+
+    // the source rows of a batch, as this lane holds them: the wavefront's vectors 16 wv ..
+    // 16 wv + 15, pair pp = vectors 2 pp (lanes with li < 8) and 2 pp + 1.  A batch's rows are
+    // requested during the previous batch.
+    uint2 raw[PPW];
+    auto load_rows = [&](int batch) __attribute__((always_inline)) {
+#pragma unroll
+        for (int pp = 0; pp < PPW; ++pp) {
+            const size_t row = src_row_of<TQ_FMT_TQ3K, D, SRC>(a, batch * NB + 16 * wv + 2 * pp + (li >> 3));
+            raw[pp] = *reinterpret_cast<const uint2*>(a.x + row * D + 16 * aa + 4 * lg);
+        }
+    };
+    if (static_cast<int>(blockIdx.x) < nbatches) load_rows(blockIdx.x);
 
     for (int batch = blockIdx.x; batch < nbatches; batch += gridDim.x) {
-        // ---- 1. codes, headers and residuals of the batch's 64 vectors, 16 per pass
-        VecTarget<TQ_FMT_TQ3K, D, SRC> tg[NB / VPP];
-        RowPiece in[NB / VPP];
+        // where thread t's vector t / 4 goes (its destination row is read now, used at the end)
+        const VecTarget<TQ_FMT_TQ3K, D, SRC> t4 = vec_target<TQ_FMT_TQ3K, D, SRC>(a, batch * NB + (tid >> 2));
+        // ---- 1, 2. rotation, codes and residuals of the batch's vectors
 #pragma unroll
-        for (int p = 0; p < NB / VPP; ++p) {
-            tg[p] = vec_target<TQ_FMT_TQ3K, D, SRC>(a, batch * NB + p * VPP + slot);
-            in[p] = load_piece<D, SRC>(a, tg[p].src_row, l);
+        for (int q0 = 0; q0 < PPW; q0 += U) {
+            f32x4_t y[U];
+            uint32_t n16v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t x01 = raw[q0 + u].x ^ sm0, x23 = raw[q0 + u].y ^ sm1;
+                const half2_t h01 = __builtin_bit_cast(half2_t, x01), h23 = __builtin_bit_cast(half2_t, x23);
+                const float ss =
+                    pair_vector_sum(__builtin_amdgcn_fdot2(h23, h23, __builtin_amdgcn_fdot2(h01, h01, 0.0f, false), false));
+                // the hardware root and reciprocal (within an ulp of the rounded results: the
+                // norm's fp16 rounding moves only within 1e-7 of an fp16 midpoint, y by under
+                // 1e-7 relative)
+                const float n = __builtin_amdgcn_sqrtf(ss);
+                n16v[u] = float_to_half_bits(fminf(n, kFp16Max));  // of vector li >> 3
+                const float sc = (n > 0.0f ? __builtin_amdgcn_rcpf(n) : 0.0f) * (kInvSqrtD * kYs);
+                // rows 4 lg + r of M H16 belong to vector lg >> 1
+                const float sc0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sc), 0));
+                const float sc1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(sc), 8));
+                const float scl = lg < 2 ? sc0 : sc1;
+                const f32x4_t pr = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, make_uint2(x01, x23)),
+                                                                         h16, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                half4_t ph, pl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = rounded(pr[r] * scl);
+                    ph[r] = static_cast<_Float16>(v);
+                    pl[r] = static_cast<_Float16>(v - static_cast<float>(ph[r]));
+                }
+                y[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, d8, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                y[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, d8, y[u], 0, 0, 0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                // y[u][r]: 2^8 times coordinate 16 aa + 4 lg + r of vector li >> 3
+                uint32_t byte = 0;
+                float g2 = 0.0f;
+                half4_t rh, rl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v = y[u][r];
+                    const bool b0 = v > m0, b1 = v > m1, b2 = v > m2;  // code = #{k : m_k < y}
+                    byte |= (static_cast<uint32_t>(b0) + static_cast<uint32_t>(b1) + static_cast<uint32_t>(b2)) << (2 * r);
+                    const float res = v - (b1 ? (b2 ? c3 : c2) : (b0 ? c1 : c0));
+                    g2 = fmaf(res, res, g2);
+                    const float xs = res * (kRScale / kYs);
+                    rh[r] = static_cast<_Float16>(xs);
+                    rl[r] = static_cast<_Float16>(xs - static_cast<float>(rh[r]));
+                }
+                const uint32_t g16 =
+                    float_to_half_bits(fminf(__builtin_amdgcn_sqrtf(pair_vector_sum(g2)) * (1.0f / kYs), kFp16Max));
+                const int slot = 16 * wv + 2 * (q0 + u) + (li >> 3);  // the vector's place in the batch
+                reinterpret_cast<uint8_t*>(blk_sh[slot])[4 + 4 * aa + lg] = static_cast<uint8_t>(byte);
+                *reinterpret_cast<half4_t*>(&rhi[slot][16 * aa + 4 * lg]) = rh;
+                *reinterpret_cast<half4_t*>(&rlo[slot][16 * aa + 4 * lg]) = rl;
+                if (aa == 0 && lg == 0) blk_sh[slot][0] = n16v[u] | (g16 << 16);
+            }
         }
-#pragma unroll
-        for (int p = 0; p < NB / VPP; ++p) {
-            float v[8];
-            const uint32_t w[4] = {in[p].x.x, in[p].x.y, in[p].x.z, in[p].x.w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = half_bits_to_float((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-            float ss = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss += v[e] * v[e];
-            const float n = sqrtf(row16_total(ss));
-            const uint32_t n16 = float_to_half_bits(fminf(n, kFp16Max));
-            const float inv = n > 0.0f ? __fdiv_rn(1.0f, n) : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = v[e] * inv * (((sgn >> e) & 1u) ? -1.0f : 1.0f);
-            wht8_row16(v, l);
-            uint32_t low = 0;
-            float r[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                v[e] *= kInvSqrtD;
-                const uint32_t code = code_of<4>(v[e], cb);
-                low |= code << (2 * e);
-                r[e] = v[e] - cb.centroids[code];  // residual in the rotated basis, rotated back below
-            }
-            wht8_row16(r, l);
-            float g2 = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                r[e] = r[e] * kInvSqrtD * (((sgn >> e) & 1u) ? -1.0f : 1.0f);
-                g2 += r[e] * r[e];
-            }
-            const uint32_t g16 = float_to_half_bits(fminf(sqrtf(row16_total(g2)), kFp16Max));
-            if (tg[p].active) {
-                uint8_t* dst = a.out + tg[p].off;
-                if (l == 0) *reinterpret_cast<uint32_t*>(dst) = n16 | (g16 << 16);
-                *reinterpret_cast<uint16_t*>(dst + 4 + 2 * l) = static_cast<uint16_t>(low);
-            }
-            half8_t h, lo;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = r[e] * kRScale;
-                h[e] = static_cast<_Float16>(x);
-                lo[e] = static_cast<_Float16>(x - static_cast<float>(h[e]));
-            }
-            *reinterpret_cast<half8_t*>(&rhi[p * VPP + slot][8 * l]) = h;
-            *reinterpret_cast<half8_t*>(&rlo[p * VPP + slot][8 * l]) = lo;
-        }
+        if (batch + static_cast<int>(gridDim.x) < nbatches) load_rows(batch + gridDim.x);
         __syncthreads();
 
-        // ---- 2. signs of S R: wavefront wv, rows 32 wv + 16 rt + 4 lg + i, vectors 16 ct + li
+        // ---- 3. signs of S' R': wavefront wv, rows 32 wv + 16 rt + 4 lg + i, vectors 16 ct + li
 #pragma unroll
         for (int ct = 0; ct < NB / 16; ++ct) {
             f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
@@ -894,7 +1027,8 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_tq3k_mfma_kernel(Write
         }
         __syncthreads();
 
-        // ---- 3. sketch bytes: thread t, vector t / 4, bytes 4 (t % 4) .. + 3 (rows 32 (t % 4) ..)
+        // ---- 4. thread t, vector t / 4: sketch bytes 4 (t % 4) .. + 3 (rows 32 (t % 4) ..), code
+        // dwords 2 (t % 4) and 2 (t % 4) + 1, and the header
         {
             const int v = tid >> 2, q = tid & 3;
             const uint32_t* sp = reinterpret_cast<const uint32_t*>(&sgn_sh[v][32 * q]);
@@ -906,8 +1040,13 @@ __global__ __launch_bounds__(kWriteThreads) void quantize_tq3k_mfma_kernel(Write
                 x |= x >> 8;
                 out |= (x & 0xFFu) << (8 * j);
             }
-            const VecTarget<TQ_FMT_TQ3K, D, SRC> t = vec_target<TQ_FMT_TQ3K, D, SRC>(a, batch * NB + v);
-            if (t.active) *reinterpret_cast<uint32_t*>(a.out + t.off + 4 + D / 4 + 4 * q) = out;
+            if (t4.active) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(a.out + t4.off);  // blocks are 4-byte aligned
+                dst[1 + D / 16 + q] = out;
+                dst[1 + 2 * q] = blk_sh[v][1 + 2 * q];
+                dst[2 + 2 * q] = blk_sh[v][2 + 2 * q];
+                if (q == 0) dst[0] = blk_sh[v][0];
+            }
         }
         __syncthreads();  // the batch's LDS is read before the next batch writes it
     }
@@ -1092,6 +1231,7 @@ int tq_quantize_append(const tq_layout* L, const tq_codebook* cbk, const tq_code
     a.hkv = L->n_kv_heads;
     a.capacity = L->capacity;
     a.batch = L->batch;
+    set_divisors(a);
     WriteArgs av = a;
     a.x = k_new;
     a.out = static_cast<uint8_t*>(k_cache);
@@ -1148,6 +1288,7 @@ int tq_ring_flush(const tq_layout* L, const tq_codebook* cbk, const tq_codebook*
     a.first = first;
     a.ring_cap = ring_cap;
     a.count = count;
+    set_divisors(a);
     WriteArgs av = a;
     a.x = static_cast<const uint16_t*>(k_ring);
     a.out = static_cast<uint8_t*>(k_cache);
@@ -1179,6 +1320,7 @@ int tq_quantize_rotated(int format, const tq_codebook* cb, const float* S_dev, c
     a.hkv = 1;
     a.capacity = 1;
     a.batch = 1;
+    set_divisors(a);
     return dispatch_quantize<Src::kRotated>(format, d, a, *cb, stream);
 }
 
