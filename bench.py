@@ -582,7 +582,10 @@ def bench_sweep(args):
     c4_pq3 = synth.scaled(synth.C4, name="c4 shapes with PQ3 keys and values", k_format=synth.PQ3,
                           v_format=synth.PQ3, k_bits=3, v_bits=3, prefill=synth.C4.context)
     c4_asym = synth.scaled(c4_pq3, name="c4 shapes with PQ3 keys and PQ4 values", v_format=synth.PQ4, v_bits=4)
-    for w in (synth.C1, synth.C2, c2_asym, synth.C3, c3_gq4v, synth.C5, c4_pq3, c4_asym):
+    # eight query heads per KV head at d 128 (64 query / 8 KV heads, grouped-query models of that shape)
+    c4_g8 = synth.scaled(synth.C4, name="c4 shapes with 64 query heads (G = 8)", n_q_heads=64,
+                         prefill=synth.C4.context)
+    for w in (synth.C1, synth.C2, c2_asym, synth.C3, c3_gq4v, synth.C5, c4_pq3, c4_asym, c4_g8):
         B, Hq, Hkv, d, N = w.batch, w.n_q_heads, w.n_kv_heads, w.head_dim, w.context
         L = tq.Layout(B, Hq, Hkv, d, w.capacity, w.k_format, w.v_format)
         if w is synth.C5:
