@@ -330,6 +330,32 @@ def test_pq3_keys_ragged_lengths(pair):
         _say(f"pq3 keys {pair} split={split}: score err {es:.2e}, output err {eo:.2e}")
 
 
+@pytest.mark.parametrize("case", ["g4", "g8", "g4_two_tables"])
+def test_pq4_sparse_ragged_lengths(case):
+    """PQ4 on the 2:4-sparse kernel: four and eight query heads per KV head (values staged in
+    LDS a tile ahead; at eight heads in stages of exactly a tile, weights one token block at a
+    time) and four heads with the values' own centroid table (values through registers):
+    contexts of 0, 1, a token block, a tile, one past it, one split, one past a split and the
+    full capacity over garbage-filled caches, with the automatic and a 256-token split."""
+    G, vk = {"g4": (4, synth.QUANTILE_MEAN), "g8": (8, synth.QUANTILE_MEAN),
+             "g4_two_tables": (4, synth.LLOYD_MAX)}[case]
+    w = synth.scaled(synth.C4, v_kind=vk, batch=8, n_q_heads=2 * G, n_kv_heads=2, context=1024, capacity=1024)
+    st = P.Setup(w)
+    L = st.layout()
+    lens = [0, 1, 16, 33, 255, 257, 700, 1024]
+    kb, vbytes, kdq, vdq = _oracle_cache(st, w, lens)
+    kc = _garbage_cache(st, L, synth.K_TENSOR, kb)
+    vc = _garbage_cache(st, L, synth.V_TENSOR, vbytes)
+    q = synth.queries(w)
+    for split in (0, 256):
+        out, scores, _, _ = P.gpu_decode(st, L, q, kc, vc, lens, split_tokens=split)
+        es, eo = P.check_read(st, q, kdq, vdq, lens, out, scores, w.capacity)
+        assert np.all(out[0] == 0.0)
+        for b, n in enumerate(lens):  # scores are written only below the context length
+            assert np.all(np.isnan(scores[b, :, n:]))
+        _say(f"pq4 sparse {case} split={split}: score err {es:.2e}, output err {eo:.2e}")
+
+
 def test_timed_partial_matches_untimed():
     """tq_decode_partial_timed writes the same records as tq_decode_partial and
     its events span a positive kernel time."""
