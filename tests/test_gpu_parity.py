@@ -150,6 +150,47 @@ def test_append_skips_out_of_range_rows():
         assert (pos in written) == (not np.all(kh[:, pos] == 0xAB))
 
 
+@pytest.mark.parametrize("case", ["pq4_d128", "pq4_d256", "pq3", "tq3k_gq2v", "tq3k_gq4v_d256"])
+def test_append_odd_shapes_and_scattered_rows(case):
+    """Appends whose row arithmetic divides by no power of two (3 sequences, 3 KV heads, a
+    capacity of 960 = 15 x 64 tokens), of 300 tokens whose destinations are scattered in-range rows
+    mixed with -1 and rows past batch x capacity: every written row equals the oracle's
+    encoding of its source row (up to the tolerated boundary flips), every other row keeps its
+    fill."""
+    base = {"pq4_d128": synth.C4, "pq4_d256": synth.C5, "pq3": synth.C2, "tq3k_gq2v": synth.C3,
+            "tq3k_gq4v_d256": synth.scaled(synth.C3, v_format=synth.GQ4V, v_bits=4, head_dim=256)}[case]
+    w = synth.scaled(base, batch=3, n_q_heads=12, n_kv_heads=3, context=960, capacity=960)
+    st = P.Setup(w)
+    L = st.layout()
+    d, T, cap = w.head_dim, 300, 960
+    rng = np.random.default_rng(5)
+    rows = {t: (rng.standard_normal((T, 3, d)) * rng.uniform(0.05, 3.0, size=(T, 3, 1))).astype(np.float16)
+            for t in (synth.K_TENSOR, synth.V_TENSOR)}
+    dst = rng.permutation(3 * cap)[:T].astype(np.int32)
+    bad = rng.choice(T, size=40, replace=False)
+    dst[bad[:20]] = -1
+    dst[bad[20:]] = 3 * cap + rng.integers(0, 5000, size=20)
+    kb, vb = tq.cache_bytes(L)
+    kc = torch.full((kb,), 0xEE, dtype=torch.uint8, device="cuda")
+    vc = torch.full((vb,), 0xEE, dtype=torch.uint8, device="cuda")
+    tq.quantize_append(L, st.cbk, st.cbv, st.S_dev, torch.from_numpy(rows[synth.K_TENSOR]).cuda(),
+                       torch.from_numpy(rows[synth.V_TENSOR]).cuda(), torch.from_numpy(dst).cuda(), kc, vc)
+    torch.cuda.synchronize()
+    valid = np.nonzero((dst >= 0) & (dst < 3 * cap))[0]
+    flips = 0
+    for tensor, cache, vbytes in ((synth.K_TENSOR, kc, st.vbk), (synth.V_TENSOR, vc, st.vbv)):
+        host = cache.cpu().numpy().reshape(3, 3, cap, vbytes)
+        touched = np.zeros((3, 3, cap), dtype=bool)
+        for h in range(3):
+            got = host[dst[valid] // cap, h, dst[valid] % cap]
+            stats = P.compare_write(st, tensor, got, st.oracle_encode(tensor, rows[tensor][valid, h]))
+            flips += stats["code_flips"]
+            touched[dst[valid] // cap, h, dst[valid] % cap] = True
+        assert np.all(host[~touched] == 0xEE), "a row outside the valid destinations was written"
+    _say(f"append {case}: {len(valid)} of {T} tokens written, code flips {flips}")
+    assert flips <= max(2, 1e-4 * 2 * 3 * len(valid) * d)
+
+
 @pytest.mark.parametrize("name", ["c4", "c5", "c2"])
 def test_append_special_vectors(name):
     """Zero vectors (decode to exactly 0), norms above the fp16 range (saturate),

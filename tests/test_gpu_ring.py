@@ -26,6 +26,7 @@ WORKLOADS = {
     "c3": synth.scaled(synth.C3, batch=2, n_q_heads=10, n_kv_heads=2, context=400, capacity=448),
     "c5": synth.scaled(synth.C5, batch=2, n_q_heads=16, n_kv_heads=2, context=300, capacity=320),
     "c4_g8": synth.scaled(synth.C4, batch=2, n_q_heads=16, n_kv_heads=2, context=300, capacity=320),
+    "c3_h3": synth.scaled(synth.C3, batch=3, n_q_heads=12, n_kv_heads=3, context=600, capacity=640),
 }
 
 
@@ -74,7 +75,7 @@ def test_ring_append_places_rows_at_pos_mod_cap(cap):
     assert np.array_equal(vr.cpu().numpy().view(np.uint16).reshape(ref_v.shape), ref_v)
 
 
-@pytest.mark.parametrize("name", ["c4", "c2", "c3", "c5"])
+@pytest.mark.parametrize("name", ["c4", "c2", "c3", "c5", "c3_h3"])
 def test_ring_flush_writes_what_append_would(name):
     """Flushing count ring tokens (wrapping around the ring) writes the blocks the
     oracle encodes for those rows, at their absolute positions, and nothing else."""
