@@ -2008,22 +2008,27 @@ struct TqCfg {
     static constexpr int QB = VF == TQ_FMT_GQ2V ? 2 : 4;     // code bits
     static constexpr int WAVES = 8, TT = 32, NTB = TT / 16, NGRP = 4, COPIES = 8;
     static constexpr int STAGE = TT * VBV;                   // a multiple of 256
+    // a weight row holds TT tokens and 8 spare entries: rows 80 bytes apart put the eight
+    // lanes of an LDS phase of the A-operand reads on distinct banks
+    static constexpr int TTP = TT + 8;
 };
 
 template <int VF>
 struct SmemTq {
     using C = TqCfg<VF>;
     union {
-        struct {
-            u32x4 mse[256 * C::COPIES];  // entry (byte b, copy c) at b * COPIES + c
-            u32x4 qjl[256 * C::COPIES];
-        } tab;
+        // both tables in 256-byte rows: row b holds the MSE entry of byte b in its eight copies,
+        // then the QJL entry in its eight copies, so that a lookup address is one byte permute
+        // of the code word (b << 8 | table << 7 | copy << 4)
+        u32x4 tab[256 * 2 * C::COPIES];
         float red[C::WAVES * 8 * (2 + C::D)];  // per-wavefront (m, l, acc) after the tile loop
     } u;
-    alignas(16) uint16_t wa[C::WAVES][C::NGRP][16][C::TT];  // value A operands [group][row][token]
+    alignas(16) uint16_t wa[C::WAVES][C::NGRP][16][C::TTP];  // value A operands [group][row][token slot]
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 
 // Key bytes of a 16-token block for lane (n, g): token n's norms (n | gamma << 16),
 // code bytes 8g .. 8g+7 (coordinates 32g .. 32g+31) and sign byte group g (dword g of
@@ -2042,6 +2047,14 @@ __device__ __forceinline__ void load_tq_keys(TqKeys& k, __amdgpu_buffer_rsrc_t r
         k.codes[tb] = __builtin_amdgcn_raw_buffer_load_b64(r, o + 4 + 8 * g, tile_off, kStreamPolicy);
         k.signs[tb] = __builtin_amdgcn_raw_buffer_load_b32(r, o + 36 + 4 * g, tile_off, kStreamPolicy);
     }
+}
+
+// Workgroup barrier for LDS data written by the wavefronts themselves (ds writes), which
+// leaves buffer loads in flight: a __syncthreads() would also wait for every buffer-to-LDS
+// load still pending.  A stage filled by such loads is read only after the reading
+// wavefront's own wait for them.
+__device__ __forceinline__ void lds_write_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // bf16 (hi, lo) halves of x as (lo << 16) | hi, by the hardware round-to-nearest-even
@@ -2070,20 +2083,8 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
     const int n = lane & 15, g = lane >> 4;
     const int hq0 = h * G;
-    int N = a.seq_lens[b];
-    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
     const int start = s * a.split_len;
-    const int end = min(start + a.split_len, N);
     const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
-
-    if (start >= end) {
-        for (int gg = 0; gg < G; ++gg) {
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
-            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
-        }
-        return;
-    }
 
     // ---- the small global reads first: the query entries of the operands this thread builds.
     // Operand entry (job, lane l): jobs 0..7 are the MSE products I, whose lane (row i, group gg)
@@ -2116,16 +2117,28 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
     const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
     const int k_lane = n * VBK;
 
-    // the first tile of this wavefront (through the empty resource when it has none)
+    // the first tile of this wavefront, requested before the sequence length arrives: its
+    // bytes lie inside the stream's range (the resource returns zeros past it), and a tile
+    // at or past the end is read and not used
     constexpr int kStep = NW * TT;
     int t0 = start + w * TT;
     TqKeys kt[2];
-    {
-        const bool any = t0 < end;
-        load_tq_keys(kt[0], any ? krs : krs_none, k_lane, g, t0 * VBK);
-        stage_bytes<C::STAGE>(any ? vrs : vrs_none, vst0[w], t0 * VBV, lane);
-    }
+    stage_bytes<C::STAGE>(vrs, vst0[w], t0 * VBV, lane);  // values first: the wait for the keys covers them
+    load_tq_keys(kt[0], krs, k_lane, g, t0 * VBK);
     __builtin_amdgcn_sched_barrier(0);
+
+    int N = a.seq_lens[b];
+    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
+    const int end = min(start + a.split_len, N);
+    if (start >= end) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged tile lands before the LDS is released
+        for (int gg = 0; gg < G; ++gg) {
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
+            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
+        }
+        return;
+    }
 
     // ---- tables: thread t fills entries t + 512 k (entry e is byte e / COPIES, copy e % COPIES)
     {
@@ -2143,8 +2156,8 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
                 m[c] = b1 ? (b0 ? csp[3] : csp[2]) : (b0 ? csp[1] : csp[0]);
                 q[c] = (b0 ? 0x3F80u : 0xBF80u) | ((b1 ? 0x3F80u : 0xBF80u) << 16);
             }
-            sm.u.tab.mse[e] = m;
-            sm.u.tab.qjl[e] = q;
+            sm.u.tab[(2 * byte) * C::COPIES + (e % C::COPIES)] = m;
+            sm.u.tab[(2 * byte + 1) * C::COPIES + (e % C::COPIES)] = q;
         }
     }
     // ---- query operands into LDS (the weight area, free until the first tile): the query times
@@ -2180,13 +2193,13 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
             }
         }
     }
-    __syncthreads();
+    lds_write_barrier();  // the first tile stays in flight
     u32x4 qa[8], sa[4];
 #pragma unroll
     for (int I = 0; I < 8; ++I) qa[I] = opl[I * 64 + lane];
 #pragma unroll
     for (int I = 0; I < 4; ++I) sa[I] = opl[(8 + I) * 64 + lane];
-    __syncthreads();  // every wavefront holds its operands before any writes weights there
+    lds_write_barrier();  // every wavefront holds its operands before any writes weights there
 
     // per lane: heads 2g + e (rows 4g + 2e + r of every product); rows of heads >= G stay at
     // m = 0, p = 0
@@ -2202,9 +2215,9 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
 #pragma unroll
     for (int gr = 0; gr < 4; ++gr) acc[gr][0] = acc[gr][1] = wsum[gr] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const char* mtab = reinterpret_cast<const char*>(sm.u.tab.mse);
-    const char* stab = reinterpret_cast<const char*>(sm.u.tab.qjl);
-    const uint32_t copy_off = lds_offset((lane & 7) * 16u);
+    const char* tabs = reinterpret_cast<const char*>(sm.u.tab);
+    // byte 0 of a lookup address: this lane's copy (lane & 7), and the QJL half of the row
+    const uint32_t lc_m = (lane & 7) * 16u, lc_q = lc_m | 128u;
     const float slack = a.v_skip > 0.0f ? 0.0f : kRescaleSlack;
     // this lane's code dword of a group and the byte of it holding channels 2n, 2n + 1
     constexpr int QB = C::QB;
@@ -2212,10 +2225,39 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
     const uint32_t cbyte = QB == 2 ? (n & 7) >> 1 : (n & 3);
     const uint32_t csh = QB == 2 ? 4 * (n & 1) : 0;  // bit of channel 2n within that byte
     const uint32_t psel = cbyte | (0x0Cu << 8) | ((cbyte + 4u) << 16) | (0x0Cu << 24);
-    uint32_t cmask = QB == 2 ? 0x00030003u : 0x000F000Fu;
-    asm("" : "+v"(cmask));  // in a register, so that mask and or fuse into one instruction
+    // Channel 2n + hf of a token's byte pair, as bf16(128 + c q) with q its code: 2-bit codes
+    // after one shift by csh, hf = 0 masked in place (c = 1) and hf = 1 two bits up (c = 4, the
+    // product scaled back by 1/4 at the end); 4-bit codes the low nibble in place and the high
+    // nibble after a shift by 4 (c = 1).  Masks in registers: mask and or fuse into one
+    // instruction.
+    constexpr uint32_t csh1 = QB == 2 ? 0u : 4u;
+    constexpr float kHf1 = QB == 2 ? 0.25f : 1.0f;
+    uint32_t cmask0 = QB == 2 ? 0x00030003u : 0x000F000Fu, cmask1 = QB == 2 ? 0x000C000Cu : 0x000F000Fu;
+    asm("" : "+v"(cmask0), "+v"(cmask1));
     const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    constexpr int TTP = C::TTP;
     uint16_t* wa_w = &sm.wa[w][0][0][0];
+    uint32_t* wa_w32 = reinterpret_cast<uint32_t*>(wa_w);
+    // Token slots: token 8 q + j of a tile sits in slot 8 q + ((j - 2 q) & 7) of its weight rows,
+    // and the value product's lane group q takes its eight tokens in that order, so that the
+    // four lane groups read four different token rows of the stage at any step and the code
+    // reads of a step fall on distinct banks.  The rotation is even: a token pair (2i, 2i + 1)
+    // keeps two adjacent slots, one dword.
+    uint32_t wslot[2];  // dword of this lane's token pair in a weight row, per token block
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+        const int tp = 16 * tb + (n & ~1), q = tp >> 3;
+        wslot[tb] = static_cast<uint32_t>(4 * q + ((((tp & 7) - 2 * q) & 7) >> 1));
+    }
+    // dword of a group pair's even / odd group: the even lane (mine = its H, nb = the odd
+    // neighbour's H) takes (mine, nb) halves, the odd lane (mine = its L, nb = the even
+    // neighbour's L) takes (nb, mine)
+    const uint32_t wsel0 = (n & 1) ? 0x01000504u : 0x05040100u;
+    const uint32_t wsel1 = (n & 1) ? 0x03020706u : 0x07060302u;
+    const int t_first = start + w * TT;
+    uint32_t xoff[8];  // stage offset of the code dword of the u-th token of lane group g
+#pragma unroll
+    for (int u = 0; u < 8; ++u) xoff[u] = lds_offset((8 * g + ((u + 2 * g) & 7)) * VBV + cw_off);
 
     auto tile = [&](auto pc, const int t0) {
         constexpr int P = decltype(pc)::value;
@@ -2240,13 +2282,14 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
                 constexpr int J = decltype(jc)::value;
                 if constexpr (J < NJ) {
                     constexpr int I = J / 2, TB = J % 2;
+                    // address bytes: (lane constant, code byte k, 0, 0)
                     if constexpr (I < 8) {
                         const uint32_t word = I < 4 ? kc.codes[TB][0] : kc.codes[TB][1];
-                        const uint32_t by = __builtin_amdgcn_ubfe(word, 8 * (I % 4), 8);
-                        ring[J % R] = *reinterpret_cast<const u32x4*>(mtab + ((by << 7) | copy_off));
+                        const uint32_t ad = __builtin_amdgcn_perm(word, lc_m, 0x0C0C0400u + ((I % 4) << 8));
+                        ring[J % R] = *reinterpret_cast<const u32x4*>(tabs + ad);
                     } else {
-                        const uint32_t by = __builtin_amdgcn_ubfe(kc.signs[TB], 8 * (I - 8), 8);
-                        ring[J % R] = *reinterpret_cast<const u32x4*>(stab + ((by << 7) | copy_off));
+                        const uint32_t ad = __builtin_amdgcn_perm(kc.signs[TB], lc_q, 0x0C0C0400u + ((I - 8) << 8));
+                        ring[J % R] = *reinterpret_cast<const u32x4*>(tabs + ad);
                     }
                 }
                 if constexpr (J >= LA) {
@@ -2288,37 +2331,43 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
 #pragma unroll
         for (int e = 0; e < 2; ++e) mx[e] = fmaxf(tv[0][e], tv[1][e]);
         if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + slack || mx[1] > m_run[1] + slack) != 0) {
+            // before the wavefront's first tile every sum is zero: only the reference moves
+            const bool first = t0 == t_first;
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const float mn = fmaxf(m_run[e], row16_max(mx[e]));
-                const float alpha = mn == m_run[e] ? 1.0f : __builtin_amdgcn_exp2f(m_run[e] - mn);
-                l_run[e] *= alpha;
+                if (!first) {
+                    const float alpha = mn == m_run[e] ? 1.0f : __builtin_amdgcn_exp2f(m_run[e] - mn);
+                    l_run[e] *= alpha;
 #pragma unroll
-                for (int gr = 0; gr < 4; ++gr) {
-                    zacc[e][gr] *= alpha;
-                    wsum[gr][2 * e] *= alpha;
-                    wsum[gr][2 * e + 1] *= alpha;
+                    for (int gr = 0; gr < 4; ++gr) {
+                        zacc[e][gr] *= alpha;
+                        wsum[gr][2 * e] *= alpha;
+                        wsum[gr][2 * e + 1] *= alpha;
 #pragma unroll
-                    for (int hf = 0; hf < 2; ++hf) {
-                        acc[gr][hf][2 * e] *= alpha;
-                        acc[gr][hf][2 * e + 1] *= alpha;
+                        for (int hf = 0; hf < 2; ++hf) {
+                            acc[gr][hf][2 * e] *= alpha;
+                            acc[gr][hf][2 * e + 1] *= alpha;
+                        }
                     }
                 }
                 m_run[e] = mn;
             }
         }
-        // weights times each group's scale, as the A operands of the value products
+        // weights times each group's scale, as the A operands of the value products, split into
+        // bf16 halves two groups at a time: H = (hi of group 2k, hi of group 2k + 1), L the lo
+        // halves.  Lanes n and n ^ 1 hold a token pair: the even lane writes the pair's hi
+        // halves (row 4g + 2e), the odd lane the lo halves (row 4g + 2e + 1), one dword per group
         bool keep = false;
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb) {
             const int t = 16 * tb + n;
             const bool tok = t < nv;
-            float scl[4], zro[4];  // the token's group scales and zeros (0 past the end: never stale)
+            uint32_t hdr[4];  // the token's (scale, zero) per group as fp16 pairs (0 past the end: never stale)
 #pragma unroll
             for (int gr = 0; gr < 4; ++gr) {
-                const uint32_t hdr = *reinterpret_cast<const uint32_t*>(vcur + lds_offset(t * VBV) + GB * gr);
-                scl[gr] = tok ? half_bits_to_float(hdr & 0xFFFFu) : 0.0f;
-                zro[gr] = tok ? half_bits_to_float(hdr >> 16) : 0.0f;
+                const uint32_t x = *reinterpret_cast<const uint32_t*>(vcur + lds_offset(t * VBV) + GB * gr);
+                hdr[gr] = tok ? x : 0u;
             }
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
@@ -2326,13 +2375,24 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
                 l_run[e] += p;
                 const float pk = p >= a.v_skip ? p : 0.0f;
                 keep = keep || pk != 0.0f;
-                uint16_t* dst = wa_w + lds_offset((4 * g + 2 * e) * TT + t);
+                uint32_t* dst = wa_w32 + lds_offset((4 * g + 2 * e + (n & 1)) * (TTP / 2) + wslot[tb]);
 #pragma unroll
-                for (int gr = 0; gr < 4; ++gr) {
-                    zacc[e][gr] = fmaf(pk, zro[gr], zacc[e][gr]);
-                    const uint32_t sp = bf16_split_hw(pk * scl[gr]);
-                    dst[gr * 16 * TT] = static_cast<uint16_t>(sp);
-                    dst[gr * 16 * TT + TT] = static_cast<uint16_t>(sp >> 16);
+                for (int gp = 0; gp < 2; ++gp) {
+                    float wv[2];
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const int gr = 2 * gp + i;
+                        zacc[e][gr] = fmaf(pk, half_bits_to_float(hdr[gr] >> 16), zacc[e][gr]);
+                        wv[i] = pk * half_bits_to_float(hdr[gr] & 0xFFFFu);
+                    }
+                    const uint32_t H = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{wv[0], wv[1]}, bf16x2_t));
+                    const float r0 = wv[0] - __uint_as_float(H << 16), r1 = wv[1] - __uint_as_float(H & 0xFFFF0000u);
+                    const uint32_t Lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(float2_t{r0, r1}, bf16x2_t));
+                    const uint32_t mine = (n & 1) ? Lo : H, give = (n & 1) ? H : Lo;
+                    const uint32_t nb = static_cast<uint32_t>(
+                        __builtin_amdgcn_mov_dpp(static_cast<int>(give), kDppXor1, 0xF, 0xF, false));
+                    dst[(2 * gp) * 16 * (TTP / 2)] = __builtin_amdgcn_perm(nb, mine, wsel0);
+                    dst[(2 * gp + 1) * 16 * (TTP / 2)] = __builtin_amdgcn_perm(nb, mine, wsel1);
                 }
             }
         }
@@ -2344,11 +2404,10 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
         // B of ones sums the weight halves the value products used
 #pragma unroll
         for (int gr = 0; gr < 4; ++gr) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(wa_w + lds_offset((gr * 16 + n) * TT + 8 * g));
+            const u32x4 av = *reinterpret_cast<const u32x4*>(wa_w + lds_offset((gr * 16 + n) * TTP + 8 * g));
             uint32_t x[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                x[u] = *reinterpret_cast<const uint32_t*>(vcur + lds_offset((8 * g + u) * VBV + cw_off) + GB * gr);
+            for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const uint32_t*>(vcur + xoff[u] + GB * gr);
             uint32_t pr[4];
 #pragma unroll
             for (int v = 0; v < 4; ++v) pr[v] = __builtin_amdgcn_perm(x[2 * v + 1], x[2 * v], psel);
@@ -2356,7 +2415,9 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
             for (int hf = 0; hf < 2; ++hf) {
                 u32x4 bv;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) bv[v] = ((pr[v] >> (csh + hf * QB)) & cmask) | 0x43004300u;
+                for (int v = 0; v < 4; ++v)
+                    bv[v] = hf == 0 ? ((pr[v] >> csh) & cmask0) | 0x43004300u
+                                    : ((pr[v] >> (csh + csh1)) & cmask1) | 0x43004300u;
                 acc[gr][hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                                       __builtin_bit_cast(bf16x8, bv), acc[gr][hf], 0, 0, 0);
             }
@@ -2394,7 +2455,8 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
                 const float corr = 128.0f * (wsum[gr][2 * e] + wsum[gr][2 * e + 1]);
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
-                    r[2 + 32 * gr + 2 * n + hf] = ((acc[gr][hf][2 * e] + acc[gr][hf][2 * e + 1]) - corr) + zacc[e][gr];
+                    r[2 + 32 * gr + 2 * n + hf] =
+                        ((acc[gr][hf][2 * e] + acc[gr][hf][2 * e + 1]) - corr) * (hf ? kHf1 : 1.0f) + zacc[e][gr];
             }
         }
     }
