@@ -103,6 +103,37 @@ struct Smem {
     float pw[kWaves][kTile * G];        // probabilities of the current tile
 };
 
+// Merge of the per-wavefront partials of a workgroup, red[w][head][2 + D] = (m, l, acc[D]) in
+// log2 units, into one split record per head ([P2] trick 3: the running (m, l, acc) states
+// combine by rescaling to the common maximum).  Threads 0 .. G-1 take, per head, the maximum
+// M, the factors 2^(m_w - M) (0 for a wavefront without tokens) into fw[w][head] and the
+// record's (M, sum_w l_w f_w); after a barrier every coordinate is sum_w f_w acc_w, the sums
+// in wavefront order.
+template <int D, int G, int NWV>
+__device__ __forceinline__ void merge_factors(const float* red, float* fw, int t, float2* ml, int splits) {
+    if (t < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NWV; ++ww) M = fmaxf(M, red[(ww * G + t) * (2 + D)]);
+        float L = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NWV; ++ww) {
+            const float* r = red + (ww * G + t) * (2 + D);
+            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+            fw[ww * G + t] = f;
+            L = fmaf(r[1], f, L);
+        }
+        ml[static_cast<size_t>(t) * splits] = make_float2(M, L);
+    }
+}
+template <int D, int G, int NWV>
+__device__ __forceinline__ float merged_coordinate(const float* red, const float* fw, int gg, int j) {
+    float A = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) A = fmaf(red[(ww * G + gg) * (2 + D) + 2 + j], fw[ww * G + gg], A);
+    return A;
+}
+
 template <int KF, int VF, int D, int G>
 __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs a, DevCodebook cbk, DevCodebook cbv) {
     using SM = Smem<KF, VF, D, G>;
@@ -359,22 +390,13 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
         for (int k = 0; k < DPL; ++k) r[2 + lane * DPL + k] = acc[g][k];
     }
     __syncthreads();
+    __shared__ float fw[kWaves * G];
+    merge_factors<D, G, kWaves>(red, fw, tid, a.ml + rec0, a.splits);
+    __syncthreads();
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
         const int g = idx / D, j = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * G + g) * (2 + D)]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float* r = red + (ww * G + g) * (2 + D);
-            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-            L = fmaf(r[1], f, L);
-            A = fmaf(r[2 + j], f, A);
-        }
         const size_t rec = rec0 + static_cast<size_t>(g) * a.splits;
-        a.acc[rec * D + j] = A;
-        if (j == 0) a.ml[rec] = make_float2(M, L);
+        a.acc[rec * D + j] = merged_coordinate<D, G, kWaves>(red, fw, g, j);
     }
 }
 
@@ -430,6 +452,14 @@ __device__ __forceinline__ void decode_half(uint32_t xl, uint32_t xh, const char
 
 // Program-order point between phases that touch the same LDS bytes through
 // differently typed accesses (no instruction is emitted).
+// Workgroup barrier for LDS data written by the wavefronts themselves (ds writes), which
+// leaves buffer loads in flight: a __syncthreads() would also wait for every buffer-to-LDS
+// load still pending.  A stage filled by such loads is read only after the reading
+// wavefront's own wait for them.
+__device__ __forceinline__ void lds_write_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ void lds_order() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -792,20 +822,8 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
     const int n = lane & 15, g = lane >> 4;  // MFMA column / row (A side) and k-group
     const int hq0 = h * G;
-    int N = a.seq_lens[b];
-    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
     const int start = s * a.split_len;
-    const int end = min(start + a.split_len, N);
     const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
-
-    if (start >= end) {
-        for (int gg = 0; gg < G; ++gg) {
-            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
-            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
-        }
-        return;
-    }
 
     const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
     const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
@@ -816,17 +834,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     const int k_word = n * VB + 4 + 16 * g;      // key words 4g..4g+3 of token n
     uint32_t* wa = sm.u.op.wa[w];
 
-    // the first tile of this wavefront in flight before anything else (tiles lie inside the
-    // cache: t0 + TT <= capacity because TT divides 64); a wavefront without tiles requests it
-    // through the empty resource, so the loads stay on one path
+    // the first tile of this wavefront in flight before anything else, before the sequence
+    // length arrives (tiles lie inside the cache: t0 + TT <= capacity because TT divides 64; a
+    // tile at or past the end is read and not used), its values first: the wait for its keys
+    // covers them
     int t0 = start + w * TT;
     KeyTile<NTB, NB> kt[2];
     ValueTile<NTB, NB> vt;
-    {
-        const bool any = t0 < end;
-        load_keys<VB>(kt[0], any ? krs : krs_none, k_norm, k_word, t0 * VB);
-        stage_tile<TT * VB>(any ? vrs : vrs_none, vst0[w], t0 * VB, lane);
-    }
+    stage_tile<TT * VB>(vrs, vst0[w], t0 * VB, lane);
+    load_keys<VB>(kt[0], krs, k_norm, k_word, t0 * VB);
 
     if (tid < 32) {
         sm.klo[tid] = bf16_split(cbk.centroids[tid & 15]);
@@ -856,7 +872,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
             sm.u.op.qa[c][lane] = v;
         }
     }
-    __syncthreads();
+
+    int N = a.seq_lens[b];
+    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
+    const int end = min(start + a.split_len, N);
+    if (start >= end) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged tile lands before the LDS is released
+        for (int gg = 0; gg < G; ++gg) {
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
+            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
+        }
+        return;
+    }
+    lds_write_barrier();  // tables and query operands; the first tile stays in flight
 
     // per lane: heads 2g and 2g+1 (when < G); inactive rows keep m = 0, p = 0
     float m_run[2], l_run[2];
@@ -1093,22 +1122,13 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
         }
     }
     __syncthreads();
+    __shared__ float fw[kWaves * G];
+    merge_factors<D, G, kWaves>(red, fw, tid, a.ml + rec0, a.splits);
+    __syncthreads();
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
         const int gg = idx / D, j = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[(ww * G + gg) * (2 + D)]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) {
-            const float* r = red + (ww * G + gg) * (2 + D);
-            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-            L = fmaf(r[1], f, L);
-            A = fmaf(r[2 + j], f, A);
-        }
         const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-        a.acc[rec * D + j] = A;
-        if (j == 0) a.ml[rec] = make_float2(M, L);
+        a.acc[rec * D + j] = merged_coordinate<D, G, kWaves>(red, fw, gg, j);
     }
 }
 
@@ -2049,14 +2069,6 @@ __device__ __forceinline__ void load_tq_keys(TqKeys& k, __amdgpu_buffer_rsrc_t r
     }
 }
 
-// Workgroup barrier for LDS data written by the wavefronts themselves (ds writes), which
-// leaves buffer loads in flight: a __syncthreads() would also wait for every buffer-to-LDS
-// load still pending.  A stage filled by such loads is read only after the reading
-// wavefront's own wait for them.
-__device__ __forceinline__ void lds_write_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // bf16 (hi, lo) halves of x as (lo << 16) | hi, by the hardware round-to-nearest-even
 // conversion: hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ uint32_t bf16_split_hw(float x) {
@@ -2461,22 +2473,13 @@ __global__ __launch_bounds__(TqCfg<VF>::WAVES * 64) void decode_partial_tq3k_ker
         }
     }
     __syncthreads();
+    __shared__ float fw[NW * G];
+    merge_factors<D, G, NW>(red, fw, tid, a.ml + rec0, a.splits);
+    __syncthreads();
     for (int idx = tid; idx < G * D; idx += blockDim.x) {
         const int gg = idx / D, j = idx % D;
-        float M = -INFINITY;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, red[(ww * G + gg) * (2 + D)]);
-        float L = 0.0f, A = 0.0f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float* r = red + (ww * G + gg) * (2 + D);
-            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-            L = fmaf(r[1], f, L);
-            A = fmaf(r[2 + j], f, A);
-        }
         const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-        a.acc[rec * D + j] = A;
-        if (j == 0) a.ml[rec] = make_float2(M, L);
+        a.acc[rec * D + j] = merged_coordinate<D, G, NW>(red, fw, gg, j);
     }
 }
 
