@@ -1966,24 +1966,32 @@ __global__ __launch_bounds__(kPairWaves * 64) __attribute__((amdgpu_waves_per_eu
                 r[2 + (V3 ? 32 * Q + 2 * n : 8 * n + 2 * Q) + p] = acc[rb][Q][p] + acc[rb][Q][2 + p];
     }
     __syncthreads();
+    // per split group: the factors of its wavefronts once per (wavefront, head), then the
+    // coordinates (the arithmetic and order of merge_factors / merged_coordinate)
+    __shared__ float fw_sp[kPairSub][kWaves * G];
+    const float* red_sg = red + sg * kWaves * G * (2 + D);
+    const int tsg = tid % (kWaves * 64);
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+    if (s < a.splits && tsg < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red_sg[(ww * G + tsg) * (2 + D)]);
+        float L = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const float* r = red_sg + (ww * G + tsg) * (2 + D);
+            const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
+            fw_sp[sg][ww * G + tsg] = f;
+            L = fmaf(r[1], f, L);
+        }
+        store_dev(a.ml + rec0 + static_cast<size_t>(tsg) * a.splits, make_float2(M, L));  // device scope: another XCD may merge them
+    }
+    __syncthreads();
     if (s < a.splits) {
-        const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
-        for (int idx = tid % (kWaves * 64); idx < G * D; idx += kWaves * 64) {
+        for (int idx = tsg; idx < G * D; idx += kWaves * 64) {
             const int gg = idx / D, j = idx % D;
-            float M = -INFINITY;
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, red[((sg * kWaves + ww) * G + gg) * (2 + D)]);
-            float L = 0.0f, A = 0.0f;
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const float* r = red + ((sg * kWaves + ww) * G + gg) * (2 + D);
-                const float f = r[0] == -INFINITY ? 0.0f : exp2f(r[0] - M);
-                L = fmaf(r[1], f, L);
-                A = fmaf(r[2 + j], f, A);
-            }
             const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
-            store_dev(a.acc + rec * D + j, A);  // device scope: another XCD may merge them
-            if (j == 0) store_dev(a.ml + rec, make_float2(M, L));
+            store_dev(a.acc + rec * D + j, merged_coordinate<D, G, kWaves>(red_sg, fw_sp[sg], gg, j));
         }
     }
     // the merge reuses the table and reduction area (the barrier in stream_arrive orders it
