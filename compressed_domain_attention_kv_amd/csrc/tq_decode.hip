@@ -887,6 +887,15 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
     }
     lds_write_barrier();  // tables and query operands; the first tile stays in flight
 
+    // d 256 (two waves per SIMD, 256 registers each): the query operand in registers for the
+    // whole split (64 of them), not re-read from LDS per tile; d 128 (four waves per SIMD) reads
+    // each chunk from LDS a few products ahead of its use
+    constexpr bool QREG = D == 256;
+    u32x4 qall[QREG ? NB * 8 : 1];
+    if constexpr (QREG) {
+#pragma unroll
+        for (int S = 0; S < NB * 8; ++S) qall[S] = sm.u.op.qa[S][lane];
+    }
     // per lane: heads 2g and 2g+1 (when < G); inactive rows keep m = 0, p = 0
     float m_run[2], l_run[2];
 #pragma unroll
@@ -944,23 +953,23 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) nk[tb][blk] = half_bits_to_float(kc.norm[tb][blk]);
         {
-            // QB query chunks in flight: chunk S is loaded at job S*NTB and last
-            // read by the product of job S*NTB + NTB-1, kLookahead jobs later
+            // (d 128) QB query chunks in flight: chunk S is loaded at job S*NTB and last read by
+            // the product of job S*NTB + NTB-1, kLookahead jobs later
             constexpr int NS = NB * 8, NJ = NS * NTB, R = kLookahead + 1, QB = 1 + (kLookahead + NTB - 1) / NTB;
             uint32_t ring[R][4];
-            u32x4 qk[QB];
+            u32x4 qk[QREG ? 1 : QB];
             static_for<NJ + kLookahead>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 if constexpr (J < NJ) {
                     constexpr int S = J / NTB, TB = J % NTB, BLK = S / 8, CC = S % 8;
-                    if constexpr (TB == 0) qk[S % QB] = sm.u.op.qa[S][lane];
+                    if constexpr (!QREG && TB == 0) qk[S % QB] = sm.u.op.qa[S][lane];
                     const uint32_t x = kc.w[TB][BLK][CC >> 1];
                     decode_half<CC & 1>(x << 2, x >> 1, klo, khi, ring[J % R]);
                 }
                 if constexpr (J >= kLookahead) {
                     constexpr int M = J - kLookahead, S = M / NTB, TB = M % NTB, BLK = S / 8;
                     dsc[TB][BLK] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, qk[S % QB]),
+                        __builtin_bit_cast(bf16x8, QREG ? qall[QREG ? S : 0] : qk[S % QB]),
                         __builtin_bit_cast(bf16x8, u32x4{ring[M % R][0], ring[M % R][1], ring[M % R][2], ring[M % R][3]}),
                         dsc[TB][BLK], 0, 0, 0);
                 }
