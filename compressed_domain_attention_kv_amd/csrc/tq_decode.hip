@@ -1142,6 +1142,372 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 }
 
 // ---------------------------------------------------------------------------
+// PQ4 at d = 256 with one centroid table for keys and values, G = 4 or 8: the products of
+// decode_partial_bf16_kernel with the centroid pairs of a whole code byte per lookup.  A
+// 64 KB table maps a byte to (T[low nibble], T[high nibble]) as bf16 (hi, lo) pairs, in 32
+// copies (one per lane of a 32-lane phase of the 8-byte LDS reads), 256-byte rows, so that a
+// lookup address (byte << 8 | copy << 3) is one byte permute of the code word:
+//   * a score product takes the four coordinates of two code bytes: two lookups (the
+//     nibble tables take four);
+//   * a value lookup gives nibble positions 2c and 2c + 1 of a token's code word, the B
+//     operands of two products: four lookups per two products (eight with nibble tables).
+// Eight wavefronts per workgroup share the table, one split per workgroup; a wavefront walks
+// 32-token tiles as the bf16 kernel does, its query operand held in registers.  A token's
+// value weights serve both 128-coordinate blocks: each block of a d 256 vector holds the
+// full-vector norm ([P1] section 9, head_dim-specific blocks), so the weights are formed once
+// from block 0's norm.
+template <int G>
+struct D256Cfg {
+    static constexpr int D = 256, NB = 2, VB = 136, TT = 32, NTB = 2, NW = 8, ROWS = 2 * G;
+    static constexpr int WA = NTB * ROWS * 16 + (ROWS < 16 ? 16 : 0);  // weight words per wavefront (+ zero row)
+};
+
+template <int G>
+struct SmemD256 {
+    using C = D256Cfg<G>;
+    union {
+        uint2 tab[256 * 32];                // (byte b, copy c) at b * 32 + c
+        float red[C::NW * G * C::D];        // per-wavefront value sums after the tile loop
+    } u;
+    union {
+        alignas(16) uint32_t wa[C::NW][C::WA];  // value-product A operand [tb][row][token] (+ zero row)
+        alignas(16) u32x4 qa[16][64];           // score A operand per chunk and lane, until held in registers
+    } op;
+    float2 ml[C::NW][G];  // per-wavefront (m, l) after the tile loop
+    float fw[C::NW * G];  // merge factors
+};
+
+template <int G>
+__global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_partial_d256_kernel(
+    DecodeArgs a, DevCodebook cb) {
+    static_assert(G == 4 || G == 8, "two heads per 16-lane row group");
+    using C = D256Cfg<G>;
+    constexpr int D = C::D, VB = C::VB, NB = C::NB, NTB = C::NTB, TT = C::TT, NW = C::NW, ROWS = C::ROWS;
+    constexpr int STAGE = StageShape<TT * VB>::SIZE;
+    static_assert(sizeof(SmemD256<G>::u.red) <= sizeof(SmemD256<G>::u.tab), "the merge fits the table area");
+    __shared__ __align__(16) SmemD256<G> sm;
+    __shared__ __align__(16) uint8_t vst0[NW][STAGE];
+    __shared__ __align__(16) uint8_t vst1[NW][STAGE];
+
+    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile offsets stay in SGPRs
+    const int n = lane & 15, g = lane >> 4;  // MFMA column / row (A side) and k-group
+    const int hq0 = h * G;
+    const int start = s * a.split_len;
+    const size_t rec0 = (static_cast<size_t>(b) * a.hq + hq0) * a.splits + s;
+
+    const size_t stream_row = (static_cast<size_t>(b) * a.hkv + h) * a.capacity;
+    const uint32_t stream_bytes = static_cast<uint32_t>(a.capacity) * VB;
+    const __amdgpu_buffer_rsrc_t krs = stream_rsrc(a.k_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = stream_rsrc(a.v_cache + stream_row * VB, stream_bytes);
+    const __amdgpu_buffer_rsrc_t krs_none = null_rsrc(a.k_cache), vrs_none = null_rsrc(a.v_cache);
+    const int k_norm = n * VB;               // key norm of token n
+    const int k_word = n * VB + 4 + 16 * g;  // key words 4g..4g+3 of token n
+
+    // the first tile before anything else, before the sequence length arrives (a tile past the
+    // stream's range reads zeros, one at or past the end is read and not used), its values
+    // first: the wait for its keys covers them
+    int t0 = start + w * TT;
+    KeyTile<NTB, NB> kt[2];
+    ValueTile<NTB, NB> vt;
+    stage_tile<TT * VB>(vrs, vst0[w], t0 * VB, lane);
+    load_keys<VB>(kt[0], krs, k_norm, k_word, t0 * VB);
+
+    // table: thread t fills entries t + 512 i, i.e. byte t / 32 + 16 i (low nibble t / 32, high
+    // nibble i) in copy t % 32; each store instruction covers 4 KB contiguously
+    {
+        static_assert(NW * 64 == 512, "the table fill assumes 512 threads");
+        const uint32_t plo = bf16_split(cb.centroids[tid >> 5]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.u.tab[tid + 512 * i] = make_uint2(plo, bf16_split(cb.centroids[i]));
+    }
+    // query A operand: row m = n = (head m/2, r = m&1), k-group g holds coordinates
+    // 128 blk + 32 g + 4 cc + u (u = 0..3) of chunk c = 8 blk + cc, each as the bf16 half r of
+    // q * log2(e)/sqrt(d), duplicated for the centroid's two halves
+    {
+        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+        const int hm = n >> 1, r = n & 1;
+        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + (hm < G ? hm : 0)) * D;
+#pragma unroll
+        for (int c = w; c < NB * 8; c += NW) {  // chunks split over the wavefronts
+            u32x4 v;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = 128 * (c >> 3) + 32 * g + 4 * (c & 7) + u;
+                const uint32_t pr = bf16_split(qg[j] * qscale);
+                const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
+                v[u] = n < ROWS ? (half | (half << 16)) : 0u;
+            }
+            sm.op.qa[c][lane] = v;
+        }
+    }
+
+    int N = a.seq_lens[b];
+    N = N < 0 ? 0 : (N > a.capacity ? a.capacity : N);
+    const int end = min(start + a.split_len, N);
+    if (start >= end) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged tile lands before the LDS is released
+        for (int gg = 0; gg < G; ++gg) {
+            const size_t rec = rec0 + static_cast<size_t>(gg) * a.splits;
+            if (tid == 0) a.ml[rec] = make_float2(-INFINITY, 0.0f);
+            for (int j = tid; j < D; j += blockDim.x) a.acc[rec * D + j] = 0.0f;
+        }
+        return;
+    }
+    lds_write_barrier();  // table and query operand; the first tile stays in flight
+    u32x4 qall[NB * 8];
+#pragma unroll
+    for (int S = 0; S < NB * 8; ++S) qall[S] = sm.op.qa[S][lane];
+    lds_write_barrier();  // every wavefront holds its query operand before any writes weights there
+    uint32_t* wa = sm.op.wa[w];
+    if (ROWS < 16 && lane < 16) wa[C::WA - 16 + lane] = 0u;
+
+    // per lane: heads 2g and 2g+1 (when < G); inactive rows keep m = 0, p = 0
+    float m_run[2], l_run[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        m_run[e] = (2 * g + e < G) ? -INFINITY : 0.0f;
+        l_run[e] = 0.0f;
+    }
+    f32x4 acc[NB][8];
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+        for (int cb8 = 0; cb8 < 8; ++cb8) acc[blk][cb8] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const char* tab = reinterpret_cast<const char*>(sm.u.tab);
+    const uint32_t lc = (lane & 31) * 8u;  // byte 0 of a lookup address: this lane's copy
+    // with sparse V the reference follows the maximum exactly, so weights against it are as
+    // small as they can be and more values drop
+    const float slack = a.v_skip > 0.0f ? 0.0f : kRescaleSlack;
+    // value-product A operand of this lane: row n (zero row when n >= ROWS), tokens 4g..4g+3
+    const uint32_t rd_lane = n < ROWS ? n * 16 + 4 * g : C::WA - 16 + 4 * g;
+    const uint32_t wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
+    const uint32_t w_lane = 4 * g * 16 + n;              // this lane's weight word in block 0
+    // this lane's value norm and words in a stage (token n; tokens 4g.., word n)
+    const uint32_t v_norm_lane = lds_offset(n * VB), v_word_lane = lds_offset(4 * g * VB + 4 + 4 * n);
+    constexpr int kStep = NW * TT;
+
+    auto entry = [&](uint32_t word, int byte) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint2*>(tab + __builtin_amdgcn_perm(word, lc, 0x0C0C0400u + (byte << 8)));
+    };
+
+    // One tile at t0; P = tile parity selects the key register set and the value stage.
+    auto tile = [&](auto pc, const int t0) {
+        constexpr int P = decltype(pc)::value;
+        KeyTile<NTB, NB>& kc = kt[P];
+        const int nv = min(TT, end - t0);  // <= 0 for the odd tile after the last one
+        const bool more = t0 + kStep < end;
+        const int t_next = more ? t0 + kStep : t0;
+        const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
+        const uint8_t* vcur = P == 0 ? vst0[w] : vst1[w];
+        stage_tile<TT * VB>(vrn, P == 0 ? vst1[w] : vst0[w], t_next * VB, lane);
+        load_keys<VB>(kt[1 - P], krn, k_norm, k_word, t_next * VB);
+
+        // ---- scores: job J = S * NTB + tb multiplies chunk S (bytes 2 (S&1), 2 (S&1) + 1 of key
+        // word (S%8)/2 of block S/8: four coordinates) for token block tb; the lookups run
+        // kLookahead jobs ahead of the products
+        f32x4 dsc[NTB][NB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) dsc[tb][blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float nk[NTB][NB];
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk) nk[tb][blk] = half_bits_to_float(kc.norm[tb][blk]);
+        {
+            constexpr int NJ = NB * 8 * NTB, R = kLookahead + 1;
+            uint2 ring[R][2];
+            static_for<NJ + kLookahead>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int S = J / NTB, TB = J % NTB, BLK = S / 8, CC = S % 8;
+                    const uint32_t x = kc.w[TB][BLK][CC >> 1];
+                    ring[J % R][0] = entry(x, 2 * (CC & 1));
+                    ring[J % R][1] = entry(x, 2 * (CC & 1) + 1);
+                }
+                if constexpr (J >= kLookahead) {
+                    constexpr int M = J - kLookahead, S = M / NTB, TB = M % NTB, BLK = S / 8;
+                    const uint2 e0 = ring[M % R][0], e1 = ring[M % R][1];
+                    dsc[TB][BLK] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, qall[S]), __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y}),
+                        dsc[TB][BLK], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
+            });
+        }
+        // this tile's value words, and block 0's norms, from its stage
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            vt.norm[tb][0] = *reinterpret_cast<const uint16_t*>(vcur + v_norm_lane + 16 * tb * VB);
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    vt.w[tb][blk][u] =
+                        *reinterpret_cast<const uint32_t*>(vcur + v_word_lane + (16 * tb + u) * VB + 68 * blk);
+        }
+
+        // ---- online softmax; lane (n, g) holds token 16 tb + n of heads 2g, 2g+1
+        const bool live = 2 * g < G;
+        float tv[NTB][2];
+        float mx[2] = {-INFINITY, -INFINITY};
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            const bool ok = live && 16 * tb + n < nv;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                float sc = 0.0f;
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk) sc += nk[tb][blk] * (dsc[tb][blk][2 * e] + dsc[tb][blk][2 * e + 1]);
+                tv[tb][e] = ok ? sc : -INFINITY;
+                mx[e] = fmaxf(mx[e], tv[tb][e]);
+            }
+        }
+        if (a.scores) {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                    if (tv[tb][e] != -INFINITY)
+                        a.scores[(static_cast<size_t>(b) * a.hq + hq0 + 2 * g + e) * a.capacity + t0 + 16 * tb + n] =
+                            tv[tb][e] * kLn2;
+        }
+        if (__builtin_amdgcn_ballot_w64(mx[0] > m_run[0] + slack || mx[1] > m_run[1] + slack) != 0) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float mn = fmaxf(m_run[e], row16_max(mx[e]));
+                const float alpha = mn == m_run[e] ? 1.0f : __builtin_amdgcn_exp2f(m_run[e] - mn);  // -inf start gives 0
+                l_run[e] *= alpha;
+#pragma unroll
+                for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                    for (int cb8 = 0; cb8 < 8; ++cb8) {
+                        acc[blk][cb8][2 * e] *= alpha;
+                        acc[blk][cb8][2 * e + 1] *= alpha;
+                    }
+                m_run[e] = mn;
+            }
+        }
+        float pw[NTB][2];
+        bool keep = false;
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) {
+            // rows past the sequence end hold whatever the cache held: their weight must be an
+            // exact 0, not 0 * (a stale norm that may be NaN)
+            const float nvn = 16 * tb + n < nv ? half_bits_to_float(vt.norm[tb][0]) : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float p = __builtin_amdgcn_exp2f(tv[tb][e] - m_run[e]);  // 0 for invalid tokens and rows
+                l_run[e] += p;
+                pw[tb][e] = (p >= a.v_skip ? p : 0.0f) * nvn;
+                keep = keep || pw[tb][e] != 0.0f;
+            }
+        }
+        // the value products of the tile only where some weight is left (uniform)
+        if (__builtin_amdgcn_ballot_w64(keep) == 0) return;
+        if (live) {
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const float wt = pw[tb][e];
+                    const uint32_t bits = __float_as_uint(wt);
+                    const float lo = wt - __uint_as_float(bits & 0xFFFF0000u);
+                    uint32_t* dst = wa + lds_offset(w_lane + (tb * ROWS + 2 * e) * 16);
+                    dst[0] = dup_hi16(bits);                 // row (h, hi)
+                    dst[16] = dup_hi16(__float_as_uint(lo));  // row (h, lo)
+                }
+        }
+        lds_order();
+
+        // ---- values: column n = code word n (coordinates 8n..8n+7 of a block), k-group g =
+        // tokens 16 tb + 4g + u, one accumulator per nibble position.  Job J = (tb, blk, c):
+        // byte c of the four tokens' words, four lookups, whose halves are the B operands of
+        // nibble positions 2c and 2c + 1; the lookups run one job ahead of the products
+        {
+            u32x4 av[NTB];
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb) av[tb] = *reinterpret_cast<const u32x4*>(wa + lds_offset(rd_lane + tb * wa_step));
+            constexpr int NJ = NTB * NB * 4, LA = 1, R = LA + 1;
+            uint2 ring[R][4];
+            static_for<NJ + LA>([&](auto jc) {
+                constexpr int J = decltype(jc)::value;
+                if constexpr (J < NJ) {
+                    constexpr int TB = J / (4 * NB), BLK = (J / 4) % NB, CQ = J % 4;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) ring[J % R][u] = entry(vt.w[TB][BLK][u], CQ);
+                }
+                if constexpr (J >= LA) {
+                    constexpr int M = J - LA, TB = M / (4 * NB), BLK = (M / 4) % NB, CQ = M % 4;
+                    const uint2(&e)[4] = ring[M % R];
+                    acc[BLK][2 * CQ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, av[TB]), __builtin_bit_cast(bf16x8, u32x4{e[0].x, e[1].x, e[2].x, e[3].x}),
+                        acc[BLK][2 * CQ], 0, 0, 0);
+                    acc[BLK][2 * CQ + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, av[TB]), __builtin_bit_cast(bf16x8, u32x4{e[0].y, e[1].y, e[2].y, e[3].y}),
+                        acc[BLK][2 * CQ + 1], 0, 0, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
+            });
+        }
+        lds_order();
+    };
+    // pairs of tiles, so that the parity is static; the second tile of the last pair may be
+    // empty (its weights are all zero, and the running maximum is finite by then)
+    for (; t0 < end; t0 += 2 * kStep) {
+        tile(std::integral_constant<int, 0>{}, t0);
+        tile(std::integral_constant<int, 1>{}, t0 + kStep);
+    }
+    // the last requests (tiles past the end) land before the LDS is released
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // ---- merge the wavefronts ([P2] trick 3: rescale to the common maximum) into the record
+#pragma unroll
+    for (int e = 0; e < 2; ++e) l_run[e] = row16_sum(l_run[e]);
+    __syncthreads();  // every lookup of the workgroup is done: the table area takes the sums
+    float* red = sm.u.red;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int hh = 2 * g + e;
+        if (hh < G) {
+            float* r = red + (w * G + hh) * D;
+            if (n == 0) sm.ml[w][hh] = make_float2(m_run[e], l_run[e]);
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int cb8 = 0; cb8 < 8; ++cb8) r[128 * blk + 8 * n + cb8] = acc[blk][cb8][2 * e] + acc[blk][cb8][2 * e + 1];
+        }
+    }
+    __syncthreads();
+    if (tid < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, sm.ml[ww][tid].x);
+        float L = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float2 r = sm.ml[ww][tid];
+            const float f = r.x == -INFINITY ? 0.0f : exp2f(r.x - M);
+            sm.fw[ww * G + tid] = f;
+            L = fmaf(r.y, f, L);
+        }
+        a.ml[rec0 + static_cast<size_t>(tid) * a.splits] = make_float2(M, L);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < G * D; idx += blockDim.x) {
+        const int gg = idx / D, j = idx % D;
+        float A = 0.0f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) A = fmaf(red[(ww * G + gg) * D + j], sm.fw[ww * G + gg], A);
+        a.acc[(rec0 + static_cast<size_t>(gg) * a.splits) * D + j] = A;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // o, marked as changed at this point: an address built from it is formed here instead of
 // being hoisted out of a loop into a register of its own.
 __device__ __forceinline__ uint32_t refresh(uint32_t o) {
@@ -2506,8 +2872,10 @@ int auto_split_tokens(const tq_layout* L) {
     // Splits per launch, measured per kernel:
     //   * PQ4 at d = 128, G = 4 or 8 (2:4-sparse kernel): four splits per 16-wavefront workgroup,
     //     one workgroup per CU, so about 1024 splits fill the chip in a single round;
-    //   * PQ4 at d = 256, G = 4 or 8 (dense bf16 kernel): one split per 4-wavefront workgroup,
-    //     best at two workgroups per CU (c5: 44 us at 512 splits, 47 at 256, 62 at 2048);
+    //   * PQ4 at d = 256, G = 4 or 8: one split per 8-wavefront workgroup of the byte-pair kernel
+    //     (150 KB of LDS), one workgroup per CU, about 256 splits; the dense bf16 kernel
+    //     (distinct key and value centroids) runs the same splits at two 4-wavefront
+    //     workgroups per CU (c5: 44 us at 512 splits with it, 47 at 256, 62 at 2048);
     //   * the generic kernel: about 2048 splits, two rounds of four workgroups per CU.
     //   * TQ3K keys at d = 128 (matrix-core kernel, eight wavefronts and 136 KB of LDS per
     //     workgroup): one workgroup per CU, about 256 splits;
@@ -2516,7 +2884,7 @@ int auto_split_tokens(const tq_layout* L) {
     const bool pq4 = L->k_format == TQ_FMT_PQ4 && L->v_format == TQ_FMT_PQ4 && (G == 4 || G == 8);
     const bool pq3 = L->k_format == TQ_FMT_PQ3 && L->head_dim == 128 && G == 4;
     const bool tq3k = L->k_format == TQ_FMT_TQ3K && L->head_dim == 128 && G <= 8;
-    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 512) : pq3 ? 1024 : tq3k ? 256 : 2048;
+    const long target = pq4 ? (L->head_dim == 128 ? 1024 : 256) : pq3 ? 1024 : tq3k ? 256 : 2048;
     long want = (target + streams - 1) / streams;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
@@ -2609,6 +2977,12 @@ int launch_partial_bf16(const DecodeArgs& a, const tq_layout* L, const tq_codebo
                          to_dev(cbv));
 }
 
+template <int G>
+int launch_partial_d256(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const Launch& l) {
+    dim3 grid(a.splits, L->n_kv_heads, L->batch);
+    return launch_kernel(decode_partial_d256_kernel<G>, grid, dim3(D256Cfg<G>::NW * 64), l, a, to_dev(cbk));
+}
+
 template <int VF, int G>
 int launch_partial_tq3k(const DecodeArgs& a, const tq_layout* L, const tq_codebook& cbk, const tq_codebook& cbv,
                         const Launch& l) {
@@ -2650,6 +3024,13 @@ int dispatch_group(int G, const DecodeArgs& a, const tq_layout* L, const tq_code
                 if (G == 4) return same_centroids(cbk, cbv) ? launch_partial_sparse<4, false>(a, L, cbk, cbv, st)
                                                             : launch_partial_sparse<4, true>(a, L, cbk, cbv, st);
                 return launch_partial_sparse<8, false>(a, L, cbk, cbv, st);
+            }
+        }
+        if constexpr (D == 256) {
+            // one table for keys and values: the byte-pair kernel
+            if (fits && same_centroids(cbk, cbv)) {
+                if (G == 4) return launch_partial_d256<4>(a, L, cbk, st);
+                if (G == 8) return launch_partial_d256<8>(a, L, cbk, st);
             }
         }
         if (fits && G == 4) return launch_partial_bf16<D, 4>(a, L, cbk, cbv, st);
