@@ -403,6 +403,8 @@ __global__ __launch_bounds__(kWaves * 64) void decode_partial_kernel(DecodeArgs 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 
 // Byte offset into a 32-entry table from byte Q of a pre-shifted code word:
@@ -1284,7 +1286,9 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
     // value-product A operand of this lane: row n (zero row when n >= ROWS), tokens 4g..4g+3
     const uint32_t rd_lane = n < ROWS ? n * 16 + 4 * g : C::WA - 16 + 4 * g;
     const uint32_t wa_step = n < ROWS ? ROWS * 16 : 0;  // words per 16-token block
-    const uint32_t w_lane = 4 * g * 16 + n;              // this lane's weight word in block 0
+    // this lane's weight word in block 0: token n at the k-group of the 2:4-sparse value product
+    // that holds it (token 4 gb + e at group 2 gb + (e & 1) + 8 (e >> 1))
+    const uint32_t w_lane = 4 * g * 16 + 2 * (n >> 2) + (n & 1) + 8 * ((n >> 1) & 1);
     // this lane's value norm and words in a stage (token n; tokens 4g.., word n)
     const uint32_t v_norm_lane = lds_offset(n * VB), v_word_lane = lds_offset(4 * g * VB + 4 + 4 * n);
     constexpr int kStep = NW * TT;
@@ -1424,32 +1428,38 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
         }
         lds_order();
 
-        // ---- values: column n = code word n (coordinates 8n..8n+7 of a block), k-group g =
-        // tokens 16 tb + 4g + u, one accumulator per nibble position.  Job J = (tb, blk, c):
-        // byte c of the four tokens' words, four lookups, whose halves are the B operands of
-        // nibble positions 2c and 2c + 1; the lookups run one job ahead of the products
+        // ---- values: column n = code word n (coordinates 8n..8n+7 of a block), one accumulator
+        // per nibble position, on v_smfmac_f32_16x16x64_bf16 (2:4-sparse A, dense B).  Job J =
+        // (tb, blk, c): byte c of the words of tokens 16 tb + 4g + u (u = 0..3), four lookups whose
+        // eight dwords are the B operand as loaded (lane group g: dense k-groups 2g, 2g + 1 and
+        // 8 + 2g, 9 + 2g, one token each: (c_hi, c_lo) of nibble 2c, then of nibble 2c + 1).  The
+        // A operand is the weights of the k-groups' tokens, nonzero at positions 0, 1 of every
+        // group for nibble 2c (index 0x4444) and at 2, 3 for nibble 2c + 1 (0xEEEE): two
+        // products per job, no register moves.  The lookups run one job ahead of the products.
         {
             u32x4 av[NTB];
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) av[tb] = *reinterpret_cast<const u32x4*>(wa + lds_offset(rd_lane + tb * wa_step));
             constexpr int NJ = NTB * NB * 4, LA = 1, R = LA + 1;
-            uint2 ring[R][4];
+            u32x8 ring[R];
             static_for<NJ + LA>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 if constexpr (J < NJ) {
                     constexpr int TB = J / (4 * NB), BLK = (J / 4) % NB, CQ = J % 4;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) ring[J % R][u] = entry(vt.w[TB][BLK][u], CQ);
+                    for (int u = 0; u < 4; ++u) {
+                        const uint2 e = entry(vt.w[TB][BLK][u], CQ);
+                        ring[J % R][2 * u] = e.x;
+                        ring[J % R][2 * u + 1] = e.y;
+                    }
                 }
                 if constexpr (J >= LA) {
                     constexpr int M = J - LA, TB = M / (4 * NB), BLK = (M / 4) % NB, CQ = M % 4;
-                    const uint2(&e)[4] = ring[M % R];
-                    acc[BLK][2 * CQ] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av[TB]), __builtin_bit_cast(bf16x8, u32x4{e[0].x, e[1].x, e[2].x, e[3].x}),
-                        acc[BLK][2 * CQ], 0, 0, 0);
-                    acc[BLK][2 * CQ + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, av[TB]), __builtin_bit_cast(bf16x8, u32x4{e[0].y, e[1].y, e[2].y, e[3].y}),
-                        acc[BLK][2 * CQ + 1], 0, 0, 0);
+                    const bf16x16 bop = __builtin_bit_cast(bf16x16, ring[M % R]);
+                    acc[BLK][2 * CQ] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(__builtin_bit_cast(bf16x8, av[TB]), bop,
+                                                                                  acc[BLK][2 * CQ], 0x4444, 0, 0);
+                    acc[BLK][2 * CQ + 1] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(
+                        __builtin_bit_cast(bf16x8, av[TB]), bop, acc[BLK][2 * CQ + 1], 0xEEEE, 0, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);  // keep the issue order written here
             });
@@ -1581,9 +1591,6 @@ TQ_PUT_BYTE1(3)
 // k = 32+8g .. 32+8g+7 in elements 8..15.  Dense k-group gd (four k) thus
 // sits in A lane group gd / 4 and in B lane group (gd & 7) / 2, element
 // quad (gd & 1) + 2 (gd / 8).
-typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
-
 __host__ __device__ constexpr int sp_lane_group(int gd) { return (gd & 7) >> 1; }
 __host__ __device__ constexpr int sp_quad(int gd) { return (gd & 1) + 2 * (gd >> 3); }
 __host__ __device__ constexpr int sp_group(int gb, int e) { return 2 * gb + (e & 1) + 8 * (e >> 1); }
