@@ -1207,6 +1207,17 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
     const int k_norm = n * VB;               // key norm of token n
     const int k_word = n * VB + 4 + 16 * g;  // key words 4g..4g+3 of token n
 
+    // the query entries this thread stages, requested first (the memory counter drains in order:
+    // a load behind the tile's would wait for it)
+    const float qscale = kLog2e / sqrtf(static_cast<float>(D));
+    const int hm = n >> 1, r = n & 1;
+    const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + (hm < G ? hm : 0)) * D;
+    float4 qv[NB * 8 / NW];
+#pragma unroll
+    for (int k = 0; k < NB * 8 / NW; ++k) {
+        const int c = w + NW * k;
+        qv[k] = *reinterpret_cast<const float4*>(qg + 128 * (c >> 3) + 32 * g + 4 * (c & 7));
+    }
     // the first tile before anything else, before the sequence length arrives (a tile past the
     // stream's range reads zeros, one at or past the end is read and not used), its values
     // first: the wait for its keys covers them
@@ -1215,33 +1226,36 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
     ValueTile<NTB, NB> vt;
     stage_tile<TT * VB>(vrs, vst0[w], t0 * VB, lane);
     load_keys<VB>(kt[0], krs, k_norm, k_word, t0 * VB);
+    __builtin_amdgcn_sched_barrier(0);  // the requests stay ahead of the table and query work
 
     // table: thread t fills entries t + 512 i, i.e. byte t / 32 + 16 i (low nibble t / 32, high
     // nibble i) in copy t % 32; each store instruction covers 4 KB contiguously
     {
         static_assert(NW * 64 == 512, "the table fill assumes 512 threads");
-        const uint32_t plo = bf16_split(cb.centroids[tid >> 5]);
+        uint32_t pc[16], plo = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sm.u.tab[tid + 512 * i] = make_uint2(plo, bf16_split(cb.centroids[i]));
+        for (int i = 0; i < 16; ++i) {
+            pc[i] = bf16_split(cb.centroids[i]);
+            plo = (tid >> 5) == i ? pc[i] : plo;  // selected, not indexed: no load of the arguments
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sm.u.tab[tid + 512 * i] = make_uint2(plo, pc[i]);
     }
     // query A operand: row m = n = (head m/2, r = m&1), k-group g holds coordinates
     // 128 blk + 32 g + 4 cc + u (u = 0..3) of chunk c = 8 blk + cc, each as the bf16 half r of
     // q * log2(e)/sqrt(d), duplicated for the centroid's two halves
     {
-        const float qscale = kLog2e / sqrtf(static_cast<float>(D));
-        const int hm = n >> 1, r = n & 1;
-        const float* qg = a.q_rot + (static_cast<size_t>(b) * a.hq + hq0 + (hm < G ? hm : 0)) * D;
 #pragma unroll
-        for (int c = w; c < NB * 8; c += NW) {  // chunks split over the wavefronts
+        for (int k = 0; k < NB * 8 / NW; ++k) {  // chunks split over the wavefronts
+            const float qe[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
             u32x4 v;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int j = 128 * (c >> 3) + 32 * g + 4 * (c & 7) + u;
-                const uint32_t pr = bf16_split(qg[j] * qscale);
+                const uint32_t pr = bf16_split(qe[u] * qscale);
                 const uint32_t half = r ? (pr >> 16) : (pr & 0xFFFFu);
                 v[u] = n < ROWS ? (half | (half << 16)) : 0u;
             }
-            sm.op.qa[c][lane] = v;
+            sm.op.qa[w + NW * k][lane] = v;
         }
     }
 
