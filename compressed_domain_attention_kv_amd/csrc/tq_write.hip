@@ -258,8 +258,9 @@ __device__ __forceinline__ void encode_vec(const WriteArgs& a, const DevCodebook
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float t = rintf((v[e] - z) * inv);
-            packed |= static_cast<uint32_t>(fminf(fmaxf(t, 0.0f), static_cast<float>(QMAX))) << (QB * e);
+            // clamp to [0, QMAX] in one median (a NaN product gives 0, as the min-max pair did)
+            const float t = __builtin_amdgcn_fmed3f(rintf((v[e] - z) * inv), 0.0f, static_cast<float>(QMAX));
+            packed |= static_cast<uint32_t>(t) << (QB * e);
         }
         if (active) {
             const int grp = l >> 2, lg = l & 3;
