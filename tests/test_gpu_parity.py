@@ -397,6 +397,33 @@ def test_pq4_sparse_ragged_lengths(case):
         _say(f"pq4 sparse {case} split={split}: score err {es:.2e}, output err {eo:.2e}")
 
 
+@pytest.mark.parametrize("case", ["g4", "g8", "g8_two_tables"])
+def test_pq4_d256_ragged_lengths(case):
+    """PQ4 at d 256: the byte-pair kernel (one table for keys and values) at four and eight
+    query heads per KV head, and the dense kernel at eight with the values' own centroids:
+    contexts of 0, 1, a token block, a tile, one past it, one past a split and the full
+    capacity over garbage-filled caches, with the automatic split and splits of 256 and 512
+    tokens (one or two tiles per wavefront, wavefronts without tokens, a last tile partly past
+    the end)."""
+    G, vk = {"g4": (4, synth.QUANTILE_MEAN), "g8": (8, synth.QUANTILE_MEAN),
+             "g8_two_tables": (8, synth.LLOYD_MAX)}[case]
+    w = synth.scaled(synth.C5, v_kind=vk, batch=8, n_q_heads=2 * G, n_kv_heads=2, context=1024, capacity=1024)
+    st = P.Setup(w)
+    L = st.layout()
+    lens = [0, 1, 16, 32, 33, 300, 700, 1024]
+    kb, vbytes, kdq, vdq = _oracle_cache(st, w, lens)
+    kc = _garbage_cache(st, L, synth.K_TENSOR, kb)
+    vc = _garbage_cache(st, L, synth.V_TENSOR, vbytes)
+    q = synth.queries(w)
+    for split in (0, 256, 512):
+        out, scores, _, _ = P.gpu_decode(st, L, q, kc, vc, lens, split_tokens=split)
+        es, eo = P.check_read(st, q, kdq, vdq, lens, out, scores, w.capacity)
+        assert np.all(out[0] == 0.0)
+        for b, n in enumerate(lens):  # scores are written only below the context length
+            assert np.all(np.isnan(scores[b, :, n:]))
+        _say(f"pq4 d256 {case} split={split}: score err {es:.2e}, output err {eo:.2e}")
+
+
 def test_timed_partial_matches_untimed():
     """tq_decode_partial_timed writes the same records as tq_decode_partial and
     its events span a positive kernel time."""
