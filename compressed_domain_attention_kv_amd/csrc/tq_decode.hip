@@ -1158,6 +1158,20 @@ __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(D =
 // value weights serve both 128-coordinate blocks: each block of a d 256 vector holds the
 // full-vector norm ([P1] section 9, head_dim-specific blocks), so the weights are formed once
 // from block 0's norm.
+// The keys of a d 256 tile with block 0's norm only (each block holds the full-vector norm).
+template <int VB, int NTB, int NB>
+__device__ __forceinline__ void load_keys_n0(KeyTile<NTB, NB>& k, __amdgpu_buffer_rsrc_t r, int norm_off, int word_off,
+                                             int tile_off) {
+#pragma unroll
+    for (int tb = 0; tb < NTB; ++tb) {
+        k.norm[tb][0] = __builtin_amdgcn_raw_buffer_load_b16(r, norm_off + 16 * tb * VB, tile_off, kStreamPolicy);
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+            k.w[tb][blk] = __builtin_bit_cast(u32x4u, __builtin_amdgcn_raw_buffer_load_b128(r, word_off + 16 * tb * VB + 68 * blk,
+                                                                                          tile_off, kStreamPolicy));
+    }
+}
+
 template <int G>
 struct D256Cfg {
     static constexpr int D = 256, NB = 2, VB = 136, TT = 32, NTB = 2, NW = 8, ROWS = 2 * G;
@@ -1221,11 +1235,18 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
     // the first tile before anything else, before the sequence length arrives (a tile past the
     // stream's range reads zeros, one at or past the end is read and not used), its values
     // first: the wait for its keys covers them
+    // keys KA tiles ahead of the products (G = 8: two, in three register sets; G = 4, whose
+    // zero rows cost registers: one), values one tile ahead in two stages
+    constexpr int KA = G == 8 ? 2 : 1, NK = KA + 1, UNR = KA == 2 ? 6 : 2;
+    constexpr int kStep = NW * TT;
     int t0 = start + w * TT;
-    KeyTile<NTB, NB> kt[2];
+    KeyTile<NTB, NB> kt[NK];
     ValueTile<NTB, NB> vt;
     stage_tile<TT * VB>(vrs, vst0[w], t0 * VB, lane);
-    load_keys<VB>(kt[0], krs, k_norm, k_word, t0 * VB);
+    static_for<KA>([&](auto kc) {
+        constexpr int K = decltype(kc)::value;
+        load_keys_n0<VB>(kt[K], krs, k_norm, k_word, (t0 + K * kStep) * VB);
+    });
     __builtin_amdgcn_sched_barrier(0);  // the requests stay ahead of the table and query work
 
     // table: thread t fills entries t + 512 i, i.e. byte t / 32 + 16 i (low nibble t / 32, high
@@ -1305,23 +1326,22 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
     const uint32_t w_lane = 4 * g * 16 + 2 * (n >> 2) + (n & 1) + 8 * ((n >> 1) & 1);
     // this lane's value norm and words in a stage (token n; tokens 4g.., word n)
     const uint32_t v_norm_lane = lds_offset(n * VB), v_word_lane = lds_offset(4 * g * VB + 4 + 4 * n);
-    constexpr int kStep = NW * TT;
 
     auto entry = [&](uint32_t word, int byte) __attribute__((always_inline)) {
         return *reinterpret_cast<const uint2*>(tab + __builtin_amdgcn_perm(word, lc, 0x0C0C0400u + (byte << 8)));
     };
 
-    // One tile at t0; P = tile parity selects the key register set and the value stage.
-    auto tile = [&](auto pc, const int t0) {
-        constexpr int P = decltype(pc)::value;
-        KeyTile<NTB, NB>& kc = kt[P];
-        const int nv = min(TT, end - t0);  // <= 0 for the odd tile after the last one
-        const bool more = t0 + kStep < end;
-        const int t_next = more ? t0 + kStep : t0;
-        const __amdgpu_buffer_rsrc_t krn = more ? krs : krs_none, vrn = more ? vrs : vrs_none;
+    // One tile at t0; I = the tile's index mod UNR: key register set I % NK (the keys of the tile
+    // KA ahead go into set (I + KA) % NK), value stage I % 2 (the next tile's values into the other)
+    auto tile = [&](auto ic, const int t0) {
+        constexpr int I = decltype(ic)::value, P = I % 2, K = I % NK, KN = (I + KA) % NK;
+        KeyTile<NTB, NB>& kc = kt[K];
+        const int nv = min(TT, end - t0);
+        const bool more = t0 + kStep < end, morek = t0 + KA * kStep < end;
+        const int t_next = more ? t0 + kStep : t0, t_nextk = morek ? t0 + KA * kStep : t0;
         const uint8_t* vcur = P == 0 ? vst0[w] : vst1[w];
-        stage_tile<TT * VB>(vrn, P == 0 ? vst1[w] : vst0[w], t_next * VB, lane);
-        load_keys<VB>(kt[1 - P], krn, k_norm, k_word, t_next * VB);
+        stage_tile<TT * VB>(more ? vrs : vrs_none, P == 0 ? vst1[w] : vst0[w], t_next * VB, lane);
+        load_keys_n0<VB>(kt[KN], morek ? krs : krs_none, k_norm, k_word, t_nextk * VB);
 
         // ---- scores: job J = S * NTB + tb multiplies chunk S (bytes 2 (S&1), 2 (S&1) + 1 of key
         // word (S%8)/2 of block S/8: four coordinates) for token block tb; the lookups run
@@ -1331,15 +1351,13 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
         for (int tb = 0; tb < NTB; ++tb)
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk) dsc[tb][blk] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        float nk[NTB][NB];
+        float nk[NTB];  // block 0's norm: both blocks hold the vector's norm
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int blk = 0; blk < NB; ++blk) nk[tb][blk] = half_bits_to_float(kc.norm[tb][blk]);
+        for (int tb = 0; tb < NTB; ++tb) nk[tb] = half_bits_to_float(kc.norm[tb][0]);
         {
-            constexpr int NJ = NB * 8 * NTB, R = kLookahead + 1;
+            constexpr int NJ = NB * 8 * NTB, LA = 2, R = LA + 1;
             uint2 ring[R][2];
-            static_for<NJ + kLookahead>([&](auto jc) {
+            static_for<NJ + LA>([&](auto jc) {
                 constexpr int J = decltype(jc)::value;
                 if constexpr (J < NJ) {
                     constexpr int S = J / NTB, TB = J % NTB, BLK = S / 8, CC = S % 8;
@@ -1347,8 +1365,8 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
                     ring[J % R][0] = entry(x, 2 * (CC & 1));
                     ring[J % R][1] = entry(x, 2 * (CC & 1) + 1);
                 }
-                if constexpr (J >= kLookahead) {
-                    constexpr int M = J - kLookahead, S = M / NTB, TB = M % NTB, BLK = S / 8;
+                if constexpr (J >= LA) {
+                    constexpr int M = J - LA, S = M / NTB, TB = M % NTB, BLK = S / 8;
                     const uint2 e0 = ring[M % R][0], e1 = ring[M % R][1];
                     dsc[TB][BLK] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                         __builtin_bit_cast(bf16x8, qall[S]), __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y}),
@@ -1380,8 +1398,8 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
             for (int e = 0; e < 2; ++e) {
                 float sc = 0.0f;
 #pragma unroll
-                for (int blk = 0; blk < NB; ++blk) sc += nk[tb][blk] * (dsc[tb][blk][2 * e] + dsc[tb][blk][2 * e + 1]);
-                tv[tb][e] = ok ? sc : -INFINITY;
+                for (int blk = 0; blk < NB; ++blk) sc += dsc[tb][blk][2 * e] + dsc[tb][blk][2 * e + 1];
+                tv[tb][e] = ok ? nk[tb] * sc : -INFINITY;
                 mx[e] = fmaxf(mx[e], tv[tb][e]);
             }
         }
@@ -1480,11 +1498,16 @@ __global__ __launch_bounds__(D256Cfg<G>::NW * 64) __attribute__((amdgpu_waves_pe
         }
         lds_order();
     };
-    // pairs of tiles, so that the parity is static; the second tile of the last pair may be
-    // empty (its weights are all zero, and the running maximum is finite by then)
-    for (; t0 < end; t0 += 2 * kStep) {
-        tile(std::integral_constant<int, 0>{}, t0);
-        tile(std::integral_constant<int, 1>{}, t0 + kStep);
+    // UNR tiles per trip, so that both buffer indexes are static; the trip stops after the last tile
+    bool go = t0 < end;  // wave-uniform
+    while (go) {
+        static_for<UNR>([&](auto ic) {
+            if (go) {
+                tile(ic, t0);
+                t0 += kStep;
+                go = t0 < end;
+            }
+        });
     }
     // the last requests (tiles past the end) land before the LDS is released
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
