@@ -39,6 +39,9 @@ CASES = {
     "c4_g8_lloyd_v": synth.scaled(synth.C4, v_kind=synth.LLOYD_MAX, batch=1, n_q_heads=16, n_kv_heads=2,
                                   context=900, capacity=960),
     "c5": synth.scaled(synth.C5, batch=2, n_q_heads=16, n_kv_heads=2, context=700, capacity=704),
+    "c5_g4": synth.scaled(synth.C5, batch=2, n_q_heads=8, n_kv_heads=2, context=600, capacity=640),
+    "c5_lloyd_v": synth.scaled(synth.C5, v_kind=synth.LLOYD_MAX, batch=1, n_q_heads=16, n_kv_heads=2, context=500,
+                               capacity=512),
     "c2": synth.scaled(synth.C2, batch=2, n_q_heads=8, n_kv_heads=2, context=777, capacity=832),
     "c3": synth.scaled(synth.C3, batch=1, n_q_heads=10, n_kv_heads=2, context=999, capacity=1024),
 }
