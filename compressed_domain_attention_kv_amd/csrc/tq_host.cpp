@@ -2,6 +2,7 @@
 // Box-Muller QJL matrix, layout arithmetic, validation and error text.
 // Plain C++17 with libm; no device code.
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -145,6 +146,10 @@ int format_bits(int format) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// A bound on how far past a stream's end a decode kernel's tile requests reach (a workgroup's
+// first tiles and the tiles it requests ahead; they read zeros there): under a thousand tokens.
+constexpr double kStreamSlack = 4096.0;
+
 int check_layout(const tq_layout* L) {
     if (!L) return TQ_ERR_INVALID;
     if (L->batch <= 0 || L->n_q_heads <= 0 || L->n_kv_heads <= 0 || L->capacity <= 0 || L->reserved != 0)
@@ -160,6 +165,10 @@ int check_layout(const tq_layout* L) {
     // every byte offset of a cache must fit in 63 bits and every index in 31
     const double vecs = static_cast<double>(L->batch) * L->n_kv_heads * L->capacity;
     if (vecs > 2147483647.0) return TQ_ERR_RANGE;
+    // the decode kernels address one (b, kv-head) stream with 32-bit byte offsets, including
+    // the tiles they request past its end (fewer than kStreamSlack tokens)
+    const double vb = static_cast<double>(std::max(vector_bytes(kf, L->head_dim), vector_bytes(vf, L->head_dim)));
+    if ((static_cast<double>(L->capacity) + kStreamSlack) * vb > 2147483647.0) return TQ_ERR_RANGE;
     return TQ_OK;
 }
 

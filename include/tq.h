@@ -131,7 +131,11 @@ typedef struct tq_layout {
     int32_t n_q_heads;  /* Hq: query heads, a multiple of n_kv_heads        */
     int32_t n_kv_heads; /* Hkv                                              */
     int32_t head_dim;   /* d: 128 or 256                                    */
-    int32_t capacity;   /* tokens per (b, kv-head) stream, multiple of 64   */
+    int32_t capacity;   /* tokens per (b, kv-head) stream, multiple of 64;
+                           (capacity + 4096) * vector bytes < 2^31 (one
+                           stream addressed with 32-bit offsets), and
+                           batch * n_kv_heads * capacity < 2^31 (else
+                           TQ_ERR_RANGE)                                  */
     int32_t k_format;   /* tq_format of keys                                */
     int32_t v_format;   /* tq_format of values                              */
     int32_t reserved;   /* must be 0                                        */

@@ -95,6 +95,27 @@ def test_layout_validation_codes():
         assert e.value.status == code
 
 
+def test_stream_length_limit_of_32_bit_stream_offsets():
+    """One (b, kv-head) stream must stay addressable with 32-bit byte offsets, with room for
+    the tiles a kernel requests past its end: (capacity + 4096) * vector bytes < 2^31.  The
+    longest accepted stream and the next multiple of 64 tokens, per format pair and d."""
+    for kf, vf, d in [(tq.FMT_PQ4, tq.FMT_PQ4, 128), (tq.FMT_PQ4, tq.FMT_PQ4, 256), (tq.FMT_PQ3, tq.FMT_PQ4, 128),
+                      (tq.FMT_TQ3K, tq.FMT_GQ2V, 128), (tq.FMT_TQ3K, tq.FMT_GQ4V, 256)]:
+        vb = max(tq.vector_bytes(kf, d), tq.vector_bytes(vf, d))
+        cap = ((2**31 - 1) // vb - 4096) // 64 * 64
+        while (cap + 4096) * vb > 2**31 - 1:
+            cap -= 64
+        k_bytes, v_bytes = tq.cache_bytes(tq.Layout(1, 1, 1, d, cap, kf, vf))
+        assert k_bytes == cap * tq.vector_bytes(kf, d) and v_bytes == cap * tq.vector_bytes(vf, d)
+        with pytest.raises(tq.TQError) as e:
+            tq.cache_bytes(tq.Layout(1, 1, 1, d, cap + 64, kf, vf))
+        assert e.value.status == -4
+    # the old bound alone (2^31 - 1 vectors) would have accepted a 24M-token d 256 stream
+    with pytest.raises(tq.TQError) as e:
+        tq.cache_bytes(tq.Layout(1, 1, 1, 256, 24 * 2**20, tq.FMT_PQ4, tq.FMT_PQ4))
+    assert e.value.status == -4
+
+
 def test_splits_and_workspace_arithmetic():
     L = tq.Layout(8, 32, 8, 128, 65536, tq.FMT_PQ4, tq.FMT_PQ4)
     s = tq.decode_splits(L)
