@@ -126,3 +126,62 @@ def test_decode_at_the_longest_accepted_stream(name, balanced):
     for g in range(G):
         err = P.rel_err_rows(got[g], ref)
         assert err <= P.OUT_TOL, f"head {g}: relative error {err:.3g}"
+
+
+@pytest.mark.parametrize("fmt_d", [(synth.PQ4, 128), (synth.PQ4, 256), (synth.PQ3, 128)], ids=["pq4_d128", "pq4_d256",
+                                                                                                "pq3_d128"])
+def test_append_at_the_end_of_the_longest_accepted_stream(fmt_d):
+    """Rows appended at the last positions of the longest stream land there, byte for byte as
+    the same rows encoded into a one-tile cache, and nothing else in the stream changes; at
+    PQ4 d 128 also through the decode step, whose partial kernel writes the step's token."""
+    fmt, d = fmt_d
+    cap = _max_capacity(fmt, fmt, d)
+    bits = 4 if fmt == synth.PQ4 else 3
+    cbk, _ = tq.build_codebook(d, bits, 0, 5, 6)
+    cbv, _ = tq.build_codebook(d, bits, 0, 7, 8)
+    L = tq.Layout(1, 4, 1, d, cap, fmt, fmt)
+    Ls = tq.Layout(1, 4, 1, d, 64, fmt, fmt)
+    vb = tq.vector_bytes(fmt, d)
+    kb, _ = tq.cache_bytes(L)
+    _say(f"append at the end: fmt {fmt} d {d} capacity {cap} ({kb / 2**30:.2f} GiB per cache)")
+    rng = np.random.default_rng(d + fmt)
+    rows_k = rng.standard_normal((3, 1, d)).astype(np.float16)
+    rows_v = rng.standard_normal((3, 1, d)).astype(np.float16)
+    # reference bytes: the same rows at positions 0..2 of a one-tile cache
+    ks = torch.zeros(tq.cache_bytes(Ls)[0], dtype=torch.uint8, device="cuda")
+    vs = torch.zeros(tq.cache_bytes(Ls)[1], dtype=torch.uint8, device="cuda")
+    tq.quantize_append(Ls, cbk, cbv, None, torch.from_numpy(rows_k).cuda(), torch.from_numpy(rows_v).cuda(),
+                       torch.tensor([0, 1, 2], dtype=torch.int32, device="cuda"), ks, vs)
+    ref_k = ks.view(64, vb)[:3].cpu().numpy()
+    ref_v = vs.view(64, vb)[:3].cpu().numpy()
+
+    kc = torch.full((kb,), 0xEE, dtype=torch.uint8, device="cuda")
+    vc = torch.full((kb,), 0xEE, dtype=torch.uint8, device="cuda")
+    pos = [cap - 3, cap - 2, cap - 1]
+    tq.quantize_append(L, cbk, cbv, None, torch.from_numpy(rows_k).cuda(), torch.from_numpy(rows_v).cuda(),
+                       torch.tensor(pos, dtype=torch.int32, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    for cache, ref, nm in ((kc, ref_k, "k"), (vc, ref_v, "v")):
+        tail = cache.view(cap, vb)[cap - 4:].cpu().numpy()
+        assert np.all(tail[0] == 0xEE), f"{nm}: the row before the appended ones changed"
+        assert np.array_equal(tail[1:], ref), f"{nm}: appended rows differ from the one-tile encoding"
+        head = cache.view(cap, vb)[: cap - 4]
+        assert bool((head == 0xEE).all()), f"{nm}: a row outside the appended ones changed"
+
+    if fmt == synth.PQ4 and d == 128:
+        # the decode step appends its token at the last position from inside the partial kernel
+        kc.view(cap, vb)[cap - 1] = 0xEE
+        vc.view(cap, vb)[cap - 1] = 0xEE
+        q = torch.from_numpy(rng.standard_normal((1, 4, d)).astype(np.float32)).cuda()
+        scratch = torch.empty_like(q)
+        ws = tq.decode_workspace(L)
+        sl = torch.tensor([cap], dtype=torch.int32, device="cuda")
+        tq.decode_step(L, cbk, cbv, torch.from_numpy(rows_k[2:3]).cuda().view(1, 1, d),
+                       torch.from_numpy(rows_v[2:3]).cuda().view(1, 1, d),
+                       torch.tensor([cap - 1], dtype=torch.int32, device="cuda"), q, scratch, kc, vc, sl, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(kc.view(cap, vb)[cap - 1].cpu().numpy(), ref_k[2]), "decode step: key row"
+        assert np.array_equal(vc.view(cap, vb)[cap - 1].cpu().numpy(), ref_v[2]), "decode step: value row"
+        assert np.array_equal(kc.view(cap, vb)[cap - 3:cap - 1].cpu().numpy(), ref_k[:2])
+    del kc, vc
+    torch.cuda.empty_cache()
