@@ -3,9 +3,11 @@
 One (batch row, KV head) stream holds the largest capacity the layout check
 allows, so the decode kernels' byte offsets into the stream reach within a few
 thousand vectors of 2^31.  Every token but the last 64 carries one key/value
-pair (k0, v0); the last 64 carry (k1, v1), with k1 along the query.  Its score
-leads either by about 40 (natural-log units: the tail decides the output) or by
-about ln(n0 / 64) (the two parts weigh about the same, so every token counts).
+pair (k0, v0) and the rest carry (k1, v1): either the last 64, with k1 along the
+query so that its score leads by about 40 (natural-log units: the tail decides
+the output), or the second half of the stream, with k1 of the size of k0 (the
+two halves weigh about the same, so every token counts, and the small scores
+keep the score rounding out of the comparison).
 With two distinct tokens the softmax has a closed form over the oracle's
 dequantization of the GPU-written blocks:
 
@@ -50,9 +52,11 @@ def _gpu():
 
 
 # the kernel families: the 2:4-sparse PQ4 kernel (four query heads per KV head), its PQ3 path,
-# the d 256 byte-pair kernel (eight heads), and the generic kernel (one head)
+# the d 256 byte-pair kernel (eight heads), the TQ3K-key kernel (five heads, GQ2V values), and
+# the generic kernel (one head)
 CASES = {
     "pq4_d128_g4": (synth.C4, 4, 128),
+    "tq3k_gq2v_d128_g5": (synth.C3, 5, 128),
     "pq3_d128_g4": (synth.C2, 4, 128),
     "pq4_d256_g8": (synth.C5, 8, 256),
     "pq4_d128_g1": (synth.C1, 1, 128),
@@ -76,8 +80,11 @@ def test_decode_at_the_longest_accepted_stream(name, balanced):
     q[0, :] = rng.standard_normal(d).astype(np.float32)  # one query for every head of the group
     qn = q[0, 0] / np.linalg.norm(q[0, 0])
     k0 = (0.3 * rng.standard_normal(d)).astype(np.float16)
-    lead_target = np.log((cap - TAIL) / TAIL) if balanced else 40.0
-    k1 = (qn * (lead_target * np.sqrt(d) / np.linalg.norm(q[0, 0])) + 0.05 * rng.standard_normal(d)).astype(np.float16)
+    n1 = cap // 2 // 64 * 64 if balanced else TAIL
+    if balanced:
+        k1 = (0.3 * rng.standard_normal(d)).astype(np.float16)
+    else:
+        k1 = (qn * (40.0 * np.sqrt(d) / np.linalg.norm(q[0, 0])) + 0.05 * rng.standard_normal(d)).astype(np.float16)
     v0 = rng.standard_normal(d).astype(np.float16)
     v1 = (rng.standard_normal(d) + 3.0).astype(np.float16)
     Ls = tq.Layout(1, G, 1, d, 64, w.k_format, w.v_format)
@@ -91,8 +98,8 @@ def test_decode_at_the_longest_accepted_stream(name, balanced):
     vblk = vc_s.view(64, st.vbv)[:2].clone()
     del kc_s, vc_s
 
-    # the long stream: n0 copies of (k0, v0), then TAIL copies of (k1, v1)
-    n0 = cap - TAIL
+    # the long stream: n0 copies of (k0, v0), then n1 copies of (k1, v1)
+    n0 = cap - n1
     kc = torch.empty(kb, dtype=torch.uint8, device="cuda")
     vc = torch.empty(vb, dtype=torch.uint8, device="cuda")
     kc.view(cap, st.vbk)[:n0] = kblk[0]
@@ -102,11 +109,16 @@ def test_decode_at_the_longest_accepted_stream(name, balanced):
 
     qd = torch.from_numpy(q).cuda()
     q_rot = torch.empty_like(qd)
-    tq.rotate_sketch_query(L, st.cbk, st.S_dev, qd, q_rot, None)
+    q_sk = torch.empty_like(qd) if w.k_format == synth.TQ3K else None
+    tq.rotate_sketch_query(L, st.cbk, st.S_dev, qd, q_rot, q_sk)
     out = torch.full((1, G, d), float("nan"), device="cuda")
-    ws = tq.decode_workspace(L)
+    # the balanced case on 8192-token splits: with the automatic split a wavefront may sum some
+    # 20,000 equal terms (TQ3K keys, one split per 161,000 tokens), whose fp32 sums drift by up
+    # to that count times 2^-24, about 1e-3, beside the output tolerance
+    split = 8192 if balanced else 0
+    ws = tq.decode_workspace(L, split)
     sl = torch.tensor([cap], dtype=torch.int32, device="cuda")
-    tq.decode_attention(L, st.cbk, st.cbv, q_rot, None, kc, vc, sl, out, ws)
+    tq.decode_attention(L, st.cbk, st.cbv, q_rot, q_sk, kc, vc, sl, out, ws, split_tokens=split)
     torch.cuda.synchronize()
     got = out.cpu().numpy()[0]
     del kc, vc, ws
@@ -118,7 +130,7 @@ def test_decode_at_the_longest_accepted_stream(name, balanced):
     qq = q[0, 0].astype(np.float64)
     s = khat @ qq / np.sqrt(d)
     lead = s[1] - s[0]
-    wts = np.array([n0 * np.exp(s[0] - s[1]), TAIL * 1.0])
+    wts = np.array([n0 * np.exp(s[0] - s[1]), n1 * 1.0])
     ref = (wts[0] * vhat[0] + wts[1] * vhat[1]) / wts.sum()
     _say(f"  score lead {lead:.1f}, weight of the n0 tokens {wts[0] / wts.sum():.2e}")
     share = wts[0] / wts.sum()
