@@ -220,7 +220,11 @@ int tq_rotate_sketch_query(const tq_layout* L, const tq_codebook* cbk, const flo
 
 /* Number of context splits and workspace bytes of a decode call.
  *   split_tokens  tokens per split, a multiple of 256, or 0 for the
- *                 library's choice (enough splits to fill the GPU)
+ *                 library's choice (enough splits to fill the GPU).  Each
+ *                 wavefront sums its share of a split in fp32, so the sums'
+ *                 rounding grows with the split: on streams of tens of
+ *                 millions of tokens a smaller split (such as 8192) keeps it
+ *                 near 1e-4 of the output
  * Workspace layout (each region starts at a multiple of 256 bytes):
  *   float2 ml[B][Hq][splits]  (m, l) of every split record
  *   float  acc[B][Hq][splits][d]
